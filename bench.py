@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of the ISA forward hot path on one MI355X.
+
+One step = one call of isa_attention (pool, saliency, context top-rho,
+pack, sharpness + Taylor, query top-gamma, full attention and merge) over one
+batch of seeded synthetic inputs already resident in HBM.  Prints one JSON
+line: the metric (queries/s), ms per layer call, the library's own dense
+flash attention on the same inputs, per-stage times from HIP events placed
+between the stages of the same stream, the roofline of the dominant kernel
+(full attention, bf16 MFMA) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gamma G]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "ISA attn queries/s + ms vs own dense FA, Ns=Nc=17550 H=24 d=128 bf16"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video_dit_layer")
+    ap.add_argument("--gamma", type=float, default=None, help="override the workload's gamma")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads of the CPU-oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    return ap.parse_args()
+
+
+def full_route_flops(views, w, kq_gamma):
+    """Algorithmic FLOPs of one full-attention launch: 4 d per (query, key)
+    pair, counting only real rows and real keys (short tail blocks included
+    at their size)."""
+    Ns, Nc, b, d = w.Ns, w.Nc, w.b, w.d
+    full = views["full_q"].cpu().numpy()
+    kept = views["kept_ctx"].cpu().numpy()
+    n_src = np.array([min(b, Ns - i * b) for i in range((Ns + b - 1) // b)], dtype=np.int64)
+    n_ctx = np.array([min(b, Nc - c * b) for c in range((Nc + b - 1) // b)], dtype=np.int64)
+    total = 0
+    for x in range(full.shape[0]):
+        for h in range(full.shape[1]):
+            rows = int(n_src[full[x, h]].sum()) if full.shape[2] else 0
+            keys = Ns + (int(n_ctx[kept[x, h]].sum()) if kept.shape[2] else 0)
+            total += 4 * d * rows * keys
+    return total
+
+
+def cpu_baseline(w, Q, K, V, gamma, heads):
+    """The fp64 oracle on `heads` heads of the same inputs, scaled to the layer."""
+    from oracle import isa_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: single-threaded BLAS assumed
+        cores = 1
+    t0 = time.perf_counter()
+    for h in range(heads):
+        p = orc.oracle_plan_head(Q[0, h], K[0, h], V[0, h], w.b, w.rho, gamma)
+        orc.oracle_forward_head(Q[0, h], K[0, h], V[0, h], w.b, p["kept_ctx"], p["full_q"])
+    dt = time.perf_counter() - t0
+    per_layer = dt / heads * w.H * w.B
+    return {"value": w.B * w.Ns / per_layer, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d of %d heads of the same inputs (plan + forward, fp64 NumPy), %.1f s, scaled by H/%d"
+                      % (heads, w.H, dt, heads)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the ISA path here runs on a single MI355X with no "
+              "sharding or collectives (--gpus %d requested)" % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_context_amd import isa
+    from sparse_attention_context_amd.configs import BY_NAME
+    from sparse_attention_context_amd.synth import workload_inputs
+
+    w = BY_NAME[args.workload]
+    gamma = w.gamma if args.gamma is None else args.gamma
+    log("workload %s B=%d H=%d d=%d Ns=%d Nc=%d b=%d rho=%g gamma=%g %s" %
+        (w.name, w.B, w.H, w.d, w.Ns, w.Nc, w.b, w.rho, gamma, w.dtype))
+    Q, K, V = workload_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    Qd = torch.from_numpy(Q).to(dev).to(dt)
+    Kd = torch.from_numpy(K).to(dev).to(dt)
+    Vd = torch.from_numpy(V).to(dev).to(dt)
+    O = torch.empty_like(Qd)
+    desc = isa.desc_for(Qd, Kd, w.b, w.rho, gamma)
+    ws = isa.new_workspace(desc, dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log("inputs resident: %.1f MB" % ((Qd.numel() + Kd.numel() + Vd.numel()) * Qd.element_size() / 1e6))
+
+    def step():
+        isa.attention(Qd, Kd, Vd, w.b, w.rho, gamma, out=O, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log("isa_attention: %.3f ms/call" % ms)
+    views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, gamma)
+    counts = views["counts"]
+
+    # per-stage durations: events between the stages of the same stream
+    stage_ms = {}
+    if not args.no_stages:
+        names = list(isa.ATTENTION_STAGES)
+        if counts["kq"] == counts["nb_s"]:
+            names[names.index("sharp_taylor")] = "sharp"
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            for i, name in enumerate(names):
+                evs[s][i].record(stream)
+                isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, gamma, out=O)
+            evs[s][-1].record(stream)
+        torch.cuda.synchronize()
+        for i, name in enumerate(names):
+            stage_ms[name] = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+        log("stages: " + ", ".join("%s %.3f" % kv for kv in stage_ms.items()))
+
+    dense_ms = None
+    if not args.no_dense and w.dtype == "bf16":
+        isa.dense_forward(Qd, Kd, Vd, out=O)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_steps):
+            isa.dense_forward(Qd, Kd, Vd, out=O)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_steps
+        log("isa_dense_forward: %.3f ms/call" % dense_ms)
+
+    # roofline of the dominant kernel (full attention)
+    flops = full_route_flops(views, w, gamma)
+    full_ms = stage_ms.get("full")
+    roofline = None
+    if full_ms and flops:
+        achieved = flops / (full_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "isa_attn_kernel (full route, gathered K/V)", "flops_per_launch": flops,
+                    "avg_launch_ms": round(full_ms, 4)}
+    dense_flops = 4 * w.d * w.Ns * (w.Ns + w.Nc) * w.B * w.H
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu oracle on %d heads ..." % args.cpu_heads)
+        cpu = cpu_baseline(w, Q, K, V, gamma, args.cpu_heads)
+        log("cpu oracle: %.1f queries/s" % cpu["value"])
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.B * w.Ns / (ms * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, context keys scaled, sharpened queries)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Ns": w.Ns, "Nc": w.Nc, "b": w.b,
+                   "rho": w.rho, "gamma": gamma, "kc": counts["kc"], "kq": counts["kq"]},
+        "dense_ms": None if dense_ms is None else round(dense_ms, 4),
+        "dense_over_isa": None if dense_ms is None else round(dense_ms / ms, 3),
+        "latency_reduction_vs_dense": None if dense_ms is None else round(1 - ms / dense_ms, 4),
+        "dense_tflops": None if dense_ms is None else round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

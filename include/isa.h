@@ -1,0 +1,185 @@
+/*
+ * isa.h -- C-ABI of the MI355X (gfx950) In-context Sparse Attention library.
+ *
+ * The operation is the forward pass of In-context Sparse Attention (ISA) as
+ * named in "Lightning Unified Video Editing via In-Context Sparse Attention"
+ * (chatpaper.ai page), English abstract: source-video query tokens attend
+ * over the source tokens concatenated with context (reference) tokens;
+ * low-saliency context is pruned by a pre-selection step; query blocks are
+ * grouped by query sharpness, the sharp (high-error) ones going to exact full
+ * attention and the rest to 0-th order Taylor sparse attention over pooled
+ * key blocks.  The abstract gives no formulas; this library computes:
+ *
+ *   blocks     each of the source rows [0,Ns) and context rows [Ns,Ns+Nc) is
+ *              cut into blocks of b rows from its own start (last one short);
+ *              block j has count n_j and mean key kbar_j, mean value vbar_j;
+ *              pooled query qbar_i is the mean query of source block i.
+ *   saliency   sal_c = sum_i P_i(c), P_i the n-weighted softmax of qbar_i
+ *              over all key blocks: n_j exp(qbar_i.kbar_j/sqrt d) / sum.
+ *   pre-select keep kc = ceil(rho*nb_c - 1e-9) context blocks, highest sal
+ *              first, ties to the lower index.  Kept key set = all source
+ *              blocks + kept context blocks.
+ *   sharpness  sh_i = mean over queries q of block i of max_j P_j(q), the
+ *              n-weighted softmax of q over the kept blocks.
+ *   grouping   kq = ceil(gamma*nb_s - 1e-9) query blocks with the highest sh
+ *              (ties to the lower index) take the full route, the rest Taylor.
+ *   full       o = softmax(q K^T/sqrt d) V over every token of the kept set.
+ *   Taylor     o = sum_j n_j e^{q.kbar_j/sqrt d} vbar_j / sum_j n_j e^{...}
+ *              over the kept blocks (exp(q.k_t) ~ exp(q.kbar_j) inside j).
+ *   merge      every source row of O is written by its block's route.
+ *
+ * Tensors (device memory, caller-owned, contiguous, d fastest):
+ *   Q [B,H,Ns,d], K and V [B,H,Ns+Nc,d] (rows [0,Ns) source, [Ns,Ns+Nc)
+ *   context), O [B,H,Ns,d]; all of element type desc->dtype.
+ *   Pointers must be 16-byte aligned.  Context-token query rows are not
+ *   computed.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Every call only enqueues work on that stream: no host
+ * synchronisation, no device allocation, no printing.  Results are
+ * deterministic (no floating-point atomics).
+ *
+ * Workspace: caller-owned device memory of isa_workspace_size() bytes,
+ * 256-byte aligned.  isa_plan() leaves the plan (pooled blocks, scores and
+ * index lists) in it; isa_forward() reads it.  It must stay alive and
+ * unmodified until the work that reads it has completed on the stream.
+ *
+ * Errors: every call validates its arguments on the host before enqueuing
+ * anything, so a call that returns an error has launched no work and left O
+ * untouched, except ISA_ERR_DEVICE, which reports a failed launch (the text
+ * of the HIP error is then available from isa_last_error()).
+ */
+#ifndef ISA_H_
+#define ISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum isa_status {
+  ISA_OK = 0,
+  ISA_ERR_INVALID_ARGUMENT = 1, /* null pointer, rho/gamma not in [0,1] or NaN,
+                                   Ns < 1, Nc < 0, B or H < 1, b < 1, misaligned */
+  ISA_ERR_UNSUPPORTED = 2,      /* d not 64/128, b > 256, unknown dtype,
+                                   sizes beyond int32 row indexing */
+  ISA_ERR_WORKSPACE = 3,        /* workspace too small or not 256-byte aligned */
+  ISA_ERR_DEVICE = 4            /* a kernel launch failed; see isa_last_error() */
+} isa_status;
+
+typedef enum isa_dtype { ISA_BF16 = 0, ISA_F32 = 1 } isa_dtype;
+
+/* Problem description.  rho and gamma are doubles so that the kept counts
+ * ceil(f*n - 1e-9) are evaluated exactly as documented. */
+typedef struct isa_desc {
+  int32_t B;      /* batch, >= 1 */
+  int32_t H;      /* heads, >= 1 */
+  int32_t Ns;     /* source (query) rows, >= 1 */
+  int32_t Nc;     /* context rows, >= 0 */
+  int32_t d;      /* head width, 64 or 128 */
+  int32_t b;      /* block size in tokens, 1..256 */
+  double rho;     /* fraction of context blocks kept, in [0,1] */
+  double gamma;   /* fraction of query blocks sent to full attention, in [0,1] */
+  int32_t dtype;  /* isa_dtype of Q, K, V and O */
+} isa_desc;
+
+/* Derived counts (host values). */
+typedef struct isa_counts {
+  int32_t nb_s;        /* source (query) blocks, ceil(Ns/b) */
+  int32_t nb_c;        /* context blocks, ceil(Nc/b) */
+  int32_t kc;          /* kept context blocks */
+  int32_t kq;          /* query blocks on the full route */
+  int32_t m_kept;      /* kept key blocks, nb_s + kc */
+  int32_t reserved;
+  int64_t full_keys;   /* key tokens seen by a full-route query: Ns + kept context tokens
+                          (an upper bound: a kept short tail block counts b) */
+} isa_counts;
+
+/* Device pointers into a planned workspace (isa_plan_views).  Shapes are
+ * per (batch, head) slice, slices stored one after another in [B,H] order.
+ * Lists are ascending int32. */
+typedef struct isa_plan_view {
+  const float* qbar;       /* [B,H,nb_s,d]      pooled source queries */
+  const float* kbar;       /* [B,H,nb_s+nb_c,d] pooled keys, source blocks first */
+  const float* vbar;       /* [B,H,nb_s+nb_c,d] pooled values (context entries of
+                              blocks that are not kept are not computed) */
+  const double* sal;       /* [B,H,nb_c]  context saliency */
+  const int32_t* kept_ctx; /* [B,H,kc]    kept context block indices */
+  const double* sh;        /* [B,H,nb_s]  query-block sharpness */
+  const int32_t* full_q;   /* [B,H,kq]    query blocks on the full route */
+  const int32_t* taylor_q; /* [B,H,nb_s-kq] query blocks on the Taylor route */
+  isa_counts counts;
+} isa_plan_view;
+
+/* The steps of the layer, in the order isa_attention runs them.  Each stage
+ * is one kernel launch and reads what the earlier stages left in the
+ * workspace (same desc, same inputs); a stage with nothing to do for the
+ * shape (e.g. saliency with Nc = 0) enqueues nothing. */
+typedef enum isa_stage {
+  ISA_STAGE_POOL = 0,         /* block means: source Q, every K block, source V (pooling) */
+  ISA_STAGE_SALIENCY = 1,     /* per-workgroup column sums of the pooled softmax (saliency) */
+  ISA_STAGE_SELECT_CTX = 2,   /* sal, kept_ctx (top-rho) and the context key-row table */
+  ISA_STAGE_POOL_KEPT_V = 3,  /* block means of V for the kept context blocks */
+  ISA_STAGE_PACK = 4,         /* kept pooled keys (bf16 hi/lo), values and log2 n_j */
+  ISA_STAGE_SHARP_TAYLOR = 5, /* per-row peak probability + Taylor output of every row into O */
+  ISA_STAGE_SHARP = 6,        /* per-row peak probability only (sharpness) */
+  ISA_STAGE_SELECT_Q = 7,     /* sh, full_q / taylor_q (top-gamma) and query-row tables */
+  ISA_STAGE_TAYLOR = 8,       /* Taylor output of the Taylor-route rows into O */
+  ISA_STAGE_FULL = 9          /* full attention of the full-route rows into O (merge by row) */
+} isa_stage;
+
+/* Runs one stage.  isa_plan = POOL, SALIENCY, SELECT_CTX, POOL_KEPT_V, PACK,
+ * SHARP, SELECT_Q; isa_forward = TAYLOR, FULL; isa_attention = POOL ..
+ * PACK, SHARP_TAYLOR, SELECT_Q, FULL.  O may be NULL for stages that do not
+ * write it.  Unknown stage: ISA_ERR_INVALID_ARGUMENT. */
+isa_status isa_run_stage(const isa_desc* desc, int stage, const void* Q, const void* K, const void* V,
+                         void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Counts implied by *desc (validates it).  Defined by the readings above. */
+isa_status isa_get_counts(const isa_desc* desc, isa_counts* out);
+
+/* Bytes of workspace isa_plan / isa_forward / isa_attention need for *desc. */
+isa_status isa_workspace_size(const isa_desc* desc, size_t* bytes);
+
+/* Selection half: pooling, context saliency and pre-selection, query
+ * sharpness and grouping.  Reads Q, K, V; writes only the workspace. */
+isa_status isa_plan(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Output half: given a workspace planned by isa_plan with the same desc and
+ * inputs, writes every source row of O (Taylor rows, then full rows). */
+isa_status isa_forward(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                       void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer in one call: plan and forward, with the sharpness pass
+ * also producing the Taylor output of every row, which the full route then
+ * overwrites for its rows.  Same O and same plan contents as
+ * isa_plan + isa_forward. */
+isa_status isa_attention(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                         void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dense attention of all Ns source queries over all Ns+Nc keys with the same
+ * flash-attention kernel as the full route (the library's own dense
+ * baseline); rho, gamma and b are ignored.  Needs no workspace.  This is the
+ * global self-attention softmax(q k^T / sqrt d) v of the intelliparadigm.com
+ * page "深度学习注意力机制：全局与时间注意力的计算效率对比", section 1. */
+isa_status isa_dense_forward(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                             void* O, void* stream);
+
+/* Device pointers to the plan held in a workspace (no device access). */
+isa_status isa_plan_views(const isa_desc* desc, void* workspace, size_t workspace_bytes,
+                          isa_plan_view* out);
+
+/* Static text for a status code. */
+const char* isa_status_string(isa_status status);
+
+/* Text of the last device error seen by this thread ("" if none). */
+const char* isa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISA_H_ */

@@ -1,0 +1,135 @@
+// C-ABI entry points declared in include/isa.h.  Each validates on the
+// host, then enqueues the kernel chain on the caller's stream.
+#include <stdio.h>
+
+#include "isa_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+isa_status device_status(hipError_t e) {
+  if (e == hipSuccess) return ISA_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s (%d)", hipGetErrorString(e), (int)e);
+  return ISA_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+isa_status check_io(const void* Q, const void* K, const void* V, const void* O, bool need_o) {
+  if (!Q || !K || !V || (need_o && !O)) return ISA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || (need_o && !aligned16(O)))
+    return ISA_ERR_INVALID_ARGUMENT;
+  return ISA_OK;
+}
+
+isa_status check_ws(const isa::Layout& L, const void* ws, size_t bytes) {
+  if (!ws) return ISA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)ws % isa::kWsAlign) != 0 || bytes < L.total) return ISA_ERR_WORKSPACE;
+  return ISA_OK;
+}
+
+#define ISA_RUN(call)                             \
+  do {                                            \
+    isa_status st_ = device_status(call);         \
+    if (st_ != ISA_OK) return st_;                \
+  } while (0)
+
+// Pooling, saliency, context pre-selection and packing of the kept set.
+isa_status select_context(const isa::Layout& L, const isa::Bufs& B, hipStream_t s) {
+  ISA_RUN(isa::launch_pool(L, B, 0, s));
+  ISA_RUN(isa::launch_saliency(L, B, s));
+  ISA_RUN(isa::launch_select_ctx(L, B, s));
+  if (L.kc > 0) ISA_RUN(isa::launch_pool(L, B, 1, s));
+  ISA_RUN(isa::launch_pack(L, B, s));
+  return ISA_OK;
+}
+
+}  // namespace
+
+extern "C" isa_status isa_plan(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, nullptr, false)) != ISA_OK) return st;
+  if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
+  const isa::Bufs B{Q, K, V, nullptr, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = select_context(L, B, s)) != ISA_OK) return st;
+  ISA_RUN(isa::launch_pooled_attention(L, B, 1, s));
+  ISA_RUN(isa::launch_select_q(L, B, s));
+  return ISA_OK;
+}
+
+extern "C" isa_status isa_forward(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                                  void* O, void* workspace, size_t workspace_bytes, void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
+  if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
+  const isa::Bufs B{Q, K, V, O, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  if (L.taylor_rows > 0) ISA_RUN(isa::launch_pooled_attention(L, B, 2, s));
+  if (L.kq > 0) ISA_RUN(isa::launch_full_attention(L, B, false, s));
+  return ISA_OK;
+}
+
+extern "C" isa_status isa_attention(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                                    void* O, void* workspace, size_t workspace_bytes, void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
+  if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
+  const isa::Bufs B{Q, K, V, O, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = select_context(L, B, s)) != ISA_OK) return st;
+  // sharpness of every row; unless every block goes to full attention the
+  // same pass also writes the Taylor output of every row
+  ISA_RUN(isa::launch_pooled_attention(L, B, L.kq == L.nb_s ? 1 : 0, s));
+  ISA_RUN(isa::launch_select_q(L, B, s));
+  if (L.kq > 0) ISA_RUN(isa::launch_full_attention(L, B, false, s));
+  return ISA_OK;
+}
+
+extern "C" isa_status isa_dense_forward(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                                        void* O, void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
+  const isa::Bufs B{Q, K, V, O, nullptr};
+  ISA_RUN(isa::launch_full_attention(L, B, true, (hipStream_t)stream));
+  return ISA_OK;
+}
+
+extern "C" isa_status isa_run_stage(const isa_desc* desc, int stage, const void* Q, const void* K,
+                                    const void* V, void* O, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if (stage < ISA_STAGE_POOL || stage > ISA_STAGE_FULL) return ISA_ERR_INVALID_ARGUMENT;
+  const bool writes_o = stage == ISA_STAGE_SHARP_TAYLOR || stage == ISA_STAGE_TAYLOR || stage == ISA_STAGE_FULL;
+  if ((st = check_io(Q, K, V, O, writes_o)) != ISA_OK) return st;
+  if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
+  const isa::Bufs B{Q, K, V, O, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  switch (stage) {
+    case ISA_STAGE_POOL: ISA_RUN(isa::launch_pool(L, B, 0, s)); break;
+    case ISA_STAGE_SALIENCY: ISA_RUN(isa::launch_saliency(L, B, s)); break;
+    case ISA_STAGE_SELECT_CTX: ISA_RUN(isa::launch_select_ctx(L, B, s)); break;
+    case ISA_STAGE_POOL_KEPT_V: if (L.kc > 0) ISA_RUN(isa::launch_pool(L, B, 1, s)); break;
+    case ISA_STAGE_PACK: ISA_RUN(isa::launch_pack(L, B, s)); break;
+    case ISA_STAGE_SHARP_TAYLOR: ISA_RUN(isa::launch_pooled_attention(L, B, 0, s)); break;
+    case ISA_STAGE_SHARP: ISA_RUN(isa::launch_pooled_attention(L, B, 1, s)); break;
+    case ISA_STAGE_SELECT_Q: ISA_RUN(isa::launch_select_q(L, B, s)); break;
+    case ISA_STAGE_TAYLOR: if (L.taylor_rows > 0) ISA_RUN(isa::launch_pooled_attention(L, B, 2, s)); break;
+    case ISA_STAGE_FULL: if (L.kq > 0) ISA_RUN(isa::launch_full_attention(L, B, false, s)); break;
+  }
+  return ISA_OK;
+}
+
+extern "C" const char* isa_last_error(void) { return g_last_error; }

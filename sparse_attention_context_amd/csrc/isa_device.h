@@ -1,0 +1,87 @@
+// Device-side helpers shared by the ISA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace isa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bfloat16 storage in global memory
+
+// ---------------------------------------------------------------------------
+// element conversions
+
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t to_bf16(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(bf16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return to_bf16(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// ---------------------------------------------------------------------------
+// MFMA operand types: 8 contraction elements per lane.
+//
+// For a 32x32 output tile, lane l holds A[row l%32][k 8*(l/32)+0..7] and
+// B[k 8*(l/32)+0..7][col l%32]; the accumulator reg r of lane l is
+// D[row 8*(r/4) + 4*(l/32) + r%4][col l%32].  bf16 uses one
+// v_mfma_f32_32x32x16_bf16; f32 uses eight v_mfma_f32_32x32x2_f32, the j-th
+// contracting element j of both halves, so both types share one register
+// layout.
+
+template <typename T> struct Operand;
+template <> struct Operand<bf16_t> { typedef bf16x8 type; };
+template <> struct Operand<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32(const f32x8& a, const f32x8& b, f32x16 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+// 8 probabilities -> B operand of the P.V product.
+__device__ __forceinline__ void make_operand(const float* p, bf16x8& out) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = (__bf16)p[j];
+}
+__device__ __forceinline__ void make_operand(const float* p, f32x8& out) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = p[j];
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte LDS chunk swizzle.  A tile row of `cpr` 16-byte chunks stores
+// logical chunk c at physical chunk c ^ f(row): sixteen consecutive rows
+// read at one logical chunk hit sixteen distinct bank groups.
+__device__ __forceinline__ int swz(int c, int row, int cpr) {
+  return cpr >= 16 ? (c ^ (row & 15)) : (c ^ (((row >> 1) ^ (row >> 4)) & 7));
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup id remap so that consecutive logical workgroups (which share a
+// head's keys) land on the same XCD: the hardware deals workgroups to the
+// 8 XCDs round-robin.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = bid & 7, s = bid >> 3;
+  return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+}  // namespace isa

@@ -1,0 +1,48 @@
+// Launchers of the ISA kernels (host side).  Each enqueues on `stream` and
+// returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "isa_layout.h"
+
+namespace isa {
+
+// Pointers of one call: inputs, output and the carved workspace.
+struct Bufs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  char* ws;
+};
+
+// Block mean-pool.  pass 0: source query blocks, every key block and the
+// source value blocks; pass 1: value blocks of the kept context blocks.
+hipError_t launch_pool(const Layout& L, const Bufs& B, int pass, hipStream_t s);
+
+// Context saliency partial column sums, one workgroup per kSalRows pooled
+// queries of one head.
+hipError_t launch_saliency(const Layout& L, const Bufs& B, hipStream_t s);
+
+// Context top-rho: sums the partials into sal, selects kept_ctx and writes
+// the full-route context row table.
+hipError_t launch_select_ctx(const Layout& L, const Bufs& B, hipStream_t s);
+
+// Packs the kept pooled blocks for the pooled-attention kernel.
+hipError_t launch_pack(const Layout& L, const Bufs& B, hipStream_t s);
+
+// Query top-gamma: block means of the per-row peaks into sh, selects full_q /
+// taylor_q and writes both query row tables.
+hipError_t launch_select_q(const Layout& L, const Bufs& B, hipStream_t s);
+
+// Pooled attention over the kept blocks.  mode 0: every source row, writes
+// O (Taylor output) and the per-row peak probability; mode 1: every source
+// row, peak only; mode 2: Taylor-route rows only, writes O.
+hipError_t launch_pooled_attention(const Layout& L, const Bufs& B, int mode, hipStream_t s);
+
+// Exact attention.  dense=false: full-route rows over the kept key tokens;
+// dense=true: every source row over every key row (no workspace needed).
+hipError_t launch_full_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s);
+
+}  // namespace isa

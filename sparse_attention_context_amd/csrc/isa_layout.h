@@ -1,0 +1,38 @@
+// Host-side plan of one ISA call: argument checks, block counts and the
+// carve-up of the caller's workspace.  No HIP types; compiled into the
+// library and usable from plain C++.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/isa.h"
+
+namespace isa {
+
+constexpr int kTileKeys = 64;      // keys per attention tile
+constexpr int kSalRows = 16;       // pooled queries per saliency workgroup
+constexpr size_t kWsAlign = 256;
+
+struct Layout {
+  int64_t BH;          // B*H slices
+  int Ns, Nc, Nk, d, b, es;   // es = element size of Q/K/V/O
+  int nb_s, nb_c, M;   // source blocks, context blocks, all blocks
+  int kc, kq, mk;      // kept context blocks, full-route query blocks, kept blocks
+  int mk_pad;          // mk rounded up to kTileKeys
+  int tail_s, tail_c;  // rows in the last source / context block
+  int sal_tiles;       // ceil(nb_s / kSalRows)
+  int64_t ctx_tok;     // kc*b: context key tokens of the full route (with tail padding)
+  int64_t full_rows;   // kq*b virtual full-route query rows
+  int64_t taylor_rows; // (nb_s-kq)*b virtual Taylor-route query rows
+  // byte offsets into the workspace
+  size_t off_qbar, off_kbar, off_vbar, off_salp, off_sal, off_kept;
+  size_t off_pkhi, off_pklo, off_pv, off_pbias, off_ctxrows;
+  size_t off_peak, off_sh, off_fullq, off_taylq, off_qrows_full, off_qrows_taylor;
+  size_t total;
+};
+
+// Validates *desc and fills *L.  Returns ISA_OK or the error of isa.h.
+isa_status make_layout(const isa_desc* desc, Layout* L);
+
+}  // namespace isa

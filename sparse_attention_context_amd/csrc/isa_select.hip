@@ -1,0 +1,339 @@
+// Top-k selection, compaction and packing of the kept key set.
+//
+// Both selections of ISA -- the context pre-selection that prunes redundant
+// context and the dynamic query grouping that sends high-error (sharp) query
+// blocks to full attention (Lightning Unified Video Editing via In-Context
+// Sparse Attention, English abstract) -- keep the k highest scores.  The
+// order is total: score descending, then index ascending, so ties go to the
+// lower index.  Lists are emitted in ascending index order.
+//
+// One workgroup (4 waves) per (batch, head).  Scores are fp64 mapped to
+// order-preserving 64-bit keys, so the selection itself is integer work:
+//   n <= kRankMax: every element counts the elements that beat it (LDS);
+//   larger n:      MSB-first radix select, 8 passes of 8 bits with an LDS
+//                  histogram, finds the k-th key T and how many keys equal
+//                  to T are still needed.
+// Compaction walks the indices in 256-wide chunks; a ballot + popcount
+// prefix inside each wave and the wave totals give every element its slot.
+#include "isa_device.h"
+#include "isa_kernels.h"
+
+namespace isa {
+
+constexpr int kRankMax = 1024;
+
+__device__ __forceinline__ uint64_t order_key(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+struct SelectSmem {
+  uint64_t keys[kRankMax];
+  int hist[256];
+  int wtot[4];
+  int wtot2[4];
+  int digit;
+  int above;
+};
+
+// Exclusive prefix count of `f` over the workgroup (thread order); *total
+// gets the workgroup sum.  Contains barriers: call from every thread.
+__device__ __forceinline__ int block_prefix(bool f, int* wtot, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t bal = __ballot(f);
+  const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) wtot[w] = __popcll(bal);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    off += i < w ? wtot[i] : 0;
+    tot += wtot[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return off + pre;
+}
+
+// Inclusive prefix sum of v over the workgroup (thread order).
+__device__ __forceinline__ int block_inclusive_sum(int v, int* wtot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wtot[w] = v;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) off += i < w ? wtot[i] : 0;
+  __syncthreads();
+  return v + off;
+}
+
+// Selects the k best of sc[0..n) and writes them ascending to sel[0..k);
+// when rest is non-null the others go ascending to rest[0..n-k).
+__device__ void select_topk(const double* sc, int n, int k, int* sel, int* rest, SelectSmem& sm) {
+  const int tid = threadIdx.x;
+  int mode;  // 0: none, 1: all, 2: rank, 3: radix
+  if (k <= 0) mode = 0;
+  else if (k >= n) mode = 1;
+  else if (n <= kRankMax) mode = 2;
+  else mode = 3;
+
+  uint64_t T = 0;
+  int need = 0;
+  if (mode == 2) {
+    for (int i = tid; i < n; i += 256) sm.keys[i] = order_key(sc[i]);
+    __syncthreads();
+  } else if (mode == 3) {
+    uint64_t prefix = 0, mask = 0;
+    need = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      sm.hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += 256) {
+        const uint64_t key = order_key(sc[i]);
+        if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255], 1);
+      }
+      __syncthreads();
+      // suffix sums: thread t owns digit 255 - t
+      const int dg = 255 - tid;
+      const int cnt = sm.hist[dg];
+      const int suf = block_inclusive_sum(cnt, sm.wtot);  // keys with digit >= dg
+      if (suf >= need && suf - cnt < need) {
+        sm.digit = dg;
+        sm.above = suf - cnt;
+      }
+      __syncthreads();
+      prefix |= (uint64_t)sm.digit << shift;
+      mask |= 0xffull << shift;
+      need -= sm.above;
+      __syncthreads();
+    }
+    T = prefix;
+  }
+
+  int base_sel = 0, base_eq = 0;
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    const int i = c0 + tid;
+    const bool valid = i < n;
+    bool f = false;
+    if (mode == 1) {
+      f = valid;
+    } else if (mode == 2) {
+      if (valid) {
+        const uint64_t ki = sm.keys[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) {
+          const uint64_t kj = sm.keys[j];
+          rank += (kj > ki) || (kj == ki && j < i);
+        }
+        f = rank < k;
+      }
+    } else if (mode == 3) {
+      const uint64_t key = valid ? order_key(sc[i]) : 0;
+      const bool eq = valid && key == T;
+      int eq_tot;
+      const int eq_pos = base_eq + block_prefix(eq, sm.wtot2, &eq_tot);
+      base_eq += eq_tot;
+      f = valid && (key > T || (eq && eq_pos < need));
+    }
+    int tot;
+    const int pos = block_prefix(f, sm.wtot, &tot);
+    if (valid) {
+      const int ps = base_sel + pos, pr = i - ps;
+      if (f) {
+        if (ps < k) sel[ps] = i;
+      } else if (rest && pr < n - k) {
+        rest[pr] = i;
+      }
+    }
+    base_sel += tot;
+  }
+}
+
+struct SelArgs {
+  const double* salp;
+  double* sal;
+  int* kept;
+  int* ctx_rows;
+  const float* peak;
+  double* sh;
+  int* full_q;
+  int* taylor_q;
+  int* qrows_full;
+  int* qrows_taylor;
+  int Ns, Nc, b, nb_s, nb_c, kc, kq, sal_tiles, tail_s;
+};
+
+__global__ __launch_bounds__(256) void isa_select_ctx_kernel(SelArgs a) {
+  __shared__ SelectSmem sm;
+  const long long bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  double* sal = a.sal + bh * a.nb_c;
+  const double* part = a.salp + bh * (long long)a.sal_tiles * a.nb_c;
+  for (int c = tid; c < a.nb_c; c += 256) {
+    double s = 0.0;
+    for (int t = 0; t < a.sal_tiles; ++t) s += part[(long long)t * a.nb_c + c];
+    sal[c] = s;
+  }
+  __syncthreads();
+  int* kept = a.kept + bh * a.kc;
+  select_topk(sal, a.nb_c, a.kc, kept, nullptr, sm);
+  __syncthreads();
+  // full-route context key rows: kept block kb covers rows Ns + kb*b + [0, b),
+  // -1 past the end of a short last block
+  const long long ntok = (long long)a.kc * a.b;
+  int* rows = a.ctx_rows + bh * ntok;
+  for (long long t = tid; t < ntok; t += 256) {
+    const int kb = kept[t / a.b];
+    const int r = kb * a.b + (int)(t % a.b);
+    rows[t] = (kb >= 0 && kb < a.nb_c && r < a.Nc) ? a.Ns + r : -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
+  __shared__ SelectSmem sm;
+  const long long bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  double* sh = a.sh + bh * a.nb_s;
+  const float* pk = a.peak + bh * a.Ns;
+  for (int i = tid; i < a.nb_s; i += 256) {
+    const int r0 = i * a.b;
+    const int n = min(a.b, a.Ns - r0);
+    double s = 0.0;
+    for (int r = 0; r < n; ++r) s += (double)pk[r0 + r];
+    sh[i] = s / n;
+  }
+  __syncthreads();
+  int* fq = a.full_q + bh * a.kq;
+  int* tq = a.taylor_q + bh * (a.nb_s - a.kq);
+  select_topk(sh, a.nb_s, a.kq, fq, tq, sm);
+  __syncthreads();
+  const long long nf = (long long)a.kq * a.b;
+  const long long nt = (long long)(a.nb_s - a.kq) * a.b;
+  int* rf = a.qrows_full + bh * nf;
+  int* rt = a.qrows_taylor + bh * nt;
+  for (long long v = tid; v < nf; v += 256) {
+    const int qb = fq[v / a.b];
+    const int r = qb * a.b + (int)(v % a.b);
+    rf[v] = (qb >= 0 && qb < a.nb_s && r < a.Ns) ? r : -1;
+  }
+  for (long long v = tid; v < nt; v += 256) {
+    const int qb = tq[v / a.b];
+    const int r = qb * a.b + (int)(v % a.b);
+    rt[v] = (qb >= 0 && qb < a.nb_s && r < a.Ns) ? r : -1;
+  }
+}
+
+static SelArgs sel_args(const Layout& L, const Bufs& B) {
+  SelArgs a;
+  a.salp = (const double*)(B.ws + L.off_salp);
+  a.sal = (double*)(B.ws + L.off_sal);
+  a.kept = (int*)(B.ws + L.off_kept);
+  a.ctx_rows = (int*)(B.ws + L.off_ctxrows);
+  a.peak = (const float*)(B.ws + L.off_peak);
+  a.sh = (double*)(B.ws + L.off_sh);
+  a.full_q = (int*)(B.ws + L.off_fullq);
+  a.taylor_q = (int*)(B.ws + L.off_taylq);
+  a.qrows_full = (int*)(B.ws + L.off_qrows_full);
+  a.qrows_taylor = (int*)(B.ws + L.off_qrows_taylor);
+  a.Ns = L.Ns; a.Nc = L.Nc; a.b = L.b; a.nb_s = L.nb_s; a.nb_c = L.nb_c;
+  a.kc = L.kc; a.kq = L.kq; a.sal_tiles = L.sal_tiles; a.tail_s = L.tail_s;
+  return a;
+}
+
+hipError_t launch_select_ctx(const Layout& L, const Bufs& B, hipStream_t s) {
+  if (L.nb_c == 0) return hipSuccess;
+  hipLaunchKernelGGL(isa_select_ctx_kernel, dim3((unsigned)L.BH), dim3(256), 0, s, sel_args(L, B));
+  return hipGetLastError();
+}
+
+hipError_t launch_select_q(const Layout& L, const Bufs& B, hipStream_t s) {
+  hipLaunchKernelGGL(isa_select_q_kernel, dim3((unsigned)L.BH), dim3(256), 0, s, sel_args(L, B));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Packing of the kept key set for the pooled (Taylor / sharpness) attention:
+// row p < nb_s is source block p, row nb_s + i is context block kept[i],
+// rows mk..mk_pad-1 are zero with bias -inf.  The bias is log2(n_j), the
+// count weight of the n-weighted softmax in the exp2 domain.  bf16 inputs
+// store each pooled key as hi = bf16(k) and lo = bf16(k - hi): the two
+// bf16 products with a bf16 query carry the logit to about 2^-17 relative,
+// well inside what the sharpness selection needs.
+
+struct PackArgs {
+  const float* kbar;
+  const float* vbar;
+  const int* kept;
+  void* pkhi;
+  bf16_t* pklo;
+  void* pv;
+  float* pbias;
+  int nb_s, nb_c, M, kc, mk, mk_pad, b, tail_s, tail_c;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void isa_pack_kernel(PackArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long bh = blockIdx.y;
+  if (p >= a.mk_pad) return;
+  int j = -1;
+  if (p < a.nb_s) j = p;
+  else if (p < a.mk) {
+    const int c = a.kept[bh * a.kc + (p - a.nb_s)];
+    j = (c >= 0 && c < a.nb_c) ? a.nb_s + c : -1;
+  }
+  const long long src = (bh * a.M + (j < 0 ? 0 : j)) * D;
+  const long long dst = (bh * a.mk_pad + p) * D;
+  for (int e = lane; e < D; e += 64) {
+    const float k = j >= 0 ? a.kbar[src + e] : 0.f;
+    const float v = j >= 0 ? a.vbar[src + e] : 0.f;
+    if constexpr (sizeof(T) == 2) {
+      const bf16_t hi = to_bf16(k);
+      ((bf16_t*)a.pkhi)[dst + e] = hi;
+      a.pklo[dst + e] = to_bf16(k - to_f32(hi));
+      ((bf16_t*)a.pv)[dst + e] = to_bf16(v);
+    } else {
+      ((float*)a.pkhi)[dst + e] = k;
+      ((float*)a.pv)[dst + e] = v;
+    }
+  }
+  if (lane == 0) {
+    float bias = -INFINITY;
+    if (j >= 0) {
+      int n;
+      if (j < a.nb_s) n = j == a.nb_s - 1 ? a.tail_s : a.b;
+      else n = (j - a.nb_s) == a.nb_c - 1 ? a.tail_c : a.b;
+      bias = log2f((float)n);
+    }
+    a.pbias[bh * a.mk_pad + p] = bias;
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_pack_t(const Layout& L, const Bufs& B, hipStream_t s) {
+  PackArgs a;
+  a.kbar = (const float*)(B.ws + L.off_kbar);
+  a.vbar = (const float*)(B.ws + L.off_vbar);
+  a.kept = (const int*)(B.ws + L.off_kept);
+  a.pkhi = B.ws + L.off_pkhi;
+  a.pklo = (bf16_t*)(B.ws + L.off_pklo);
+  a.pv = B.ws + L.off_pv;
+  a.pbias = (float*)(B.ws + L.off_pbias);
+  a.nb_s = L.nb_s; a.nb_c = L.nb_c; a.M = L.M; a.kc = L.kc; a.mk = L.mk; a.mk_pad = L.mk_pad;
+  a.b = L.b; a.tail_s = L.tail_s; a.tail_c = L.tail_c;
+  hipLaunchKernelGGL((isa_pack_kernel<T, D>), dim3((L.mk_pad + 3) / 4, (unsigned)L.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const Layout& L, const Bufs& B, hipStream_t s) {
+  if (L.es == 2) return L.d == 128 ? launch_pack_t<bf16_t, 128>(L, B, s) : launch_pack_t<bf16_t, 64>(L, B, s);
+  return L.d == 128 ? launch_pack_t<float, 128>(L, B, s) : launch_pack_t<float, 64>(L, B, s);
+}
+
+}  // namespace isa

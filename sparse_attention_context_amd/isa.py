@@ -1,0 +1,218 @@
+"""ctypes binding to libisa.so (include/isa.h): argument marshalling only.
+
+PyTorch supplies device memory (``data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``); every step of the layer runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libisa.so")
+
+ISA_BF16 = 0
+ISA_F32 = 1
+
+STATUS = {0: "ISA_OK", 1: "ISA_ERR_INVALID_ARGUMENT", 2: "ISA_ERR_UNSUPPORTED", 3: "ISA_ERR_WORKSPACE",
+          4: "ISA_ERR_DEVICE"}
+
+EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "isa_attention",
+           "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_status_string", "isa_last_error"]
+
+# isa_stage values (include/isa.h)
+STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
+          "taylor", "full"]
+STAGE = {name: i for i, name in enumerate(STAGES)}
+# the stage sequence of isa_attention when some query blocks stay on the Taylor route
+ATTENTION_STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "select_q", "full"]
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Ns", ctypes.c_int32), ("Nc", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("b", ctypes.c_int32), ("rho", ctypes.c_double),
+                ("gamma", ctypes.c_double), ("dtype", ctypes.c_int32)]
+
+
+class Counts(ctypes.Structure):
+    _fields_ = [("nb_s", ctypes.c_int32), ("nb_c", ctypes.c_int32), ("kc", ctypes.c_int32),
+                ("kq", ctypes.c_int32), ("m_kept", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("full_keys", ctypes.c_int64)]
+
+
+class PlanView(ctypes.Structure):
+    _fields_ = [("qbar", ctypes.c_void_p), ("kbar", ctypes.c_void_p), ("vbar", ctypes.c_void_p),
+                ("sal", ctypes.c_void_p), ("kept_ctx", ctypes.c_void_p), ("sh", ctypes.c_void_p),
+                ("full_q", ctypes.c_void_p), ("taylor_q", ctypes.c_void_p), ("counts", Counts)]
+
+
+class IsaError(RuntimeError):
+    def __init__(self, fn, code, detail=""):
+        self.code = code
+        super().__init__("%s failed: %s%s" % (fn, STATUS.get(code, code), (" -- " + detail) if detail else ""))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libisa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.isa_get_counts.argtypes = [P(Desc), P(Counts)]
+        L.isa_workspace_size.argtypes = [P(Desc), P(sz)]
+        L.isa_plan.argtypes = [P(Desc), vp, vp, vp, vp, sz, vp]
+        L.isa_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp]
+        L.isa_attention.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp]
+        L.isa_dense_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp]
+        L.isa_plan_views.argtypes = [P(Desc), vp, sz, P(PlanView)]
+        L.isa_run_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
+        L.isa_status_string.argtypes = [ctypes.c_int]
+        L.isa_status_string.restype = ctypes.c_char_p
+        L.isa_last_error.argtypes = []
+        L.isa_last_error.restype = ctypes.c_char_p
+        for fn in EXPORTS[:8]:
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn, code):
+    if code != 0:
+        detail = lib().isa_last_error().decode() if code == 4 else ""
+        raise IsaError(fn, code, detail)
+
+
+def make_desc(B, H, Ns, Nc, d, b, rho, gamma, dtype):
+    dt = {torch.bfloat16: ISA_BF16, torch.float32: ISA_F32, "bf16": ISA_BF16, "f32": ISA_F32}.get(dtype, dtype)
+    return Desc(int(B), int(H), int(Ns), int(Nc), int(d), int(b), float(rho), float(gamma), int(dt))
+
+
+def desc_for(Q, K, b, rho, gamma):
+    """Descriptor of Q [B,H,Ns,d], K [B,H,Ns+Nc,d] (torch tensors)."""
+    B, H, Ns, d = Q.shape
+    return make_desc(B, H, Ns, K.shape[2] - Ns, d, b, rho, gamma, Q.dtype)
+
+
+def counts(desc):
+    c = Counts()
+    _check("isa_get_counts", lib().isa_get_counts(ctypes.byref(desc), ctypes.byref(c)))
+    return c
+
+
+def workspace_size(desc):
+    n = ctypes.c_size_t()
+    _check("isa_workspace_size", lib().isa_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _inputs(Q, K, V):
+    for t in (Q, K, V):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("Q, K, V must be contiguous device tensors")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise ValueError("Q, K, V must share one dtype")
+
+
+def new_workspace(desc, device):
+    return torch.empty(workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+def plan(Q, K, V, b, rho, gamma, workspace=None, stream=None):
+    """isa_plan: returns the workspace holding the plan."""
+    _inputs(Q, K, V)
+    desc = desc_for(Q, K, b, rho, gamma)
+    ws = new_workspace(desc, Q.device) if workspace is None else workspace
+    _check("isa_plan", lib().isa_plan(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(ws),
+                                      ws.numel(), _stream(stream)))
+    return ws
+
+
+def forward(Q, K, V, workspace, b, rho, gamma, out=None, stream=None):
+    """isa_forward on a planned workspace: returns O."""
+    _inputs(Q, K, V)
+    desc = desc_for(Q, K, b, rho, gamma)
+    O = torch.empty_like(Q) if out is None else out
+    _check("isa_forward", lib().isa_forward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                            _ptr(workspace), workspace.numel(), _stream(stream)))
+    return O
+
+
+def attention(Q, K, V, b, rho, gamma, out=None, workspace=None, stream=None):
+    """isa_attention (plan + forward in one call): returns (O, workspace)."""
+    _inputs(Q, K, V)
+    desc = desc_for(Q, K, b, rho, gamma)
+    ws = new_workspace(desc, Q.device) if workspace is None else workspace
+    O = torch.empty_like(Q) if out is None else out
+    _check("isa_attention", lib().isa_attention(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                                _ptr(ws), ws.numel(), _stream(stream)))
+    return O, ws
+
+
+def dense_forward(Q, K, V, out=None, stream=None):
+    """isa_dense_forward: dense attention of every source row over every key."""
+    _inputs(Q, K, V)
+    desc = desc_for(Q, K, 1, 1.0, 1.0)
+    O = torch.empty_like(Q) if out is None else out
+    _check("isa_dense_forward", lib().isa_dense_forward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
+                                                        _ptr(O), _stream(stream)))
+    return O
+
+
+def run_stage(stage, Q, K, V, workspace, b, rho, gamma, out=None, stream=None):
+    """isa_run_stage: one kernel of the layer (stage name or isa_stage value)."""
+    desc = desc_for(Q, K, b, rho, gamma)
+    code = STAGE[stage] if isinstance(stage, str) else int(stage)
+    _check("isa_run_stage", lib().isa_run_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
+                                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def plan_views(Q, K, workspace, b, rho, gamma):
+    """Tensor views of a planned workspace: dict of device tensors + counts."""
+    desc = desc_for(Q, K, b, rho, gamma)
+    v = PlanView()
+    _check("isa_plan_views", lib().isa_plan_views(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                                                  ctypes.byref(v)))
+    c = v.counts
+    B, H, _, d = Q.shape
+    base = workspace.data_ptr()
+
+    def view(ptr, dtype, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        esz = torch.empty(0, dtype=dtype).element_size()
+        off = ptr - base
+        return workspace[off:off + n * esz].view(dtype).view(*shape)
+
+    return {
+        "qbar": view(v.qbar, torch.float32, (B, H, c.nb_s, d)),
+        "kbar": view(v.kbar, torch.float32, (B, H, c.nb_s + c.nb_c, d)),
+        "vbar": view(v.vbar, torch.float32, (B, H, c.nb_s + c.nb_c, d)),
+        "sal": view(v.sal, torch.float64, (B, H, c.nb_c)),
+        "kept_ctx": view(v.kept_ctx, torch.int32, (B, H, c.kc)),
+        "sh": view(v.sh, torch.float64, (B, H, c.nb_s)),
+        "full_q": view(v.full_q, torch.int32, (B, H, c.kq)),
+        "taylor_q": view(v.taylor_q, torch.int32, (B, H, c.nb_s - c.kq)),
+        "counts": {"nb_s": c.nb_s, "nb_c": c.nb_c, "kc": c.kc, "kq": c.kq, "m_kept": c.m_kept,
+                   "full_keys": c.full_keys},
+    }
