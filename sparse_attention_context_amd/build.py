@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libisa.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 
-HIP_SOURCES = ["isa_pool.hip", "isa_score.hip", "isa_select.hip", "isa_attn.hip", "isa_abi.hip"]
+HIP_SOURCES = ["isa_pool.hip", "isa_score.hip", "isa_select.hip", "isa_attn.hip", "isa_flash.hip", "isa_abi.hip"]
 CXX_SOURCES = ["isa_layout.cpp"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

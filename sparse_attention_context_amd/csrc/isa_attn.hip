@@ -424,7 +424,7 @@ hipError_t launch_pooled_attention(const Layout& L, const Bufs& B, int mode, hip
 }
 
 hipError_t launch_full_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s) {
-  if (L.es == 2) return L.d == 128 ? full_t<bf16_t, 128>(L, B, dense, s) : full_t<bf16_t, 64>(L, B, dense, s);
+  if (L.es == 2) return launch_flash_attention(L, B, dense, s);
   return L.d == 128 ? full_t<float, 128>(L, B, dense, s) : full_t<float, 64>(L, B, dense, s);
 }
 

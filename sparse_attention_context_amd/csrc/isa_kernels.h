@@ -45,4 +45,8 @@ hipError_t launch_pooled_attention(const Layout& L, const Bufs& B, int mode, hip
 // dense=true: every source row over every key row (no workspace needed).
 hipError_t launch_full_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s);
 
+// bf16 pipelined flash attention (full route with split-K, or dense); used
+// by launch_full_attention for bf16 inputs.
+hipError_t launch_flash_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s);
+
 }  // namespace isa

@@ -17,6 +17,25 @@ static int kept_count(double f, int n) {
   return (int)c;
 }
 
+int choose_splits(int64_t units, int ntiles) {
+  if (units <= 0 || ntiles <= 1) return 1;
+  int best = 1;
+  double best_cost = 0;
+  for (int s = 1; s <= kMaxSplits && s <= ntiles; ++s) {
+    const int per = (ntiles + s - 1) / s;
+    if ((int64_t)per * (s - 1) >= ntiles) continue;  // an empty split
+    const double rounds = ceil((double)(units * s) / kCUs);
+    const double cost = rounds * (per + 3.0) + (s > 1 ? 0.02 * ntiles : 0.0);
+    if (s == 1 || cost < best_cost * 0.98) {
+      if (s == 1 || cost < best_cost) {
+        best = s;
+        best_cost = cost;
+      }
+    }
+  }
+  return best;
+}
+
 static size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 isa_status make_layout(const isa_desc* desc, Layout* L) {
@@ -53,6 +72,11 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   L->ctx_tok = (int64_t)L->kc * D.b;
   L->full_rows = (int64_t)L->kq * D.b;
   L->taylor_rows = (int64_t)(L->nb_s - L->kq) * D.b;
+  {
+    const int64_t row_tiles = (L->full_rows + kFlashRows - 1) / kFlashRows;
+    const int ntiles = (int)((D.Ns + L->ctx_tok + 63) / 64);
+    L->full_splits = L->es == 2 ? choose_splits(bh * row_tiles, ntiles) : 1;
+  }
 
   const size_t d = (size_t)D.d;
   const size_t pk_es = L->es;  // packed pooled keys/values: bf16 or f32
@@ -78,6 +102,11 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   take(&L->off_taylq, bh * (L->nb_s - L->kq) * 4);
   take(&L->off_qrows_full, bh * L->full_rows * 4);
   take(&L->off_qrows_taylor, bh * L->taylor_rows * 4);
+  {
+    const int64_t prow = L->full_splits > 1 ? bh * ((L->full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L->full_splits : 0;
+    take(&L->off_part_acc, prow * d * 4);
+    take(&L->off_part_ml, prow * 2 * 4);
+  }
   L->total = o;
   return ISA_OK;
 }

@@ -12,6 +12,17 @@ namespace isa {
 
 constexpr int kTileKeys = 64;      // keys per attention tile
 constexpr int kSalRows = 16;       // pooled queries per saliency workgroup
+#ifndef ISA_FLASH_WAVES
+#define ISA_FLASH_WAVES 8
+#endif
+#ifndef ISA_FLASH_PIPE
+#define ISA_FLASH_PIPE 0
+#endif
+constexpr int kFlashWaves = ISA_FLASH_WAVES;    // waves per full-attention workgroup
+constexpr int kFlashPipe = ISA_FLASH_PIPE;      // issue S(j+1) before the softmax of S(j)
+constexpr int kFlashRows = 32 * kFlashWaves;    // query rows per full-attention workgroup
+constexpr int kCUs = 256;          // compute units of the target GPU (split-K balance)
+constexpr int kMaxSplits = 8;
 constexpr size_t kWsAlign = 256;
 
 struct Layout {
@@ -25,14 +36,22 @@ struct Layout {
   int64_t ctx_tok;     // kc*b: context key tokens of the full route (with tail padding)
   int64_t full_rows;   // kq*b virtual full-route query rows
   int64_t taylor_rows; // (nb_s-kq)*b virtual Taylor-route query rows
+  int full_splits;     // key-range splits of the full-route attention (bf16)
   // byte offsets into the workspace
   size_t off_qbar, off_kbar, off_vbar, off_salp, off_sal, off_kept;
   size_t off_pkhi, off_pklo, off_pv, off_pbias, off_ctxrows;
   size_t off_peak, off_sh, off_fullq, off_taylq, off_qrows_full, off_qrows_taylor;
+  size_t off_part_acc, off_part_ml;
   size_t total;
 };
 
 // Validates *desc and fills *L.  Returns ISA_OK or the error of isa.h.
 isa_status make_layout(const isa_desc* desc, Layout* L);
+
+// Key-range splits for `units` workgroups of `ntiles` key tiles each, on
+// kCUs compute units running one workgroup each: the count that minimises
+// (rounds of workgroups) x (tiles per workgroup + fixed cost), 1 unless a
+// split saves at least 2%.
+int choose_splits(int64_t units, int ntiles);
 
 }  // namespace isa
