@@ -166,7 +166,7 @@ def main():
         achieved = flops / (full_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "kernel": "isa_attn_kernel (full route, gathered K/V)", "flops_per_launch": flops,
+                    "kernel": "isa_flash_kernel (full route, gathered K/V; split-K merge timed separately)", "flops_per_launch": flops,
                     "avg_launch_ms": round(full_ms, 4)}
     dense_flops = 4 * w.d * w.Ns * (w.Ns + w.Nc) * w.B * w.H
 

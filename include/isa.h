@@ -127,12 +127,14 @@ typedef enum isa_stage {
   ISA_STAGE_SHARP = 6,        /* per-row peak probability only (sharpness) */
   ISA_STAGE_SELECT_Q = 7,     /* sh, full_q / taylor_q (top-gamma) and query-row tables */
   ISA_STAGE_TAYLOR = 8,       /* Taylor output of the Taylor-route rows into O */
-  ISA_STAGE_FULL = 9          /* full attention of the full-route rows into O (merge by row) */
+  ISA_STAGE_FULL = 9,         /* full attention of the full-route rows: into O, or into
+                                 split partials when the key range is split */
+  ISA_STAGE_FULL_MERGE = 10   /* merges the full route's split partials into O (no-op unsplit) */
 } isa_stage;
 
 /* Runs one stage.  isa_plan = POOL, SALIENCY, SELECT_CTX, POOL_KEPT_V, PACK,
- * SHARP, SELECT_Q; isa_forward = TAYLOR, FULL; isa_attention = POOL ..
- * PACK, SHARP_TAYLOR, SELECT_Q, FULL.  O may be NULL for stages that do not
+ * SHARP, SELECT_Q; isa_forward = TAYLOR, FULL, FULL_MERGE; isa_attention =
+ * POOL .. PACK, SHARP_TAYLOR, SELECT_Q, FULL, FULL_MERGE.  O may be NULL for stages that do not
  * write it.  Unknown stage: ISA_ERR_INVALID_ARGUMENT. */
 isa_status isa_run_stage(const isa_desc* desc, int stage, const void* Q, const void* K, const void* V,
                          void* O, void* workspace, size_t workspace_bytes, void* stream);

@@ -72,7 +72,10 @@ extern "C" isa_status isa_forward(const isa_desc* desc, const void* Q, const voi
   const isa::Bufs B{Q, K, V, O, (char*)workspace};
   hipStream_t s = (hipStream_t)stream;
   if (L.taylor_rows > 0) ISA_RUN(isa::launch_pooled_attention(L, B, 2, s));
-  if (L.kq > 0) ISA_RUN(isa::launch_full_attention(L, B, false, s));
+  if (L.kq > 0) {
+    ISA_RUN(isa::launch_full_attention(L, B, false, s));
+    ISA_RUN(isa::launch_full_merge(L, B, s));
+  }
   return ISA_OK;
 }
 
@@ -90,7 +93,10 @@ extern "C" isa_status isa_attention(const isa_desc* desc, const void* Q, const v
   // same pass also writes the Taylor output of every row
   ISA_RUN(isa::launch_pooled_attention(L, B, L.kq == L.nb_s ? 1 : 0, s));
   ISA_RUN(isa::launch_select_q(L, B, s));
-  if (L.kq > 0) ISA_RUN(isa::launch_full_attention(L, B, false, s));
+  if (L.kq > 0) {
+    ISA_RUN(isa::launch_full_attention(L, B, false, s));
+    ISA_RUN(isa::launch_full_merge(L, B, s));
+  }
   return ISA_OK;
 }
 
@@ -111,8 +117,9 @@ extern "C" isa_status isa_run_stage(const isa_desc* desc, int stage, const void*
   isa::Layout L;
   isa_status st = isa::make_layout(desc, &L);
   if (st != ISA_OK) return st;
-  if (stage < ISA_STAGE_POOL || stage > ISA_STAGE_FULL) return ISA_ERR_INVALID_ARGUMENT;
-  const bool writes_o = stage == ISA_STAGE_SHARP_TAYLOR || stage == ISA_STAGE_TAYLOR || stage == ISA_STAGE_FULL;
+  if (stage < ISA_STAGE_POOL || stage > ISA_STAGE_FULL_MERGE) return ISA_ERR_INVALID_ARGUMENT;
+  const bool writes_o = stage == ISA_STAGE_SHARP_TAYLOR || stage == ISA_STAGE_TAYLOR || stage == ISA_STAGE_FULL ||
+                        stage == ISA_STAGE_FULL_MERGE;
   if ((st = check_io(Q, K, V, O, writes_o)) != ISA_OK) return st;
   if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
   const isa::Bufs B{Q, K, V, O, (char*)workspace};
@@ -128,6 +135,7 @@ extern "C" isa_status isa_run_stage(const isa_desc* desc, int stage, const void*
     case ISA_STAGE_SELECT_Q: ISA_RUN(isa::launch_select_q(L, B, s)); break;
     case ISA_STAGE_TAYLOR: if (L.taylor_rows > 0) ISA_RUN(isa::launch_pooled_attention(L, B, 2, s)); break;
     case ISA_STAGE_FULL: if (L.kq > 0) ISA_RUN(isa::launch_full_attention(L, B, false, s)); break;
+    case ISA_STAGE_FULL_MERGE: if (L.kq > 0) ISA_RUN(isa::launch_full_merge(L, B, s)); break;
   }
   return ISA_OK;
 }

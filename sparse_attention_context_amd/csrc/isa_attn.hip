@@ -1,4 +1,5 @@
-// Flash-style attention kernels of ISA on gfx950 MFMA.
+// Flash-style attention kernels of ISA on gfx950 MFMA, fp32-input path (the
+// bf16 path is the pipelined kernel family of isa_flash.hip).
 //
 // Two routes of "Lightning Unified Video Editing via In-Context Sparse
 // Attention" (English abstract) share this kernel:
@@ -419,13 +420,21 @@ static hipError_t full_t(const Layout& L, const Bufs& B, bool dense, hipStream_t
 }
 
 hipError_t launch_pooled_attention(const Layout& L, const Bufs& B, int mode, hipStream_t s) {
-  if (L.es == 2) return L.d == 128 ? pooled_t<bf16_t, 128>(L, B, mode, s) : pooled_t<bf16_t, 64>(L, B, mode, s);
+  if (L.es == 2) {
+    const FlashWhat w = mode == 0 ? FlashWhat::kSharpTaylor : (mode == 1 ? FlashWhat::kSharp : FlashWhat::kTaylor);
+    return launch_flash(L, B, w, s);
+  }
   return L.d == 128 ? pooled_t<float, 128>(L, B, mode, s) : pooled_t<float, 64>(L, B, mode, s);
 }
 
 hipError_t launch_full_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s) {
-  if (L.es == 2) return launch_flash_attention(L, B, dense, s);
+  if (L.es == 2) return launch_flash(L, B, dense ? FlashWhat::kDense : FlashWhat::kFull, s);
   return L.d == 128 ? full_t<float, 128>(L, B, dense, s) : full_t<float, 64>(L, B, dense, s);
+}
+
+hipError_t launch_full_merge(const Layout& L, const Bufs& B, hipStream_t s) {
+  if (L.es == 2) return launch_flash(L, B, FlashWhat::kFullMerge, s);
+  return hipSuccess;
 }
 
 }  // namespace isa

@@ -1,50 +1,68 @@
-// Exact (full-route and dense) flash attention on gfx950 bf16 MFMA.
+// Flash-style attention of ISA on gfx950 bf16 MFMA: full route, dense
+// baseline and the pooled (sharpness + 0-th order Taylor) pass.
 //
-// The full route of "Lightning Unified Video Editing via In-Context Sparse
-// Attention" (English abstract) sends the high-error query blocks to exact
-// softmax attention; here over every source token plus every token of the
-// kept context blocks, the K/V rows gathered through the kept-context row
-// table.  The dense mode (every source query over every key row) is the
-// global self-attention softmax(q k^T / sqrt d) v of the intelliparadigm.com
-// page (section 1) and is the library's own dense baseline.
+// "Lightning Unified Video Editing via In-Context Sparse Attention" (English
+// abstract) sends high-error query blocks to full attention and the rest to a
+// 0-th order Taylor sparse attention, after grouping queries by sharpness.
+//  * full route (FK_GATHER): exact softmax attention over every source token
+//    plus every token of the kept context blocks, K/V rows gathered through
+//    the kept-context row table;
+//  * dense (FK_DENSE): every source query over every key row, the global
+//    self-attention softmax(q k^T / sqrt d) v of the intelliparadigm.com page,
+//    section 1 -- the library's own dense baseline;
+//  * pooled (FK_POOLED): the same online softmax over the kept pooled blocks,
+//    each weighted by its count n_j (an additive log2 n_j in the exp2
+//    domain).  Its output is the Taylor route; the peak probability of that
+//    softmax, exp2(max - ref) / l, is the query sharpness.  Pooled keys come
+//    as bf16 hi + lo parts (two MFMAs) so the logits carry ~2^-17.
 //
-// Workgroup: 4 waves, 128 query rows (32 per wave), key tiles of 64.
-// Each wave computes S^T = K Q^T with 32x32x16 MFMAs (lane = one query,
-// 32 keys in registers), the online softmax in fp32 on exp2, and
-// O^T += V^T P^T (P^T is already the B-operand layout; V is transposed into
-// LDS with the keys of each 16-key group permuted to match).  LDS rows are
-// padded by 16 bytes, which spreads 16 consecutive rows over all banks.
+// Workgroup: NW waves, 32 query rows each; key tiles of 64.  Each wave
+// computes S^T = K Q^T with 32x32x16 MFMAs (lane = one query, 32 keys), the
+// online softmax in fp32 on exp2, and O^T += V^T P^T: P^T is already the
+// B-operand layout, and V is transposed into LDS with the keys of each
+// 16-key group permuted to match.  LDS rows are padded by 16 bytes, which
+// spreads 16 consecutive rows over all banks and makes every operand address
+// a per-lane base plus an immediate.
 //
-// Pipeline per tile j (one barrier per tile, 3-stage LDS ring):
-//   global loads of tile j+2 (row table looked up one tile earlier, so the
-//   loads never wait on the lookup) | lookup of tile j+3's rows |
-//   S(j+1) = K(j+1) Q^T on the MFMA pipe while the VALU does the softmax of
-//   S(j) | O += V(j)^T P(j)^T | tile j+2 regs -> LDS.
-// The running max only moves when a tile raises it by more than 2^8 in the
-// exp2 domain (the accumulator is then rescaled); otherwise exp2 arguments
-// stay <= 8, which fp32 sums and bf16 probabilities carry exactly as well.
+// Pipeline per tile j (one barrier per tile, 3-stage LDS ring): global loads
+// of tile j+2 (row table looked up one tile earlier, so no load waits on a
+// lookup) | lookup of tile j+3's rows | S = K(j) Q^T | softmax | O += V(j)^T
+// P^T | tile j+2 registers -> LDS.  A row's reference maximum only moves when
+// a tile raises that row's max by more than 2^8 in the exp2 domain (then its
+// accumulator is rescaled); exp2 arguments stay <= 8, exact in fp32 sums and
+// bf16 probabilities.  The true running max is tracked separately for the
+// peak probability.
 //
-// Long key ranges over few row tiles are split across workgroups (split-K);
-// each writes unnormalised fp32 partials (acc, max, sum) and a combine kernel
-// merges them in split order (deterministic).
+// Full-route key ranges over few row tiles are split across workgroups
+// (split-K); each split writes unnormalised fp32 partials (acc, ref max, sum)
+// and the merge kernel combines them in split order (deterministic).
 #include "isa_device.h"
 #include "isa_kernels.h"
 
 namespace isa {
 
+enum { FK_DENSE = 0, FK_GATHER = 1, FK_POOLED = 2 };
+enum { FR_IDENTITY = 0, FR_TABLE = 1 };
+
 struct FlashArgs {
   const void* Q;
   void* O;
-  const void* K;
+  const void* K;        // token modes: [BH][Nk][D]
   const void* V;
   const int* ctx_rows;  // gather: [BH][ctx_tok] absolute rows, -1 past a short last block
   const int* kept;      // gather: [BH][kc]
   long long ctx_tok;
   int kc, nb_c, b, tail_c;
-  const int* q_rows;    // gather: [BH][n_rows]
+  const void* pkhi;     // pooled: [BH][mk_pad][D]
+  const void* pklo;
+  const void* pv;
+  const float* pbias;   // pooled: [BH][mk_pad] log2 n_j, -inf for padding
+  int mk_pad;
+  const int* q_rows;    // row table: [BH][n_rows]
   long long n_rows;     // virtual query rows per head
-  float* part_acc;      // split-K: [BH][row_tiles*128][nsplit][D]
-  float* part_ml;       // split-K: [BH][row_tiles*128][nsplit][2]
+  float* peak;          // pooled: [BH][Ns]
+  float* part_acc;      // split-K: [BH][row_tiles*BM][nsplit][D]
+  float* part_ml;       // split-K: [BH][row_tiles*BM][nsplit][2]
   int nsplit, tiles_per_split;
   int Ns, Nk;
   int row_tiles;
@@ -52,24 +70,28 @@ struct FlashArgs {
   float scale_log2;     // log2(e)/sqrt(d)
 };
 
-template <int D, bool GATHER, int NW, bool PIPE>
+template <int D, int KM, int RM, int NW, bool WO, bool WP>
 __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   typedef bf16x8 Op;
+  constexpr bool GATHER = KM == FK_GATHER, POOLED = KM == FK_POOLED;
   constexpr int NTHR = NW * 64;
   constexpr int ES = 2, BN = 64, BM = 32 * NW, NSTAGE = 3;
   constexpr int KRB = D * ES, KCPR = KRB / 16;   // global K/V row: bytes, 16-byte chunks
   constexpr int KRS = KRB + 16;                  // LDS K row stride (one chunk of padding)
   constexpr int VRS = BN * ES + 16;              // LDS V^T row stride
-  constexpr int KT = BN * KRS, VT = D * VRS, STAGE = KT + VT;
-  constexpr int NKC = BN * KCPR / NTHR;     // K chunks per thread
-  constexpr int VDG = NTHR / 16;            // threads sharing 4 keys (one d-group each)
-  constexpr int DPT = D / VDG;              // V elements per key per thread
-  constexpr int VW = DPT * ES / 4;          // 32-bit words per key per thread
+  constexpr int KT = BN * KRS, VT = WO ? D * VRS : 0;
+  constexpr int NKT = POOLED ? 2 : 1;            // K tiles per stage (hi, lo)
+  constexpr int STAGE = NKT * KT + VT;
+  constexpr int NKC = BN * KCPR / NTHR;          // K chunks per thread per K tile
+  constexpr int VDG = NTHR / 16;                 // threads sharing 4 keys (one d-group each)
+  constexpr int DPT = D / VDG;                   // V elements per key per thread
+  constexpr int VW = DPT * ES / 4;               // 32-bit words per key per thread
   constexpr int NT = D / 32;
-  constexpr int NR = NKC + 4;               // key rows a thread loads per tile
+  constexpr int NR = NKC + 4;                    // key rows a thread loads per tile
   static_assert(NKC >= 1 && DPT >= 2 && (DPT & 1) == 0, "tile mapping");
 
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(16))) float sbias[POOLED ? NSTAGE : 1][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -82,7 +104,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   // ---- query row of this lane (invalid rows read row 0 and store nothing)
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   int qrow;
-  if constexpr (GATHER) qrow = vrow < a.n_rows ? a.q_rows[(long long)bh * a.n_rows + vrow] : -1;
+  if constexpr (RM == FR_TABLE) qrow = vrow < a.n_rows ? a.q_rows[(long long)bh * a.n_rows + vrow] : -1;
   else qrow = vrow < a.Ns ? (int)vrow : -1;
   Op qB[D / 16];
   {
@@ -97,6 +119,8 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
     n_keys = a.Ns + (int)a.ctx_tok;
     const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
     n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
+  } else if constexpr (POOLED) {
+    n_keys = n_valid = a.mk_pad;  // padding rows carry bias -inf
   } else {
     n_keys = n_valid = a.Nk;
   }
@@ -105,13 +129,22 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
   const int t_last = t_begin + nt - 1;
 
-  const char* Kg = (const char*)a.K + (long long)bh * a.Nk * KRB;
-  const char* Vg = (const char*)a.V + (long long)bh * a.Nk * KRB;
+  const char* Kg;
+  const char* Kg_lo = nullptr;
+  const char* Vg;
+  if constexpr (POOLED) {
+    Kg = (const char*)a.pkhi + (long long)bh * a.mk_pad * KRB;
+    Kg_lo = (const char*)a.pklo + (long long)bh * a.mk_pad * KRB;
+    Vg = (const char*)a.pv + (long long)bh * a.mk_pad * KRB;
+  } else {
+    Kg = (const char*)a.K + (long long)bh * a.Nk * KRB;
+    Vg = (const char*)a.V + (long long)bh * a.Nk * KRB;
+  }
   const int* crow = GATHER ? a.ctx_rows + (long long)bh * a.ctx_tok : nullptr;
   const int ctx_last = (int)a.ctx_tok - 1;
 
   struct Rows { int r[NR]; };
-  struct Staged { u32x4 k[NKC]; uint32_t v[4][VW]; };
+  struct Staged { u32x4 k[NKT][NKC]; uint32_t v[WO ? 4 : 1][VW]; float bias; };
   struct STile { f32x16 t[2]; };
 
   const int vdc = tid % VDG, vkg = tid / VDG;   // V: d-group, 4-key group (0..15)
@@ -128,62 +161,77 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
         int c = 0;
         if (ctx_last >= 0) c = crow[min(max(t - a.Ns, 0), ctx_last)];
         rows.r[r] = t < a.Ns ? t : (t < n_valid && c >= 0 ? c : 0);
+      } else if constexpr (POOLED) {
+        rows.r[r] = t;
       } else {
         rows.r[r] = t < n_valid ? t : 0;
       }
     }
     return rows;
   };
-  auto load = [&](Rows rows) -> Staged {
+  auto load = [&](Rows rows, int tile) -> Staged {
     Staged g;
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
       const int c = (tid + NTHR * i) % KCPR;
-      g.k[i] = *(const u32x4*)(Kg + (long long)rows.r[i] * KRB + c * 16);
+      g.k[0][i] = *(const u32x4*)(Kg + (long long)rows.r[i] * KRB + c * 16);
+      if constexpr (POOLED) g.k[NKT - 1][i] = *(const u32x4*)(Kg_lo + (long long)rows.r[i] * KRB + c * 16);
     }
+    if constexpr (WO) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* src = Vg + (long long)rows.r[NKC + i] * KRB + vdc * DPT * ES;
-      if constexpr (VW == 1) {
-        g.v[i][0] = *(const uint32_t*)src;
-      } else if constexpr (VW == 2) {
-        const u32x2 v = *(const u32x2*)src;
-        g.v[i][0] = v.x; g.v[i][1] = v.y;
-      } else {
-        const u32x4 v = *(const u32x4*)src;
-        g.v[i][0] = v.x; g.v[i][1] = v.y; g.v[i][2] = v.z; g.v[i][3] = v.w;
+      for (int i = 0; i < 4; ++i) {
+        const char* src = Vg + (long long)rows.r[NKC + i] * KRB + vdc * DPT * ES;
+        if constexpr (VW == 1) {
+          g.v[i][0] = *(const uint32_t*)src;
+        } else if constexpr (VW == 2) {
+          const u32x2 v = *(const u32x2*)src;
+          g.v[i][0] = v.x; g.v[i][1] = v.y;
+        } else {
+          const u32x4 v = *(const u32x4*)src;
+          g.v[i][0] = v.x; g.v[i][1] = v.y; g.v[i][2] = v.z; g.v[i][3] = v.w;
+        }
       }
+    }
+    g.bias = 0.f;
+    if constexpr (POOLED) {
+      if (tid < BN) g.bias = a.pbias[(long long)bh * a.mk_pad + tile * BN + tid];
     }
     return g;
   };
   auto store = [&](int stage, Staged g) {
     char* Ks = smem + stage * STAGE;
-    char* Vs = Ks + KT;
 #pragma unroll
-    for (int i = 0; i < NKC; ++i) {
-      const int q = tid + NTHR * i;
-      const int kr = q / KCPR, c = q % KCPR;
-      *(u32x4*)(Ks + kr * KRS + c * 16) = g.k[i];
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < NKC; ++i) {
+        const int q = tid + NTHR * i;
+        const int kr = q / KCPR, c = q % KCPR;
+        *(u32x4*)(Ks + kt * KT + kr * KRS + c * 16) = g.k[kt][i];
+      }
+    if constexpr (WO) {
+      // V^T: row d, 64 keys; key group g4 of each 16-key group sits at
+      // position group {0,2,1,3}[g4] (the order of the P^T operand)
+      char* Vs = Ks + NKT * KT;
+      const int g4 = vkg & 3;
+      const int pos = 16 * (vkg >> 2) + 4 * (g4 == 1 ? 2 : (g4 == 2 ? 1 : g4));
+      const int byte = pos * ES;
+#pragma unroll
+      for (int j = 0; j < DPT; ++j) {
+        const int d = vdc * DPT + j;
+        const int wd = j >> 1, sh = (j & 1) * 16;
+        const uint32_t e0 = (g.v[0][wd] >> sh) & 0xffffu, e1 = (g.v[1][wd] >> sh) & 0xffffu;
+        const uint32_t e2 = (g.v[2][wd] >> sh) & 0xffffu, e3 = (g.v[3][wd] >> sh) & 0xffffu;
+        *(u32x2*)(Vs + d * VRS + byte) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+      }
     }
-    // V^T: row d, 64 keys; key group g4 of each 16-key group sits at
-    // position group {0,2,1,3}[g4] (the order of the P^T operand)
-    const int g4 = vkg & 3;
-    const int pos = 16 * (vkg >> 2) + 4 * (g4 == 1 ? 2 : (g4 == 2 ? 1 : g4));
-    const int byte = pos * ES;
-#pragma unroll
-    for (int j = 0; j < DPT; ++j) {
-      const int d = vdc * DPT + j;
-      const int wd = j >> 1, sh = (j & 1) * 16;
-      const uint32_t e0 = (g.v[0][wd] >> sh) & 0xffffu, e1 = (g.v[1][wd] >> sh) & 0xffffu;
-      const uint32_t e2 = (g.v[2][wd] >> sh) & 0xffffu, e3 = (g.v[3][wd] >> sh) & 0xffffu;
-      *(u32x2*)(Vs + d * VRS + byte) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+    if constexpr (POOLED) {
+      if (tid < BN) sbias[stage][tid] = g.bias;
     }
   };
   // Operands: lane (l32, h) reads row 32*i + l32, elements 16*s + 8*h .. +7
   // of a padded tile: one per-lane base, the rest are immediate offsets.
-  // Sixteen consecutive padded rows start in sixteen distinct bank groups.
   const int kbase = l32 * KRS + 16 * h;
-  const int vbase = KT + l32 * VRS + 16 * h;
+  const int vbase = NKT * KT + l32 * VRS + 16 * h;
   auto qk = [&](int stage) -> STile {
     const char* Ks = smem + stage * STAGE + kbase;
     STile S;
@@ -191,22 +239,37 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
     for (int ti = 0; ti < 2; ++ti) {
       S.t[ti] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) S.t[ti] = mma32(*(const Op*)(Ks + 32 * ti * KRS + 32 * s), qB[s], S.t[ti]);
+      for (int s = 0; s < D / 16; ++s) {
+        S.t[ti] = mma32(*(const Op*)(Ks + 32 * ti * KRS + 32 * s), qB[s], S.t[ti]);
+        if constexpr (POOLED) S.t[ti] = mma32(*(const Op*)(Ks + KT + 32 * ti * KRS + 32 * s), qB[s], S.t[ti]);
+      }
     }
     return S;
   };
 
-  f32x16 acc[NT];
+  f32x16 acc[WO ? NT : 1];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.f;
+  for (int t = 0; t < (WO ? NT : 1); ++t) acc[t] = f32x16{};
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
-  const float thresh = 8.0f / sc;  // raw-logit headroom before a rescale
+  // exp2-domain headroom before the reference max moves; token modes keep
+  // logits raw (x = S), pooled mode works on x = S*sc + log2 n_j directly
+  const float thresh = POOLED ? 8.0f : 8.0f / sc;
 
   auto softmax_pv = [&](int j, STile St) {
     f32x16* S = St.t;
     const int t0 = (t_begin + j) * BN;
-    if (t0 + BN > n_valid) {
+    if constexpr (POOLED) {
+      const float* bs = sbias[j % NSTAGE];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 bb = *(const f32x4*)(bs + 32 * ti + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[ti][4 * g + e] = fmaf(S[ti][4 * g + e], sc, bb[e]);
+        }
+    } else if (t0 + BN > n_valid) {
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -219,71 +282,71 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if (__ballot(mx > m_ref + thresh)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sc);
+    if constexpr (WP) m_true = fmaxf(m_true, mx);
+    // each row moves its own reference (rows of a wave never influence one
+    // another, so a row's result does not depend on how rows are grouped);
+    // the branch is taken when any row of the wave needs it
+    const bool move = mx > m_ref + thresh;
+    if (__ballot(move)) {
+      const float m_new = move ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(POOLED ? (m_ref - m_new) : (m_ref - m_new) * sc);
       l_run *= alpha;
+      if constexpr (WO) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+      }
       m_ref = m_new;
     }
-    const float msc = m_ref * sc;
+    const float msub = POOLED ? m_ref : m_ref * sc;
     Op pB[4];
+    float psum = 0.f;  // tile-local sum first: fewer roundings at the running sum's scale
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, -msc));
-        l_run += p;
+        const float x = S[s >> 1][8 * (s & 1) + jj];
+        const float p = __builtin_amdgcn_exp2f(POOLED ? x - msub : fmaf(x, sc, -msub));
+        psum += p;
         pB[s][jj] = (__bf16)p;
       }
     }
-    const char* Vs = smem + (j % NSTAGE) * STAGE + vbase;
+    l_run += psum;
+    if constexpr (WO) {
+      const char* Vs = smem + (j % NSTAGE) * STAGE + vbase;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[t] = mma32(*(const Op*)(Vs + 32 * t * VRS + 32 * s), pB[s], acc[t]);
+        for (int s = 0; s < 4; ++s) acc[t] = mma32(*(const Op*)(Vs + 32 * t * VRS + 32 * s), pB[s], acc[t]);
+    }
   };
 
   // ---- prologue: tiles 0 and 1 in LDS, tile 2's rows looked up
   Rows ra = {}, rb = {};
   Staged gs = {};
-  STile Sa = {}, Sb = {};
   if (nt > 0) {
     ra = lookup(t_begin);
-    store(0, load(ra));
+    store(0, load(ra, t_begin));
     rb = lookup(min(t_begin + 1, t_last));
-    gs = load(rb);
+    gs = load(rb, min(t_begin + 1, t_last));
     ra = lookup(min(t_begin + 2, t_last));
     __syncthreads();
-    if constexpr (PIPE) Sa = qk(0);
     if (nt > 1) store(1, gs);
     __syncthreads();
   }
 
   // Tile j: the rows of tile j+2 were looked up one tile earlier, those of
   // tile j+3 are fetched now; loads past the last tile re-read it and are
-  // never stored.  PIPE issues S(j+1) before the softmax of S(j).
+  // never stored.
   for (int j = 0; j < nt; j += 2) {
-    gs = load(ra);
+    gs = load(ra, min(t_begin + j + 2, t_last));
     rb = lookup(min(t_begin + j + 3, t_last));
-    if constexpr (PIPE) {
-      if (j + 1 < nt) Sb = qk((j + 1) % NSTAGE);
-      softmax_pv(j, Sa);
-    } else {
-      softmax_pv(j, qk(j % NSTAGE));
-    }
+    softmax_pv(j, qk(j % NSTAGE));
     if (j + 2 < nt) store((j + 2) % NSTAGE, gs);
     __syncthreads();
     if (j + 1 < nt) {
-      gs = load(rb);
+      gs = load(rb, min(t_begin + j + 3, t_last));
       ra = lookup(min(t_begin + j + 4, t_last));
-      if constexpr (PIPE) {
-        if (j + 2 < nt) Sa = qk((j + 2) % NSTAGE);
-        softmax_pv(j + 1, Sb);
-      } else {
-        softmax_pv(j + 1, qk((j + 1) % NSTAGE));
-      }
+      softmax_pv(j + 1, qk((j + 1) % NSTAGE));
       if (j + 3 < nt) store((j + 3) % NSTAGE, gs);
       __syncthreads();
     }
@@ -294,17 +357,22 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   if (a.nsplit == 1) {
     if (qrow >= 0) {
       const float inv = 1.0f / l_tot;
-      bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
+      if constexpr (WO) {
+        bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * t + 8 * g + 4 * h;
-          *(u32x2*)(op + d0) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
-                                     pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
-        }
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * t + 8 * g + 4 * h;
+            *(u32x2*)(op + d0) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                                       pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+          }
+      }
+      if constexpr (WP) {
+        if (h == 0) a.peak[(long long)bh * a.Ns + qrow] = __builtin_amdgcn_exp2f(m_true - m_ref) * inv;
+      }
     }
-  } else {
+  } else if constexpr (WO) {
     const long long prow = ((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split;
     float* pa = a.part_acc + prow * D;
 #pragma unroll
@@ -316,9 +384,9 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   }
 }
 
-// Merges the split-K partials of each query row, in split order.
-template <int D, bool GATHER>
-__global__ __launch_bounds__(256) void isa_flash_combine_kernel(FlashArgs a) {
+// Merges the split-K partials of each full-route query row, in split order.
+template <int D>
+__global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   constexpr int TPR = D / 4;           // threads per row, 4 elements each
   constexpr int RPB = 256 / TPR;       // rows per workgroup
   const long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -327,9 +395,7 @@ __global__ __launch_bounds__(256) void isa_flash_combine_kernel(FlashArgs a) {
   const long long bh = gid / rows_head;
   const long long vrow = gid - bh * rows_head;
   if (bh >= a.n_wg) return;  // n_wg carries BH here
-  int qrow;
-  if constexpr (GATHER) qrow = vrow < a.n_rows ? a.q_rows[bh * a.n_rows + vrow] : -1;
-  else qrow = vrow < a.Ns ? (int)vrow : -1;
+  const int qrow = vrow < a.n_rows ? a.q_rows[bh * a.n_rows + vrow] : -1;
   if (qrow < 0) return;
   const long long prow = gid * a.nsplit;
   float mstar = -INFINITY;
@@ -340,57 +406,89 @@ __global__ __launch_bounds__(256) void isa_flash_combine_kernel(FlashArgs a) {
     if (m == -INFINITY) continue;
     const float wgt = __builtin_amdgcn_exp2f((m - mstar) * a.scale_log2);
     l += wgt * a.part_ml[(prow + s) * 2 + 1];
-    const float4 v = *(const float4*)(a.part_acc + (prow + s) * D + e);
+    const f32x4 v = *(const f32x4*)(a.part_acc + (prow + s) * D + e);
     o0 += wgt * v.x; o1 += wgt * v.y; o2 += wgt * v.z; o3 += wgt * v.w;
   }
   const float inv = 1.0f / l;
   bf16_t* op = (bf16_t*)a.O + (bh * a.Ns + qrow) * D + e;
-  *(uint2*)op = uint2{pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv)};
+  *(u32x2*)op = u32x2{pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv)};
 }
 
-template <int D, bool GATHER>
-static hipError_t flash_t(const Layout& L, const Bufs& B, hipStream_t s) {
+// ---------------------------------------------------------------------------
+
+static FlashArgs flash_args(const Layout& L, const Bufs& B) {
   FlashArgs a = {};
   a.Q = B.Q; a.O = B.O; a.K = B.K; a.V = B.V;
   a.Ns = L.Ns; a.Nk = L.Nk;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)L.d));
-  long long keys;
-  if (GATHER) {
+  a.nsplit = 1;
+  if (B.ws) {
     a.ctx_rows = (const int*)(B.ws + L.off_ctxrows);
     a.kept = (const int*)(B.ws + L.off_kept);
-    a.q_rows = (const int*)(B.ws + L.off_qrows_full);
+    a.pkhi = B.ws + L.off_pkhi;
+    a.pklo = B.ws + L.off_pklo;
+    a.pv = B.ws + L.off_pv;
+    a.pbias = (const float*)(B.ws + L.off_pbias);
+    a.peak = (float*)(B.ws + L.off_peak);
     a.part_acc = (float*)(B.ws + L.off_part_acc);
     a.part_ml = (float*)(B.ws + L.off_part_ml);
-    a.ctx_tok = L.ctx_tok;
-    a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;
-    a.n_rows = L.full_rows;
-    a.nsplit = L.full_splits;
-    keys = (long long)L.Ns + L.ctx_tok;
-  } else {
-    a.n_rows = L.Ns;
-    a.nsplit = 1;
-    keys = L.Nk;
   }
-  a.row_tiles = (int)((a.n_rows + kFlashRows - 1) / kFlashRows);
+  a.ctx_tok = L.ctx_tok;
+  a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;
+  a.mk_pad = L.mk_pad;
+  return a;
+}
+
+template <int D, int KM, int RM, bool WO, bool WP>
+static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, long long BH, hipStream_t s) {
+  a.n_rows = n_rows;
+  a.row_tiles = (int)((n_rows + kFlashRows - 1) / kFlashRows);
   const int ntiles = (int)((keys + 63) / 64);
   a.tiles_per_split = (ntiles + a.nsplit - 1) / a.nsplit;
-  const long long nwg = (long long)a.row_tiles * L.BH * a.nsplit;
+  const long long nwg = (long long)a.row_tiles * BH * a.nsplit;
   if (nwg == 0) return hipSuccess;
   a.n_wg = (int)nwg;
-  hipLaunchKernelGGL((isa_flash_kernel<D, GATHER, kFlashWaves, kFlashPipe != 0>), dim3((unsigned)nwg),
+  hipLaunchKernelGGL((isa_flash_kernel<D, KM, RM, kFlashWaves, WO, WP>), dim3((unsigned)nwg),
                      dim3(kFlashWaves * 64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  constexpr int RPB = 256 / (D / 4);
-  const long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
-  a.n_wg = (int)L.BH;
-  hipLaunchKernelGGL((isa_flash_combine_kernel<D, GATHER>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_flash_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s) {
-  if (L.d == 128) return dense ? flash_t<128, false>(L, B, s) : flash_t<128, true>(L, B, s);
-  return dense ? flash_t<64, false>(L, B, s) : flash_t<64, true>(L, B, s);
+template <int D>
+static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStream_t s) {
+  FlashArgs a = flash_args(L, B);
+  switch (what) {
+    case FlashWhat::kDense:
+      return flash_launch<D, FK_DENSE, FR_IDENTITY, true, false>(a, L.Ns, L.Nk, L.BH, s);
+    case FlashWhat::kFull:
+      a.q_rows = (const int*)(B.ws + L.off_qrows_full);
+      a.nsplit = L.full_splits;
+      return flash_launch<D, FK_GATHER, FR_TABLE, true, false>(a, L.full_rows, (long long)L.Ns + L.ctx_tok,
+                                                                L.BH, s);
+    case FlashWhat::kFullMerge: {
+      if (L.full_splits <= 1 || L.full_rows == 0) return hipSuccess;
+      a.q_rows = (const int*)(B.ws + L.off_qrows_full);
+      a.nsplit = L.full_splits;
+      a.n_rows = L.full_rows;
+      a.row_tiles = (int)((L.full_rows + kFlashRows - 1) / kFlashRows);
+      a.n_wg = (int)L.BH;
+      constexpr int RPB = 256 / (D / 4);
+      const long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
+      hipLaunchKernelGGL((isa_flash_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+    case FlashWhat::kSharpTaylor:
+      return flash_launch<D, FK_POOLED, FR_IDENTITY, true, true>(a, L.Ns, L.mk_pad, L.BH, s);
+    case FlashWhat::kSharp:
+      return flash_launch<D, FK_POOLED, FR_IDENTITY, false, true>(a, L.Ns, L.mk_pad, L.BH, s);
+    case FlashWhat::kTaylor:
+      a.q_rows = (const int*)(B.ws + L.off_qrows_taylor);
+      return flash_launch<D, FK_POOLED, FR_TABLE, true, false>(a, L.taylor_rows, L.mk_pad, L.BH, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_flash(const Layout& L, const Bufs& B, FlashWhat what, hipStream_t s) {
+  return L.d == 128 ? flash_t<128>(L, B, what, s) : flash_t<64>(L, B, what, s);
 }
 
 }  // namespace isa

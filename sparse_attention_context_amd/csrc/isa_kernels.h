@@ -41,12 +41,17 @@ hipError_t launch_select_q(const Layout& L, const Bufs& B, hipStream_t s);
 // row, peak only; mode 2: Taylor-route rows only, writes O.
 hipError_t launch_pooled_attention(const Layout& L, const Bufs& B, int mode, hipStream_t s);
 
-// Exact attention.  dense=false: full-route rows over the kept key tokens;
-// dense=true: every source row over every key row (no workspace needed).
+// Exact attention.  dense=false: full-route rows over the kept key tokens
+// (bf16: the flash kernel, writing split partials when split; the merge is
+// launch_full_merge); dense=true: every source row over every key row (no
+// workspace needed).
 hipError_t launch_full_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s);
 
-// bf16 pipelined flash attention (full route with split-K, or dense); used
-// by launch_full_attention for bf16 inputs.
-hipError_t launch_flash_attention(const Layout& L, const Bufs& B, bool dense, hipStream_t s);
+// Merges the full route's split-K partials into O (nothing when unsplit or f32).
+hipError_t launch_full_merge(const Layout& L, const Bufs& B, hipStream_t s);
+
+// The bf16 flash kernel family (isa_flash.hip).
+enum class FlashWhat { kDense, kFull, kFullMerge, kSharpTaylor, kSharp, kTaylor };
+hipError_t launch_flash(const Layout& L, const Bufs& B, FlashWhat what, hipStream_t s);
 
 }  // namespace isa

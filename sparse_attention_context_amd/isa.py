@@ -25,10 +25,11 @@ EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "i
 
 # isa_stage values (include/isa.h)
 STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
-          "taylor", "full"]
+          "taylor", "full", "full_merge"]
 STAGE = {name: i for i, name in enumerate(STAGES)}
 # the stage sequence of isa_attention when some query blocks stay on the Taylor route
-ATTENTION_STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "select_q", "full"]
+ATTENTION_STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "select_q", "full",
+                    "full_merge"]
 
 
 class Desc(ctypes.Structure):
