@@ -11,7 +11,7 @@
 namespace isa {
 
 constexpr int kTileKeys = 64;      // keys per attention tile
-constexpr int kSalRows = 16;       // pooled queries per saliency workgroup
+constexpr int kSalRows = 32;       // pooled queries per saliency workgroup
 #ifndef ISA_FLASH_WAVES
 #define ISA_FLASH_WAVES 8
 #endif

@@ -9,7 +9,8 @@
 //
 // One workgroup (4 waves) per (batch, head).  Scores are fp64 mapped to
 // order-preserving 64-bit keys, so the selection itself is integer work:
-//   n <= kRankMax: every element counts the elements that beat it (LDS);
+//   n <= kSortMax: bitonic sort of (key, index) pairs in LDS under the total
+//                  order above; the first k sorted positions are selected;
 //   larger n:      MSB-first radix select, 8 passes of 8 bits with an LDS
 //                  histogram, finds the k-th key T and how many keys equal
 //                  to T are still needed.
@@ -20,7 +21,7 @@
 
 namespace isa {
 
-constexpr int kRankMax = 1024;
+constexpr int kSortMax = 2048;
 
 __device__ __forceinline__ uint64_t order_key(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
@@ -28,7 +29,9 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 }
 
 struct SelectSmem {
-  uint64_t keys[kRankMax];
+  uint64_t keys[kSortMax];
+  int idx[kSortMax];
+  unsigned char chosen[kSortMax];
   int hist[256];
   int wtot[4];
   int wtot2[4];
@@ -76,16 +79,43 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* wtot) {
 // when rest is non-null the others go ascending to rest[0..n-k).
 __device__ void select_topk(const double* sc, int n, int k, int* sel, int* rest, SelectSmem& sm) {
   const int tid = threadIdx.x;
-  int mode;  // 0: none, 1: all, 2: rank, 3: radix
+  int mode;  // 0: none, 1: all, 2: sort, 3: radix
   if (k <= 0) mode = 0;
   else if (k >= n) mode = 1;
-  else if (n <= kRankMax) mode = 2;
+  else if (n <= kSortMax) mode = 2;
   else mode = 3;
 
   uint64_t T = 0;
   int need = 0;
   if (mode == 2) {
-    for (int i = tid; i < n; i += 256) sm.keys[i] = order_key(sc[i]);
+    // bitonic sort, descending by (key, then lower index first), padded to a
+    // power of two with entries that sort last
+    int np = 1;
+    while (np < n) np <<= 1;
+    for (int i = tid; i < np; i += 256) {
+      sm.keys[i] = i < n ? order_key(sc[i]) : 0ull;
+      sm.idx[i] = i < n ? i : 0x7fffffff;
+      sm.chosen[i] = 0;
+    }
+    __syncthreads();
+    for (int size = 2; size <= np; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < (np >> 1); t += 256) {
+          const int lo = 2 * t - (t & (stride - 1));
+          const int hi = lo + stride;
+          const bool desc = (lo & size) == 0;  // this run sorts descending
+          const uint64_t ka = sm.keys[lo], kb = sm.keys[hi];
+          const int ia = sm.idx[lo], ib = sm.idx[hi];
+          const bool b_first = kb > ka || (kb == ka && ib < ia);
+          if (b_first == desc) {
+            sm.keys[lo] = kb; sm.keys[hi] = ka;
+            sm.idx[lo] = ib; sm.idx[hi] = ia;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < k; i += 256) sm.chosen[sm.idx[i]] = 1;
     __syncthreads();
   } else if (mode == 3) {
     uint64_t prefix = 0, mask = 0;
@@ -123,15 +153,7 @@ __device__ void select_topk(const double* sc, int n, int k, int* sel, int* rest,
     if (mode == 1) {
       f = valid;
     } else if (mode == 2) {
-      if (valid) {
-        const uint64_t ki = sm.keys[i];
-        int rank = 0;
-        for (int j = 0; j < n; ++j) {
-          const uint64_t kj = sm.keys[j];
-          rank += (kj > ki) || (kj == ki && j < i);
-        }
-        f = rank < k;
-      }
+      f = valid && sm.chosen[i];
     } else if (mode == 3) {
       const uint64_t key = valid ? order_key(sc[i]) : 0;
       const bool eq = valid && key == T;
@@ -200,11 +222,21 @@ __global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
   const int tid = threadIdx.x;
   double* sh = a.sh + bh * a.nb_s;
   const float* pk = a.peak + bh * a.Ns;
+  // block means of the per-row peaks, rows added in order; the rows of a
+  // block are fetched 8 at a time with independent loads
   for (int i = tid; i < a.nb_s; i += 256) {
     const int r0 = i * a.b;
     const int n = min(a.b, a.Ns - r0);
     double s = 0.0;
-    for (int r = 0; r < n; ++r) s += (double)pk[r0 + r];
+    int r = 0;
+    for (; r + 8 <= n; r += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pk[r0 + r + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += (double)v[u];
+    }
+    for (; r < n; ++r) s += (double)pk[r0 + r];
     sh[i] = s / n;
   }
   __syncthreads();

@@ -72,7 +72,7 @@ SMALL = [
     (2, 3, 128, 1000, 700, 64, 0.25, 0.2, "bf16"),
     (1, 2, 128, 777, 333, 128, 0.3, 0.5, "bf16"),
     (1, 2, 64, 150, 100, 1, 0.4, 0.3, "bf16"),
-    (1, 1, 64, 3000, 2500, 2, 0.3, 0.2, "bf16"),      # > 1024 blocks: radix select
+    (1, 1, 64, 5000, 4200, 2, 0.3, 0.2, "bf16"),      # > 2048 blocks: radix select
     (1, 2, 64, 500, 0, 32, 0.5, 0.3, "bf16"),         # no context
     (1, 2, 64, 100, 300, 256, 0.5, 0.5, "bf16"),      # one query block
     (1, 2, 128, 1000, 900, 200, 0.5, 0.5, "bf16"),    # b above the key tile
@@ -105,6 +105,30 @@ def test_small_shapes_elementwise(case):
     for key in ("sal", "kept_ctx", "sh", "full_q", "taylor_q"):
         assert torch.equal(views[key], v2[key]), key
     assert torch.equal(O, O2)
+
+
+def test_exact_ties_go_to_the_lower_index():
+    """Exact ties in both scores: zero context keys make every full-size
+    context block equally salient; zero queries make every query block
+    equally sharp.  The kept and full-route lists must be the lowest indices."""
+    B, H, d, Ns, Nc, b = 1, 2, 64, 640, 600, 32      # context tail of 24 rows
+    Q, K, V = make_inputs(B, H, d, Ns, Nc, seed=3, dtype="bf16")
+    K[:, :, Ns:] = 0.0
+    Q[:] = 0.0
+    Qd, Kd, Vd = (device_tensor(t, "bf16") for t in (Q, K, V))
+    for rho, gamma in ((0.25, 0.25), (0.5, 0.6)):
+        O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
+        torch.cuda.synchronize()
+        v = isa.plan_views(Qd, Kd, ws, b, rho, gamma)
+        kc, kq = v["counts"]["kc"], v["counts"]["kq"]
+        for h in range(H):
+            assert v["kept_ctx"][0, h].tolist() == list(range(kc))
+            assert v["full_q"][0, h].tolist() == list(range(kq))
+            ref = orc.oracle_plan_head(Q[0, h], K[0, h], V[0, h], b, rho, gamma)
+            assert ref["kept_ctx"].tolist() == list(range(kc))
+            assert ref["full_q"].tolist() == list(range(kq))
+            Oref = orc.oracle_forward_head(Q[0, h], K[0, h], V[0, h], b, ref["kept_ctx"], ref["full_q"])
+            assert_output(O[0, h].float().cpu().numpy(), Oref, "bf16")
 
 
 def test_repeat_runs_are_bit_identical():
