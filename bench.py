@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for counter collection: one layer call, one dense call and a 1 GiB elementwise copy "
+                         "(the copy calibrates byte counters), no timing")
     return ap.parse_args()
 
 
@@ -113,6 +116,18 @@ def main():
 
     def step():
         isa.attention(Qd, Kd, Vd, w.b, w.rho, gamma, out=O, workspace=ws)
+
+    if args.profile_pass:
+        step()
+        torch.cuda.synchronize()
+        if w.dtype == "bf16":
+            isa.dense_forward(Qd, Kd, Vd, out=O)
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)                                  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        log("profile pass done (copy probe: 1 GiB read + 1 GiB written by the elementwise mul kernel)")
+        return
 
     for _ in range(args.warmup):
         step()

@@ -14,11 +14,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libisa.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 HIP_SOURCES = ["isa_pool.hip", "isa_score.hip", "isa_select.hip", "isa_attn.hip", "isa_flash.hip", "isa_abi.hip"]
 CXX_SOURCES = ["isa_layout.cpp"]
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE,
     # packed fp32 ops are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -43,7 +44,7 @@ def build(verbose=False, jobs=8):
     objs = []
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

@@ -12,6 +12,10 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;  // LDS operand of ds_read_b64_tr_b16
+typedef __attribute__((address_space(3))) char lds_char;
 typedef uint16_t bf16_t;  // bfloat16 storage in global memory
 
 // ---------------------------------------------------------------------------

@@ -19,15 +19,18 @@
 // Workgroup: NW waves, 32 query rows each; key tiles of 64.  Each wave
 // computes S^T = K Q^T with 32x32x16 MFMAs (lane = one query, 32 keys), the
 // online softmax in fp32 on exp2, and O^T += V^T P^T: P^T is already the
-// B-operand layout, and V is transposed into LDS with the keys of each
-// 16-key group permuted to match.  LDS rows are padded by 16 bytes, which
-// spreads 16 consecutive rows over all banks and makes every operand address
-// a per-lane base plus an immediate.
+// B-operand layout, and the V^T operand is read from a row-major V tile with
+// the LDS transpose read ds_read_b64_tr_b16 (within each 16-lane group, lane
+// i receives element i%4 of the 8 bytes loaded by lane 4j + i/4, j = 0..3;
+// lanes that load 4 consecutive d of key rows K0 + m/4 therefore receive 4
+// keys of one d).  K rows are padded by 16 bytes and V rows by 64, which
+// keeps the operand reads free of bank conflicts and makes every operand
+// address a per-lane base plus an immediate.
 //
-// Pipeline per tile j (one barrier per tile, 3-stage LDS ring): global loads
-// of tile j+2 (row table looked up one tile earlier, so no load waits on a
-// lookup) | lookup of tile j+3's rows | S = K(j) Q^T | softmax | O += V(j)^T
-// P^T | tile j+2 registers -> LDS.  A row's reference maximum only moves when
+// Pipeline per tile j (one barrier per tile, 2-stage LDS ring): global loads
+// of tile j+1 (row table looked up one tile earlier, so no load waits on a
+// lookup) | lookup of tile j+2's rows | S = K(j) Q^T | softmax |
+// O += V(j)^T P^T | tile j+1 registers -> LDS.  A row's reference maximum only moves when
 // a tile raises that row's max by more than 2^8 in the exp2 domain (then its
 // accumulator is rescaled); exp2 arguments stay <= 8, exact in fp32 sums and
 // bf16 probabilities.  The true running max is tracked separately for the
@@ -75,20 +78,21 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   typedef bf16x8 Op;
   constexpr bool GATHER = KM == FK_GATHER, POOLED = KM == FK_POOLED;
   constexpr int NTHR = NW * 64;
-  constexpr int ES = 2, BN = 64, BM = 32 * NW, NSTAGE = 3;
+  constexpr int ES = 2, BN = 64, BM = 32 * NW;
+  // LDS stages of the K/V ring; tile j+PF is loaded while tile j is computed
+  // (two stages measured faster than three: fewer registers for the ring).
+  constexpr int NSTAGE = 2;
+  constexpr int PF = NSTAGE - 1;
   constexpr int KRB = D * ES, KCPR = KRB / 16;   // global K/V row: bytes, 16-byte chunks
   constexpr int KRS = KRB + 16;                  // LDS K row stride (one chunk of padding)
-  constexpr int VRS = BN * ES + 16;              // LDS V^T row stride
-  constexpr int KT = BN * KRS, VT = WO ? D * VRS : 0;
+  constexpr int VRS = KRB + 64;                  // LDS V row stride (4 rows x 64 B on distinct banks)
+  constexpr int KT = BN * KRS, VT = WO ? BN * VRS : 0;
   constexpr int NKT = POOLED ? 2 : 1;            // K tiles per stage (hi, lo)
   constexpr int STAGE = NKT * KT + VT;
-  constexpr int NKC = BN * KCPR / NTHR;          // K chunks per thread per K tile
-  constexpr int VDG = NTHR / 16;                 // threads sharing 4 keys (one d-group each)
-  constexpr int DPT = D / VDG;                   // V elements per key per thread
-  constexpr int VW = DPT * ES / 4;               // 32-bit words per key per thread
+  constexpr int NKC = BN * KCPR / NTHR;          // 16-byte chunks per thread per K (or V) tile
   constexpr int NT = D / 32;
-  constexpr int NR = NKC + 4;                    // key rows a thread loads per tile
-  static_assert(NKC >= 1 && DPT >= 2 && (DPT & 1) == 0, "tile mapping");
+  constexpr int NR = NKC;                        // key rows a thread loads per tile (K and V share them)
+  static_assert(NKC >= 1, "tile mapping");
 
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(16))) float sbias[POOLED ? NSTAGE : 1][BN];
@@ -144,13 +148,10 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   const int ctx_last = (int)a.ctx_tok - 1;
 
   struct Rows { int r[NR]; };
-  struct Staged { u32x4 k[NKT][NKC]; uint32_t v[WO ? 4 : 1][VW]; float bias; };
+  struct Staged { u32x4 k[NKT][NKC]; u32x4 v[WO ? NKC : 1]; float bias; };
   struct STile { f32x16 t[2]; };
 
-  const int vdc = tid % VDG, vkg = tid / VDG;   // V: d-group, 4-key group (0..15)
-  auto key_of = [&](int r) -> int {
-    return r < NKC ? (tid + NTHR * r) / KCPR : 4 * vkg + (r - NKC);
-  };
+  auto key_of = [&](int r) -> int { return (tid + NTHR * r) / KCPR; };
   // source rows of the thread's keys of tile `tile` (padding -> row 0, masked later)
   auto lookup = [&](int tile) -> Rows {
     Rows rows;
@@ -179,17 +180,9 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
     }
     if constexpr (WO) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* src = Vg + (long long)rows.r[NKC + i] * KRB + vdc * DPT * ES;
-        if constexpr (VW == 1) {
-          g.v[i][0] = *(const uint32_t*)src;
-        } else if constexpr (VW == 2) {
-          const u32x2 v = *(const u32x2*)src;
-          g.v[i][0] = v.x; g.v[i][1] = v.y;
-        } else {
-          const u32x4 v = *(const u32x4*)src;
-          g.v[i][0] = v.x; g.v[i][1] = v.y; g.v[i][2] = v.z; g.v[i][3] = v.w;
-        }
+      for (int i = 0; i < NKC; ++i) {
+        const int c = (tid + NTHR * i) % KCPR;
+        g.v[i] = *(const u32x4*)(Vg + (long long)rows.r[i] * KRB + c * 16);
       }
     }
     g.bias = 0.f;
@@ -209,19 +202,12 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
         *(u32x4*)(Ks + kt * KT + kr * KRS + c * 16) = g.k[kt][i];
       }
     if constexpr (WO) {
-      // V^T: row d, 64 keys; key group g4 of each 16-key group sits at
-      // position group {0,2,1,3}[g4] (the order of the P^T operand)
       char* Vs = Ks + NKT * KT;
-      const int g4 = vkg & 3;
-      const int pos = 16 * (vkg >> 2) + 4 * (g4 == 1 ? 2 : (g4 == 2 ? 1 : g4));
-      const int byte = pos * ES;
 #pragma unroll
-      for (int j = 0; j < DPT; ++j) {
-        const int d = vdc * DPT + j;
-        const int wd = j >> 1, sh = (j & 1) * 16;
-        const uint32_t e0 = (g.v[0][wd] >> sh) & 0xffffu, e1 = (g.v[1][wd] >> sh) & 0xffffu;
-        const uint32_t e2 = (g.v[2][wd] >> sh) & 0xffffu, e3 = (g.v[3][wd] >> sh) & 0xffffu;
-        *(u32x2*)(Vs + d * VRS + byte) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+      for (int i = 0; i < NKC; ++i) {
+        const int q = tid + NTHR * i;
+        const int kr = q / KCPR, c = q % KCPR;
+        *(u32x4*)(Vs + kr * VRS + c * 16) = g.v[i];
       }
     }
     if constexpr (POOLED) {
@@ -231,7 +217,9 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   // Operands: lane (l32, h) reads row 32*i + l32, elements 16*s + 8*h .. +7
   // of a padded tile: one per-lane base, the rest are immediate offsets.
   const int kbase = l32 * KRS + 16 * h;
-  const int vbase = NKT * KT + l32 * VRS + 16 * h;
+  // V^T operand of lane (l32, h) in 16-lane group g = lane/16, m = lane%16:
+  // transposed reads at key rows 16 s + 4 h + m/4 (+8), d = 32 t + 16 (g%2) + 4 (m%4)
+  const int vbase = NKT * KT + (4 * h + ((lane & 15) >> 2)) * VRS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * ES;
   auto qk = [&](int stage) -> STile {
     const char* Ks = smem + stage * STAGE + kbase;
     STile S;
@@ -312,42 +300,52 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
     }
     l_run += psum;
     if constexpr (WO) {
-      const char* Vs = smem + (j % NSTAGE) * STAGE + vbase;
+      // addressing stays in the LDS address space so the constant offsets
+      // fold into the instructions
+      const lds_char* Vs = (const lds_char*)smem + (j % NSTAGE) * STAGE + vbase;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc[t] = mma32(*(const Op*)(Vs + 32 * t * VRS + 32 * s), pB[s], acc[t]);
+        for (int s = 0; s < 4; ++s) {
+          const lds_char* p = Vs + 16 * s * VRS + 32 * t * ES;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * VRS));
+          const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[t] = mma32(__builtin_bit_cast(Op, v), pB[s], acc[t]);
+        }
     }
   };
 
-  // ---- prologue: tiles 0 and 1 in LDS, tile 2's rows looked up
+  // ---- prologue: tiles 0 .. PF-1 in LDS, the rows of tile PF looked up
   Rows ra = {}, rb = {};
   Staged gs = {};
   if (nt > 0) {
-    ra = lookup(t_begin);
-    store(0, load(ra, t_begin));
-    rb = lookup(min(t_begin + 1, t_last));
-    gs = load(rb, min(t_begin + 1, t_last));
-    ra = lookup(min(t_begin + 2, t_last));
-    __syncthreads();
-    if (nt > 1) store(1, gs);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (p < nt) {
+        const int tp = t_begin + p;
+        store(p, load(lookup(tp), tp));
+      }
+    }
+    ra = lookup(min(t_begin + PF, t_last));
     __syncthreads();
   }
 
-  // Tile j: the rows of tile j+2 were looked up one tile earlier, those of
-  // tile j+3 are fetched now; loads past the last tile re-read it and are
-  // never stored.
+  // Tile j: the rows of tile j+PF were looked up one tile earlier, those of
+  // tile j+PF+1 are fetched now; loads past the last tile re-read it and are
+  // never stored.  Stage (j+PF) % NSTAGE was last read in tile j-1, which
+  // every wave finished before the barrier that closed it.
   for (int j = 0; j < nt; j += 2) {
-    gs = load(ra, min(t_begin + j + 2, t_last));
-    rb = lookup(min(t_begin + j + 3, t_last));
+    gs = load(ra, min(t_begin + j + PF, t_last));
+    rb = lookup(min(t_begin + j + PF + 1, t_last));
     softmax_pv(j, qk(j % NSTAGE));
-    if (j + 2 < nt) store((j + 2) % NSTAGE, gs);
+    if (j + PF < nt) store((j + PF) % NSTAGE, gs);
     __syncthreads();
     if (j + 1 < nt) {
-      gs = load(rb, min(t_begin + j + 3, t_last));
-      ra = lookup(min(t_begin + j + 4, t_last));
+      gs = load(rb, min(t_begin + j + 1 + PF, t_last));
+      ra = lookup(min(t_begin + j + PF + 2, t_last));
       softmax_pv(j + 1, qk((j + 1) % NSTAGE));
-      if (j + 3 < nt) store((j + 3) % NSTAGE, gs);
+      if (j + 1 + PF < nt) store((j + 1 + PF) % NSTAGE, gs);
       __syncthreads();
     }
   }

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/isa.h"
+#include "isa.h"
 
 namespace isa {
 
