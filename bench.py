@@ -13,6 +13,7 @@ between the stages of the same stream, the roofline of the dominant kernel
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,7 +38,8 @@ def parse():
     ap.add_argument("--workload", default="video_dit_layer")
     ap.add_argument("--gamma", type=float, default=None, help="override the workload's gamma")
     ap.add_argument("--dense-steps", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads of the CPU-oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads of the CPU-oracle sample (0: every head of the layer)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
@@ -65,6 +67,29 @@ def full_route_flops(views, w, kq_gamma):
     return total
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(ROOT, "profiles", "isa_video_dit_counters.txt")
+FLASH_SRC = os.path.join(ROOT, "sparse_attention_context_amd", "csrc", "isa_flash.hip")
+
+
+def counted_traffic(kernel_label):
+    """HBM bytes per launch of `kernel_label` from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE scaled by what they read for a
+    1 GiB copy), or None when the summary is missing or was taken on a
+    different version of the flash kernel source."""
+    try:
+        text = open(COUNTERS).read().splitlines()
+        src_hash = hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if not any(src_hash in ln for ln in text if "sha256" in ln):
+        return None
+    for ln in text:
+        if ln.startswith(kernel_label):
+            return float(ln.split()[-3]) * 1e6
+    return None
+
+
 def cpu_baseline(w, Q, K, V, gamma, heads):
     """The fp64 oracle on `heads` heads of the same inputs, scaled to the layer."""
     from oracle import isa_oracle as orc
@@ -73,6 +98,7 @@ def cpu_baseline(w, Q, K, V, gamma, heads):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing: single-threaded BLAS assumed
         cores = 1
+    heads = w.H if heads <= 0 else min(heads, w.H)
     t0 = time.perf_counter()
     for h in range(heads):
         p = orc.oracle_plan_head(Q[0, h], K[0, h], V[0, h], w.b, w.rho, gamma)
@@ -179,15 +205,34 @@ def main():
     roofline = None
     if full_ms and flops:
         achieved = flops / (full_ms * 1e-3) / 1e12
+        traffic = counted_traffic("isa_flash_kernel<128,1,1,8> full route") if w.name == "video_dit_layer" else None
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                     "kernel": "isa_flash_kernel (full route, gathered K/V; split-K merge timed separately)", "flops_per_launch": flops,
                     "avg_launch_ms": round(full_ms, 4)}
     dense_flops = 4 * w.d * w.Ns * (w.Ns + w.Nc) * w.B * w.H
 
+    # the other kernels against their own rooflines (algorithmic work per launch)
+    others = []
+    es = 2 if w.dtype == "bf16" else 4
+    nb_s = (w.Ns + w.b - 1) // w.b
+    M = nb_s + (w.Nc + w.b - 1) // w.b
+    if stage_ms.get("pool"):
+        pool_bytes = w.B * w.H * ((w.Ns + (w.Ns + w.Nc) + w.Ns) * w.d * es + (nb_s + 2 * M) * w.d * 4)
+        gbs = pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9
+        others.append({"kernel": "isa_pool_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": pool_bytes})
+    if stage_ms.get("sharp_taylor"):
+        mk = nb_s + counts["kc"]
+        tf = 4 * w.d * w.Ns * mk * w.B * w.H / (stage_ms["sharp_taylor"] * 1e-3) / 1e12
+        others.append({"kernel": "isa_flash_kernel pooled (sharpness + Taylor)", "bound": "mfma",
+                       "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "note": "4 d FLOP per (query, kept block); the lo half of the split keys is not counted"})
+
     cpu = None
     if not args.no_cpu:
-        log("cpu oracle on %d heads ..." % args.cpu_heads)
+        log("cpu oracle on %s heads ..." % (args.cpu_heads or "all"))
         cpu = cpu_baseline(w, Q, K, V, gamma, args.cpu_heads)
         log("cpu oracle: %.1f queries/s" % cpu["value"])
 
@@ -212,6 +257,7 @@ def main():
         "dense_tflops": None if dense_ms is None else round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roofline,
+        "other_rooflines": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -46,7 +46,8 @@ struct AttnArgs {
   const void* pv;
   const float* pbias;    // pooled: [BH][mk_pad]
   int mk_pad;
-  const int* q_rows;     // row table: [BH][n_rows]
+  const int* q_list;     // route block list: [BH][q_k] (table rows)
+  int q_k, nb_s;
   long long n_rows;      // virtual rows per head
   float* peak;           // [BH][Ns]
   int Ns, Nk;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void isa_attn_kernel(AttnArgs a) {
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   int qrow;
   if constexpr (RM == RM_IDENTITY) qrow = vrow < a.Ns ? (int)vrow : -1;
-  else qrow = vrow < a.n_rows ? a.q_rows[(long long)bh * a.n_rows + vrow] : -1;
+  else qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
 
   Op qB[D / 16];
   {
@@ -388,6 +389,7 @@ static AttnArgs attn_args(const Layout& L, const Bufs& B) {
   a.ctx_tok = L.ctx_tok;
   a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;
   a.mk_pad = L.mk_pad;
+  a.nb_s = L.nb_s;
   return a;
 }
 
@@ -407,7 +409,8 @@ static hipError_t pooled_t(const Layout& L, const Bufs& B, int mode, hipStream_t
   AttnArgs a = attn_args(L, B);
   if (mode == 0) return launch_attn_t<T, D, KM_POOLED, RM_IDENTITY, true, true>(a, L.Ns, L.BH, s);
   if (mode == 1) return launch_attn_t<T, D, KM_POOLED, RM_IDENTITY, false, true>(a, L.Ns, L.BH, s);
-  a.q_rows = (const int*)(B.ws + L.off_qrows_taylor);
+  a.q_list = (const int*)(B.ws + L.off_taylq);
+  a.q_k = L.nb_s - L.kq;
   return launch_attn_t<T, D, KM_POOLED, RM_TABLE, true, false>(a, L.taylor_rows, L.BH, s);
 }
 
@@ -415,7 +418,8 @@ template <typename T, int D>
 static hipError_t full_t(const Layout& L, const Bufs& B, bool dense, hipStream_t s) {
   AttnArgs a = attn_args(L, B);
   if (dense) return launch_attn_t<T, D, KM_DENSE, RM_IDENTITY, true, false>(a, L.Ns, L.BH, s);
-  a.q_rows = (const int*)(B.ws + L.off_qrows_full);
+  a.q_list = (const int*)(B.ws + L.off_fullq);
+  a.q_k = L.kq;
   return launch_attn_t<T, D, KM_GATHER, RM_TABLE, true, false>(a, L.full_rows, L.BH, s);
 }
 

@@ -90,4 +90,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 
 __device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Source row of virtual row v of a route whose query blocks are list[0..k)
+// (ascending): row list[v / b] * b + v % b, or -1 past the end of the list,
+// past the end of a short last block, or for an out-of-range block entry.
+__device__ __forceinline__ int route_row(const int* list, int k, int b, int nb, int Ns, long long v) {
+  if (v < 0 || v >= (long long)k * b) return -1;
+  const unsigned vv = (unsigned)v, ub = (unsigned)b;
+  const unsigned i = vv / ub;
+  const int blk = list[i];
+  const int row = blk * b + (int)(vv - i * ub);
+  return (blk >= 0 && blk < nb && row < Ns) ? row : -1;
+}
+
 }  // namespace isa

@@ -61,7 +61,8 @@ struct FlashArgs {
   const void* pv;
   const float* pbias;   // pooled: [BH][mk_pad] log2 n_j, -inf for padding
   int mk_pad;
-  const int* q_rows;    // row table: [BH][n_rows]
+  const int* q_list;    // route block list: [BH][q_k] (table rows)
+  int q_k, nb_s;        // blocks in the list per head; source blocks
   long long n_rows;     // virtual query rows per head
   float* peak;          // pooled: [BH][Ns]
   float* part_acc;      // split-K: [BH][row_tiles*BM][nsplit][D]
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   // ---- query row of this lane (invalid rows read row 0 and store nothing)
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   int qrow;
-  if constexpr (RM == FR_TABLE) qrow = vrow < a.n_rows ? a.q_rows[(long long)bh * a.n_rows + vrow] : -1;
+  if constexpr (RM == FR_TABLE) qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
   else qrow = vrow < a.Ns ? (int)vrow : -1;
   Op qB[D / 16];
   {
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   const long long bh = gid / rows_head;
   const long long vrow = gid - bh * rows_head;
   if (bh >= a.n_wg) return;  // n_wg carries BH here
-  const int qrow = vrow < a.n_rows ? a.q_rows[bh * a.n_rows + vrow] : -1;
+  const int qrow = route_row(a.q_list + bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
   if (qrow < 0) return;
   const long long prow = gid * a.nsplit;
   float mstar = -INFINITY;
@@ -434,6 +435,7 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
   a.ctx_tok = L.ctx_tok;
   a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;
   a.mk_pad = L.mk_pad;
+  a.nb_s = L.nb_s;
   return a;
 }
 
@@ -458,13 +460,15 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
     case FlashWhat::kDense:
       return flash_launch<D, FK_DENSE, FR_IDENTITY, true, false>(a, L.Ns, L.Nk, L.BH, s);
     case FlashWhat::kFull:
-      a.q_rows = (const int*)(B.ws + L.off_qrows_full);
+      a.q_list = (const int*)(B.ws + L.off_fullq);
+      a.q_k = L.kq;
       a.nsplit = L.full_splits;
       return flash_launch<D, FK_GATHER, FR_TABLE, true, false>(a, L.full_rows, (long long)L.Ns + L.ctx_tok,
                                                                 L.BH, s);
     case FlashWhat::kFullMerge: {
       if (L.full_splits <= 1 || L.full_rows == 0) return hipSuccess;
-      a.q_rows = (const int*)(B.ws + L.off_qrows_full);
+      a.q_list = (const int*)(B.ws + L.off_fullq);
+      a.q_k = L.kq;
       a.nsplit = L.full_splits;
       a.n_rows = L.full_rows;
       a.row_tiles = (int)((L.full_rows + kFlashRows - 1) / kFlashRows);
@@ -479,7 +483,8 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
     case FlashWhat::kSharp:
       return flash_launch<D, FK_POOLED, FR_IDENTITY, false, true>(a, L.Ns, L.mk_pad, L.BH, s);
     case FlashWhat::kTaylor:
-      a.q_rows = (const int*)(B.ws + L.off_qrows_taylor);
+      a.q_list = (const int*)(B.ws + L.off_taylq);
+      a.q_k = L.nb_s - L.kq;
       return flash_launch<D, FK_POOLED, FR_TABLE, true, false>(a, L.taylor_rows, L.mk_pad, L.BH, s);
   }
   return hipErrorInvalidValue;

@@ -100,8 +100,6 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   take(&L->off_sh, bh * L->nb_s * 8);
   take(&L->off_fullq, bh * L->kq * 4);
   take(&L->off_taylq, bh * (L->nb_s - L->kq) * 4);
-  take(&L->off_qrows_full, bh * L->full_rows * 4);
-  take(&L->off_qrows_taylor, bh * L->taylor_rows * 4);
   {
     const int64_t prow = L->full_splits > 1 ? bh * ((L->full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L->full_splits : 0;
     take(&L->off_part_acc, prow * d * 4);

@@ -185,8 +185,6 @@ struct SelArgs {
   double* sh;
   int* full_q;
   int* taylor_q;
-  int* qrows_full;
-  int* qrows_taylor;
   int Ns, Nc, b, nb_s, nb_c, kc, kq, sal_tiles, tail_s;
 };
 
@@ -207,11 +205,13 @@ __global__ __launch_bounds__(256) void isa_select_ctx_kernel(SelArgs a) {
   __syncthreads();
   // full-route context key rows: kept block kb covers rows Ns + kb*b + [0, b),
   // -1 past the end of a short last block
-  const long long ntok = (long long)a.kc * a.b;
+  const int ntok = a.kc * a.b;
   int* rows = a.ctx_rows + bh * ntok;
-  for (long long t = tid; t < ntok; t += 256) {
-    const int kb = kept[t / a.b];
-    const int r = kb * a.b + (int)(t % a.b);
+  const unsigned ub = (unsigned)a.b;
+  for (int t = tid; t < ntok; t += 256) {
+    const unsigned i = (unsigned)t / ub;
+    const int kb = kept[i];
+    const int r = kb * a.b + (int)((unsigned)t - i * ub);
     rows[t] = (kb >= 0 && kb < a.nb_c && r < a.Nc) ? a.Ns + r : -1;
   }
 }
@@ -243,21 +243,6 @@ __global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
   int* fq = a.full_q + bh * a.kq;
   int* tq = a.taylor_q + bh * (a.nb_s - a.kq);
   select_topk(sh, a.nb_s, a.kq, fq, tq, sm);
-  __syncthreads();
-  const long long nf = (long long)a.kq * a.b;
-  const long long nt = (long long)(a.nb_s - a.kq) * a.b;
-  int* rf = a.qrows_full + bh * nf;
-  int* rt = a.qrows_taylor + bh * nt;
-  for (long long v = tid; v < nf; v += 256) {
-    const int qb = fq[v / a.b];
-    const int r = qb * a.b + (int)(v % a.b);
-    rf[v] = (qb >= 0 && qb < a.nb_s && r < a.Ns) ? r : -1;
-  }
-  for (long long v = tid; v < nt; v += 256) {
-    const int qb = tq[v / a.b];
-    const int r = qb * a.b + (int)(v % a.b);
-    rt[v] = (qb >= 0 && qb < a.nb_s && r < a.Ns) ? r : -1;
-  }
 }
 
 static SelArgs sel_args(const Layout& L, const Bufs& B) {
@@ -270,8 +255,6 @@ static SelArgs sel_args(const Layout& L, const Bufs& B) {
   a.sh = (double*)(B.ws + L.off_sh);
   a.full_q = (int*)(B.ws + L.off_fullq);
   a.taylor_q = (int*)(B.ws + L.off_taylq);
-  a.qrows_full = (int*)(B.ws + L.off_qrows_full);
-  a.qrows_taylor = (int*)(B.ws + L.off_qrows_taylor);
   a.Ns = L.Ns; a.Nc = L.Nc; a.b = L.b; a.nb_s = L.nb_s; a.nb_c = L.nb_c;
   a.kc = L.kc; a.kq = L.kq; a.sal_tiles = L.sal_tiles; a.tail_s = L.tail_s;
   return a;
