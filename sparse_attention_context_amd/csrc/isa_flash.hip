@@ -37,8 +37,9 @@
 // peak probability.
 //
 // Full-route key ranges over few row tiles are split across workgroups
-// (split-K); each split writes unnormalised fp32 partials (acc, ref max, sum)
-// and the merge kernel combines them in split order (deterministic).
+// (split-K); each split writes its own normalised output in bf16 with its
+// reference max and sum in fp32, and the merge kernel takes the sum-weighted
+// mean of the splits in split order (deterministic).
 #include "isa_device.h"
 #include "isa_kernels.h"
 
@@ -65,7 +66,7 @@ struct FlashArgs {
   int q_k, nb_s;        // blocks in the list per head; source blocks
   long long n_rows;     // virtual query rows per head
   float* peak;          // pooled: [BH][Ns]
-  float* part_acc;      // split-K: [BH][row_tiles*BM][nsplit][D]
+  bf16_t* part_o;       // split-K: [BH][row_tiles*BM][nsplit][D] normalised split outputs
   float* part_ml;       // split-K: [BH][row_tiles*BM][nsplit][2]
   int nsplit, tiles_per_split;
   int Ns, Nk;
@@ -372,13 +373,16 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
       }
     }
   } else if constexpr (WO) {
+    // split partial: this split's normalised output (bf16) and its (ref max, sum)
     const long long prow = ((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split;
-    float* pa = a.part_acc + prow * D;
+    bf16_t* po = a.part_o + prow * D;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *(f32x4*)(pa + 32 * t + 8 * g + 4 * h) = f32x4{acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]};
+        *(u32x2*)(po + 32 * t + 8 * g + 4 * h) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                                                       pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
     if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref, l_tot};
   }
 }
@@ -399,14 +403,16 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   const long long prow = gid * a.nsplit;
   float mstar = -INFINITY;
   for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[(prow + s) * 2]);
+  // split s weighs in with its sum rescaled to the common max
   float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
   for (int s = 0; s < a.nsplit; ++s) {
     const float m = a.part_ml[(prow + s) * 2];
     if (m == -INFINITY) continue;
-    const float wgt = __builtin_amdgcn_exp2f((m - mstar) * a.scale_log2);
-    l += wgt * a.part_ml[(prow + s) * 2 + 1];
-    const f32x4 v = *(const f32x4*)(a.part_acc + (prow + s) * D + e);
-    o0 += wgt * v.x; o1 += wgt * v.y; o2 += wgt * v.z; o3 += wgt * v.w;
+    const float wgt = __builtin_amdgcn_exp2f((m - mstar) * a.scale_log2) * a.part_ml[(prow + s) * 2 + 1];
+    l += wgt;
+    const u32x2 v = *(const u32x2*)(a.part_o + (prow + s) * D + e);
+    o0 += wgt * __uint_as_float(v.x << 16); o1 += wgt * __uint_as_float(v.x & 0xffff0000u);
+    o2 += wgt * __uint_as_float(v.y << 16); o3 += wgt * __uint_as_float(v.y & 0xffff0000u);
   }
   const float inv = 1.0f / l;
   bf16_t* op = (bf16_t*)a.O + (bh * a.Ns + qrow) * D + e;
@@ -429,7 +435,7 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
     a.pv = B.ws + L.off_pv;
     a.pbias = (const float*)(B.ws + L.off_pbias);
     a.peak = (float*)(B.ws + L.off_peak);
-    a.part_acc = (float*)(B.ws + L.off_part_acc);
+    a.part_o = (bf16_t*)(B.ws + L.off_part_o);
     a.part_ml = (float*)(B.ws + L.off_part_ml);
   }
   a.ctx_tok = L.ctx_tok;

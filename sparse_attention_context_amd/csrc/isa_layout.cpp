@@ -102,7 +102,7 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   take(&L->off_taylq, bh * (L->nb_s - L->kq) * 4);
   {
     const int64_t prow = L->full_splits > 1 ? bh * ((L->full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L->full_splits : 0;
-    take(&L->off_part_acc, prow * d * 4);
+    take(&L->off_part_o, prow * d * 2);
     take(&L->off_part_ml, prow * 2 * 4);
   }
   L->total = o;

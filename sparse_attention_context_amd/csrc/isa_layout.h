@@ -41,7 +41,7 @@ struct Layout {
   size_t off_qbar, off_kbar, off_vbar, off_salp, off_sal, off_kept;
   size_t off_pkhi, off_pklo, off_pv, off_pbias, off_ctxrows;
   size_t off_peak, off_sh, off_fullq, off_taylq;
-  size_t off_part_acc, off_part_ml;
+  size_t off_part_o, off_part_ml;
   size_t total;
 };
 
