@@ -41,7 +41,8 @@
  *
  * Workspace: caller-owned device memory of isa_workspace_size() bytes,
  * 256-byte aligned.  isa_plan() leaves the plan (pooled blocks, scores and
- * index lists) in it; isa_forward() reads it.  It must stay alive and
+ * index lists) in it; isa_forward() reads it and adds each source row's
+ * log-sum-exp, which isa_backward() reads (bf16).  It must stay alive and
  * unmodified until the work that reads it has completed on the stream.
  *
  * Errors: every call validates its arguments on the host before enqueuing
@@ -125,7 +126,7 @@ typedef enum isa_stage {
   ISA_STAGE_PACK = 4,         /* kept pooled keys (bf16 hi/lo), values and log2 n_j */
   ISA_STAGE_SHARP_TAYLOR = 5, /* per-row peak probability + Taylor output of every row into O */
   ISA_STAGE_SHARP = 6,        /* per-row peak probability only (sharpness) */
-  ISA_STAGE_SELECT_Q = 7,     /* sh, full_q / taylor_q (top-gamma) and query-row tables */
+  ISA_STAGE_SELECT_Q = 7,     /* sh and full_q / taylor_q (top-gamma) */
   ISA_STAGE_TAYLOR = 8,       /* Taylor output of the Taylor-route rows into O */
   ISA_STAGE_FULL = 9,         /* full attention of the full-route rows: into O, or into
                                  split partials when the key range is split */
@@ -169,6 +170,55 @@ isa_status isa_attention(const isa_desc* desc, const void* Q, const void* K, con
  * page "深度学习注意力机制：全局与时间注意力的计算效率对比", section 1. */
 isa_status isa_dense_forward(const isa_desc* desc, const void* Q, const void* K, const void* V,
                              void* O, void* stream);
+
+/* ---- Backward pass (bf16 only) -------------------------------------------
+ *
+ * The pages give no backward pass.  These calls compute the derivatives of
+ * the forward above for L = sum(dO * O) with the selection frozen: kept_ctx
+ * and full_q are discrete decisions and get no gradient (nor do sal and sh),
+ * the counts n_j are constants, a pooled key's (value's) gradient is shared
+ * equally by the rows of its block (it is their mean), and rows of pruned
+ * context blocks get zero gradient:
+ *   full rows   ds = p (dO.v - D), D = dO.o;  dq = ds K/sqrt d,
+ *               dk += ds^T q/sqrt d, dv += p^T dO over the kept tokens;
+ *   Taylor rows the same over the kept pooled blocks (p n_j-weighted), then
+ *               dk_t += dkbar_j/n_j, dv_t += dvbar_j/n_j for rows t of block j.
+ *
+ * workspace: the forward workspace of an isa_attention or isa_plan +
+ * isa_forward call with the same desc and inputs (plan and per-row log-sum-
+ * exp); read only.  bwd_workspace: caller-owned device memory of
+ * isa_backward_workspace_size() bytes, 256-byte aligned.  O is the forward's
+ * output and dO its gradient, both [B,H,Ns,d]; dQ [B,H,Ns,d], dK and dV
+ * [B,H,Ns+Nc,d] are written entirely.  All of element type bf16; f32 gives
+ * ISA_ERR_UNSUPPORTED.  Deterministic (no atomics). */
+
+typedef enum isa_bwd_stage {
+  ISA_BWD_DELTA = 0,        /* D = rowsum(dO * O) of every source row */
+  ISA_BWD_DKV_POOLED = 1,   /* Taylor rows: per-split partial gradients of the kept pooled keys, values */
+  ISA_BWD_DKV_REDUCE = 2,   /* sums those partials in split order (zero without Taylor rows) */
+  ISA_BWD_DKV_FULL = 3,     /* full rows: dK, dV of every source and kept context row, plus the
+                               pooled share of its block */
+  ISA_BWD_ZERO_PRUNED = 4,  /* zeroes dK, dV rows of pruned context blocks */
+  ISA_BWD_DQ_FULL = 5,      /* full rows: dQ, or split partials when the key range is split */
+  ISA_BWD_DQ_MERGE = 6,     /* merges the dQ split partials (no-op unsplit) */
+  ISA_BWD_DQ_POOLED = 7     /* Taylor rows: dQ */
+} isa_bwd_stage;
+
+/* Bytes of backward workspace isa_backward needs for *desc. */
+isa_status isa_backward_workspace_size(const isa_desc* desc, size_t* bytes);
+
+/* dQ, dK, dV of the layer planned in `workspace` (stages DELTA .. DQ_POOLED
+ * in order). */
+isa_status isa_backward(const isa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const void* workspace, size_t workspace_bytes, void* bwd_workspace,
+                        size_t bwd_workspace_bytes, void* dQ, void* dK, void* dV, void* stream);
+
+/* One backward stage (one kernel launch); same arguments as isa_backward.
+ * Unknown stage: ISA_ERR_INVALID_ARGUMENT. */
+isa_status isa_run_backward_stage(const isa_desc* desc, int stage, const void* Q, const void* K, const void* V,
+                                  const void* O, const void* dO, const void* workspace, size_t workspace_bytes,
+                                  void* bwd_workspace, size_t bwd_workspace_bytes, void* dQ, void* dK, void* dV,
+                                  void* stream);
 
 /* Device pointers to the plan held in a workspace (no device access). */
 isa_status isa_plan_views(const isa_desc* desc, void* workspace, size_t workspace_bytes,

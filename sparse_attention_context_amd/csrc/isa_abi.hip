@@ -140,4 +140,59 @@ extern "C" isa_status isa_run_stage(const isa_desc* desc, int stage, const void*
   return ISA_OK;
 }
 
+namespace {
+
+// Validates the backward arguments; fills the two layouts.
+isa_status bwd_prepare(const isa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                       const void* dO, const void* ws, size_t ws_bytes, void* bws, size_t bws_bytes, void* dQ,
+                       void* dK, void* dV, isa::Layout* L, isa::BwdLayout* W) {
+  isa_status st = isa::make_layout(desc, L);
+  if (st != ISA_OK) return st;
+  if ((st = isa::make_bwd_layout(*L, W)) != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
+  if ((st = check_io(dO, dQ, dK, dV, true)) != ISA_OK) return st;
+  if ((st = check_ws(*L, ws, ws_bytes)) != ISA_OK) return st;
+  if (!bws) return ISA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)bws % isa::kWsAlign) != 0 || bws_bytes < W->total) return ISA_ERR_WORKSPACE;
+  return ISA_OK;
+}
+
+}  // namespace
+
+extern "C" isa_status isa_run_backward_stage(const isa_desc* desc, int stage, const void* Q, const void* K,
+                                             const void* V, const void* O, const void* dO, const void* workspace,
+                                             size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes,
+                                             void* dQ, void* dK, void* dV, void* stream) {
+  if (stage < ISA_BWD_DELTA || stage > ISA_BWD_DQ_POOLED) return ISA_ERR_INVALID_ARGUMENT;
+  isa::Layout L;
+  isa::BwdLayout W;
+  isa_status st = bwd_prepare(desc, Q, K, V, O, dO, workspace, workspace_bytes, bwd_workspace, bwd_workspace_bytes,
+                              dQ, dK, dV, &L, &W);
+  if (st != ISA_OK) return st;
+  const isa::BwdBufs B{Q, K, V, O, dO, dQ, dK, dV, (const char*)workspace, (char*)bwd_workspace};
+  static const isa::BwdWhat kWhat[] = {isa::BwdWhat::kDelta,    isa::BwdWhat::kDkvPooled, isa::BwdWhat::kDkvReduce,
+                                       isa::BwdWhat::kDkvFull,  isa::BwdWhat::kZeroPruned, isa::BwdWhat::kDqFull,
+                                       isa::BwdWhat::kDqMerge,  isa::BwdWhat::kDqPooled};
+  ISA_RUN(isa::launch_backward(L, W, B, kWhat[stage], (hipStream_t)stream));
+  return ISA_OK;
+}
+
+extern "C" isa_status isa_backward(const isa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                                   const void* dO, const void* workspace, size_t workspace_bytes, void* bwd_workspace,
+                                   size_t bwd_workspace_bytes, void* dQ, void* dK, void* dV, void* stream) {
+  isa::Layout L;
+  isa::BwdLayout W;
+  isa_status st = bwd_prepare(desc, Q, K, V, O, dO, workspace, workspace_bytes, bwd_workspace, bwd_workspace_bytes,
+                              dQ, dK, dV, &L, &W);
+  if (st != ISA_OK) return st;
+  const isa::BwdBufs B{Q, K, V, O, dO, dQ, dK, dV, (const char*)workspace, (char*)bwd_workspace};
+  hipStream_t s = (hipStream_t)stream;
+  // the pooled-key gradients must exist before the full dK/dV epilogue adds them
+  for (isa::BwdWhat w : {isa::BwdWhat::kDelta, isa::BwdWhat::kDkvPooled, isa::BwdWhat::kDkvReduce,
+                         isa::BwdWhat::kDkvFull, isa::BwdWhat::kZeroPruned, isa::BwdWhat::kDqFull,
+                         isa::BwdWhat::kDqMerge, isa::BwdWhat::kDqPooled})
+    ISA_RUN(isa::launch_backward(L, W, B, w, s));
+  return ISA_OK;
+}
+
 extern "C" const char* isa_last_error(void) { return g_last_error; }

@@ -66,6 +66,7 @@ struct FlashArgs {
   int q_k, nb_s;        // blocks in the list per head; source blocks
   long long n_rows;     // virtual query rows per head
   float* peak;          // pooled: [BH][Ns]
+  float* lse;           // [BH][Ns] log2-domain log-sum-exp of each written row (null: not kept)
   bf16_t* part_o;       // split-K: [BH][row_tiles*BM][nsplit][D] normalised split outputs
   float* part_ml;       // split-K: [BH][row_tiles*BM][nsplit][2]
   int nsplit, tiles_per_split;
@@ -371,6 +372,10 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
       if constexpr (WP) {
         if (h == 0) a.peak[(long long)bh * a.Ns + qrow] = __builtin_amdgcn_exp2f(m_true - m_ref) * inv;
       }
+      if constexpr (WO) {
+        // p = exp2(x - lse) with x = S*sc (tokens) or S*sc + log2 n_j (pooled)
+        if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = (POOLED ? m_ref : m_ref * sc) + __builtin_log2f(l_tot);
+      }
     }
   } else if constexpr (WO) {
     // split partial: this split's normalised output (bf16) and its (ref max, sum)
@@ -415,6 +420,7 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
     o2 += wgt * __uint_as_float(v.y << 16); o3 += wgt * __uint_as_float(v.y & 0xffff0000u);
   }
   const float inv = 1.0f / l;
+  if (a.lse && e == 0) a.lse[bh * a.Ns + qrow] = mstar * a.scale_log2 + __builtin_log2f(l);
   bf16_t* op = (bf16_t*)a.O + (bh * a.Ns + qrow) * D + e;
   *(u32x2*)op = u32x2{pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv)};
 }
@@ -437,6 +443,7 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
     a.peak = (float*)(B.ws + L.off_peak);
     a.part_o = (bf16_t*)(B.ws + L.off_part_o);
     a.part_ml = (float*)(B.ws + L.off_part_ml);
+    a.lse = (float*)(B.ws + L.off_lse);
   }
   a.ctx_tok = L.ctx_tok;
   a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;

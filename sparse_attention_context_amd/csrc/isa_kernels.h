@@ -54,4 +54,22 @@ hipError_t launch_full_merge(const Layout& L, const Bufs& B, hipStream_t s);
 enum class FlashWhat { kDense, kFull, kFullMerge, kSharpTaylor, kSharp, kTaylor };
 hipError_t launch_flash(const Layout& L, const Bufs& B, FlashWhat what, hipStream_t s);
 
+// Backward pass (isa_flash_bwd.hip): inputs, forward output, its gradient,
+// the three gradients, the planned forward workspace (read only) and the
+// backward workspace.
+struct BwdBufs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  const char* ws;
+  char* bws;
+};
+enum class BwdWhat { kDelta, kDkvPooled, kDkvReduce, kDkvFull, kZeroPruned, kDqFull, kDqMerge, kDqPooled };
+hipError_t launch_backward(const Layout& L, const BwdLayout& W, const BwdBufs& B, BwdWhat what, hipStream_t s);
+
 }  // namespace isa

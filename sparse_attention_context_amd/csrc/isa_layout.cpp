@@ -105,11 +105,54 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
     take(&L->off_part_o, prow * d * 2);
     take(&L->off_part_ml, prow * 2 * 4);
   }
+  take(&L->off_lse, bh * D.Ns * 4);
   L->total = o;
   return ISA_OK;
 }
 
+isa_status make_bwd_layout(const Layout& L, BwdLayout* B) {
+  if (!B) return ISA_ERR_INVALID_ARGUMENT;
+  if (L.es != 2) return ISA_ERR_UNSUPPORTED;
+  const size_t bh = (size_t)L.BH, d = (size_t)L.d;
+  B->dkv_key_tiles = (L.mk + kBwdKeys - 1) / kBwdKeys;
+  // pooled dK/dV: split the Taylor rows so that about four workgroups per
+  // compute unit exist, never more splits than row steps
+  const int64_t steps = (L.taylor_rows + kBwdRows - 1) / kBwdRows;
+  const int64_t units = (int64_t)bh * B->dkv_key_tiles;
+  int64_t sp = units > 0 ? (4 * (int64_t)kCUs + units - 1) / units : 1;
+  sp = sp < 1 ? 1 : sp;
+  sp = sp > steps ? steps : sp;
+  sp = sp > 64 ? 64 : sp;
+  B->dkv_splits = (int)(sp < 1 ? 1 : sp);
+  size_t o = 0;
+  auto take = [&](size_t* off, size_t bytes) {
+    *off = o;
+    o = align_up(o + (bytes ? bytes : 1));
+  };
+  take(&B->off_delta, bh * L.Ns * 4);
+  take(&B->off_part_dkv, (size_t)B->dkv_splits * bh * L.mk_pad * 2 * d * 4);
+  take(&B->off_dkvbar, bh * L.mk_pad * 2 * d * 4);
+  {
+    const int64_t prow = L.full_splits > 1 ? (int64_t)bh * ((L.full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L.full_splits : 0;
+    take(&B->off_part_dq, prow * d * 4);
+  }
+  B->total = o;
+  return ISA_OK;
+}
+
 }  // namespace isa
+
+extern "C" isa_status isa_backward_workspace_size(const isa_desc* desc, size_t* bytes) {
+  if (!bytes) return ISA_ERR_INVALID_ARGUMENT;
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  isa::BwdLayout B;
+  st = isa::make_bwd_layout(L, &B);
+  if (st != ISA_OK) return st;
+  *bytes = B.total;
+  return ISA_OK;
+}
 
 extern "C" isa_status isa_get_counts(const isa_desc* desc, isa_counts* out) {
   if (!out) return ISA_ERR_INVALID_ARGUMENT;

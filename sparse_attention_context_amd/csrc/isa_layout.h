@@ -42,11 +42,31 @@ struct Layout {
   size_t off_pkhi, off_pklo, off_pv, off_pbias, off_ctxrows;
   size_t off_peak, off_sh, off_fullq, off_taylq;
   size_t off_part_o, off_part_ml;
+  size_t off_lse;      // [BH][Ns] log2-domain log-sum-exp of each source row's softmax
   size_t total;
 };
 
 // Validates *desc and fills *L.  Returns ISA_OK or the error of isa.h.
 isa_status make_layout(const isa_desc* desc, Layout* L);
+
+// Backward pass (bf16): keys per dK/dV workgroup (4 waves x 32) and query
+// rows staged per step.
+constexpr int kBwdKeys = 128;
+constexpr int kBwdRows = 64;
+
+struct BwdLayout {
+  int dkv_splits;      // query-row splits of the pooled (Taylor) dK/dV pass
+  int dkv_key_tiles;   // ceil(mk / kBwdKeys)
+  // byte offsets into the backward workspace
+  size_t off_delta;    // [BH][Ns] fp32: rowsum(dO * O)
+  size_t off_part_dkv; // [dkv_splits][BH][mk_pad][2][d] fp32 pooled-key gradient partials
+  size_t off_dkvbar;   // [BH][mk_pad][2][d] fp32: pooled-key gradients (dkbar, dvbar)
+  size_t off_part_dq;  // [BH][full row tiles * kFlashRows][full_splits][d] fp32 split-K partials of dQ
+  size_t total;
+};
+
+// Fills *B for the layout L (ISA_ERR_UNSUPPORTED unless bf16).
+isa_status make_bwd_layout(const Layout& L, BwdLayout* B);
 
 // Key-range splits for `units` workgroups of `ntiles` key tiles each, on
 // kCUs compute units running one workgroup each: the count that minimises

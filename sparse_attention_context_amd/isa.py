@@ -21,7 +21,8 @@ STATUS = {0: "ISA_OK", 1: "ISA_ERR_INVALID_ARGUMENT", 2: "ISA_ERR_UNSUPPORTED", 
           4: "ISA_ERR_DEVICE"}
 
 EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "isa_attention",
-           "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_status_string", "isa_last_error"]
+           "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_backward_workspace_size", "isa_backward",
+           "isa_run_backward_stage", "isa_status_string", "isa_last_error"]
 
 # isa_stage values (include/isa.h)
 STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
@@ -30,6 +31,9 @@ STAGE = {name: i for i, name in enumerate(STAGES)}
 # the stage sequence of isa_attention when some query blocks stay on the Taylor route
 ATTENTION_STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "select_q", "full",
                     "full_merge"]
+# isa_bwd_stage values, in the order isa_backward runs them
+BWD_STAGES = ["delta", "dkv_pooled", "dkv_reduce", "dkv_full", "zero_pruned", "dq_full", "dq_merge", "dq_pooled"]
+BWD_STAGE = {name: i for i, name in enumerate(BWD_STAGES)}
 
 
 class Desc(ctypes.Structure):
@@ -76,11 +80,15 @@ def lib():
         L.isa_dense_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp]
         L.isa_plan_views.argtypes = [P(Desc), vp, sz, P(PlanView)]
         L.isa_run_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
+        L.isa_backward_workspace_size.argtypes = [P(Desc), P(sz)]
+        L.isa_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp]
+        L.isa_run_backward_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp,
+                                             vp]
         L.isa_status_string.argtypes = [ctypes.c_int]
         L.isa_status_string.restype = ctypes.c_char_p
         L.isa_last_error.argtypes = []
         L.isa_last_error.restype = ctypes.c_char_p
-        for fn in EXPORTS[:8]:
+        for fn in EXPORTS[:11]:
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -217,3 +225,46 @@ def plan_views(Q, K, workspace, b, rho, gamma):
         "counts": {"nb_s": c.nb_s, "nb_c": c.nb_c, "kc": c.kc, "kq": c.kq, "m_kept": c.m_kept,
                    "full_keys": c.full_keys},
     }
+
+
+def backward_workspace_size(desc):
+    n = ctypes.c_size_t()
+    _check("isa_backward_workspace_size", lib().isa_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def new_backward_workspace(desc, device):
+    return torch.empty(backward_workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+def _bwd_args(Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma):
+    _inputs(Q, K, V)
+    for t in (O, dO):
+        if t.shape != Q.shape or t.dtype != Q.dtype or not t.is_contiguous():
+            raise ValueError("O and dO must be contiguous and shaped and typed like Q")
+    desc = desc_for(Q, K, b, rho, gamma)
+    bws = new_backward_workspace(desc, Q.device) if bwd_workspace is None else bwd_workspace
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.empty_like(K) if dK is None else dK
+    dV = torch.empty_like(V) if dV is None else dV
+    return desc, bws, dQ, dK, dV
+
+
+def backward(Q, K, V, O, dO, workspace, b, rho, gamma, bwd_workspace=None, dQ=None, dK=None, dV=None, stream=None):
+    """isa_backward: (dQ, dK, dV, bwd_workspace) of the layer planned in `workspace`
+    (from attention() or plan() + forward() on the same inputs), O its output."""
+    desc, bws, dQ, dK, dV = _bwd_args(Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma)
+    _check("isa_backward", lib().isa_backward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
+                                              _ptr(workspace), workspace.numel(), _ptr(bws), bws.numel(),
+                                              _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)))
+    return dQ, dK, dV, bws
+
+
+def run_backward_stage(stage, Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma, stream=None):
+    """isa_run_backward_stage: one kernel of the backward pass (name or isa_bwd_stage value)."""
+    desc = desc_for(Q, K, b, rho, gamma)
+    code = BWD_STAGE[stage] if isinstance(stage, str) else int(stage)
+    _check("isa_run_backward_stage",
+           lib().isa_run_backward_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
+                                        _ptr(workspace), workspace.numel(), _ptr(bwd_workspace),
+                                        bwd_workspace.numel(), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)))

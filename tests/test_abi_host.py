@@ -114,3 +114,42 @@ def test_status_strings():
     for code in range(5):
         assert L.isa_status_string(code).decode().startswith(isa.STATUS[code])
     assert L.isa_last_error() == b""
+
+
+def test_backward_validation_before_launch():
+    L = isa.lib()
+    d = _desc(dtype="bf16")
+    need = isa.workspace_size(d)
+    bneed = isa.backward_workspace_size(d)
+    assert bneed > 0 and bneed % 256 == 0
+    host = ctypes.create_string_buffer(need + bneed + 1024)
+    base = (ctypes.addressof(host) + 255) // 256 * 256
+    ws = ctypes.c_void_p(base)
+    bws = ctypes.c_void_p(base + (need + 255) // 256 * 256)
+    p = ctypes.c_void_p(base)  # never dereferenced: every call below fails validation
+    nul = ctypes.c_void_p(0)
+    D = ctypes.byref(d)
+    # f32 has no backward
+    f = _desc(dtype="f32")
+    with pytest.raises(isa.IsaError) as e:
+        isa.backward_workspace_size(f)
+    assert e.value.code == 2
+    assert L.isa_backward(ctypes.byref(f), p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 2
+    # null / misaligned tensors, small or misaligned workspaces
+    assert L.isa_backward(D, p, p, p, p, nul, ws, need, bws, bneed, p, p, p, nul) == 1
+    assert L.isa_backward(D, p, p, p, p, p, ws, need, bws, bneed, p, nul, p, nul) == 1
+    assert L.isa_backward(D, p, p, p, p, ctypes.c_void_p(base + 4), ws, need, bws, bneed, p, p, p, nul) == 1
+    assert L.isa_backward(D, p, p, p, p, p, ws, need - 1, bws, bneed, p, p, p, nul) == 3
+    assert L.isa_backward(D, p, p, p, p, p, ws, need, bws, bneed - 1, p, p, p, nul) == 3
+    assert L.isa_backward(D, p, p, p, p, p, ws, need, ctypes.c_void_p(base + 16), bneed, p, p, p, nul) == 3
+    assert L.isa_backward(D, p, p, p, p, p, ws, need, nul, bneed, p, p, p, nul) == 1
+    assert L.isa_run_backward_stage(D, 8, p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 1
+    assert L.isa_run_backward_stage(D, -1, p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 1
+
+
+def test_backward_workspace_sizes_of_the_workloads():
+    for w in ALL:
+        if w.dtype != "bf16":
+            continue
+        d = isa.make_desc(w.B, w.H, w.Ns, w.Nc, w.d, w.b, w.rho, w.gamma, w.dtype)
+        assert 0 < isa.backward_workspace_size(d) < 2e9
