@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing isa_backward")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter collection: one layer call, one dense call and a 1 GiB elementwise copy "
                          "(the copy calibrates byte counters), no timing")
@@ -108,6 +110,58 @@ def cpu_baseline(w, Q, K, V, gamma, heads):
     return {"value": w.B * w.Ns / per_layer, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
             "sample": "%d of %d heads of the same inputs (plan + forward, fp64 NumPy), %.1f s, scaled by H/%d"
                       % (heads, w.H, dt, heads)}
+
+
+def time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
+    """isa_backward on the same layer (plan frozen, dO seeded N(0,1) in bf16):
+    whole-call time, per-stage HIP events, and the full-route kernels against
+    the bf16 MFMA peak at their algorithmic FLOPs per (query, key) pair."""
+    import torch
+    from sparse_attention_context_amd import isa
+    g = torch.Generator(device=Qd.device).manual_seed(7)
+    dO = torch.randn(Qd.shape, generator=g, device=Qd.device, dtype=torch.float32).to(Qd.dtype)
+    isa.attention(Qd, Kd, Vd, w.b, w.rho, gamma, out=O, workspace=ws)
+    dQ, dK, dV, bws = isa.backward(Qd, Kd, Vd, O, dO, ws, w.b, w.rho, gamma)
+
+    def bstep():
+        isa.backward(Qd, Kd, Vd, O, dO, ws, w.b, w.rho, gamma, bwd_workspace=bws, dQ=dQ, dK=dK, dV=dV)
+
+    bstep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.backward_steps):
+        bstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.backward_steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(isa.BWD_STAGES) + 1)]
+           for _ in range(args.backward_steps)]
+    for k in range(args.backward_steps):
+        for i, name in enumerate(isa.BWD_STAGES):
+            evs[k][i].record(stream)
+            isa.run_backward_stage(name, Qd, Kd, Vd, O, dO, ws, bws, dQ, dK, dV, w.b, w.rho, gamma)
+        evs[k][-1].record(stream)
+    torch.cuda.synchronize()
+    st = {name: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.backward_steps)) / args.backward_steps
+          for i, name in enumerate(isa.BWD_STAGES)}
+    log("isa_backward: %.3f ms/call; stages: %s" % (ms, ", ".join("%s %.3f" % kv for kv in st.items())))
+    pairs = full_route_flops(views, w, gamma) // (4 * w.d)
+    # per (query, key) pair of the full route: dK kernel S, dP, dK (6 d); dV kernel S, dV (4 d); dQ kernel S, dP, dQ (6 d)
+    kernels = {"dk_full": ("isa_bwd_dkdv_kernel dK (full route)", 6), "dv_full": ("isa_bwd_dkdv_kernel dV (full route)", 4),
+               "dq_full": ("isa_bwd_dq_kernel (full route)", 6)}
+    rooflines = []
+    for key, (label, per) in kernels.items():
+        if st.get(key):
+            flops = per * w.d * pairs
+            tf = flops / (st[key] * 1e-3) / 1e12
+            rooflines.append({"kernel": label, "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops,
+                              "avg_launch_ms": round(st[key], 4)})
+    dominant = max(rooflines, key=lambda r: r["avg_launch_ms"]) if rooflines else None
+    return {"ms_per_call": round(ms, 4), "queries_per_s": round(w.B * w.Ns / (ms * 1e-3), 1),
+            "stage_ms": {k: round(v, 4) for k, v in st.items()}, "dominant": dominant, "rooflines": rooflines,
+            "data": "dO seeded N(0,1) in bf16; plan of the timed forward"}
 
 
 def main():
@@ -230,6 +284,10 @@ def main():
                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                        "note": "4 d FLOP per (query, kept block); the lo half of the split keys is not counted"})
 
+    backward = None
+    if not args.no_backward and w.dtype == "bf16":
+        backward = time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream)
+
     cpu = None
     if not args.no_cpu:
         log("cpu oracle on %s heads ..." % (args.cpu_heads or "all"))
@@ -259,6 +317,7 @@ def main():
         "roofline": roofline,
         "other_rooflines": others,
         "cpu_baseline": cpu,
+        "backward": backward,
     }
     print(json.dumps(out), flush=True)
 

@@ -194,14 +194,16 @@ isa_status isa_dense_forward(const isa_desc* desc, const void* Q, const void* K,
 
 typedef enum isa_bwd_stage {
   ISA_BWD_DELTA = 0,        /* D = rowsum(dO * O) of every source row */
-  ISA_BWD_DKV_POOLED = 1,   /* Taylor rows: per-split partial gradients of the kept pooled keys, values */
-  ISA_BWD_DKV_REDUCE = 2,   /* sums those partials in split order (zero without Taylor rows) */
-  ISA_BWD_DKV_FULL = 3,     /* full rows: dK, dV of every source and kept context row, plus the
-                               pooled share of its block */
-  ISA_BWD_ZERO_PRUNED = 4,  /* zeroes dK, dV rows of pruned context blocks */
-  ISA_BWD_DQ_FULL = 5,      /* full rows: dQ, or split partials when the key range is split */
-  ISA_BWD_DQ_MERGE = 6,     /* merges the dQ split partials (no-op unsplit) */
-  ISA_BWD_DQ_POOLED = 7     /* Taylor rows: dQ */
+  ISA_BWD_DK_POOLED = 1,    /* Taylor rows: per-split partial gradients of the kept pooled keys */
+  ISA_BWD_DV_POOLED = 2,    /* Taylor rows: per-split partial gradients of the kept pooled values */
+  ISA_BWD_DKV_REDUCE = 3,   /* sums those partials in split order (zero without Taylor rows) */
+  ISA_BWD_DK_FULL = 4,      /* full rows: dK of every source and kept context row, plus the pooled
+                               share of its block */
+  ISA_BWD_DV_FULL = 5,      /* the same for dV */
+  ISA_BWD_ZERO_PRUNED = 6,  /* zeroes dK, dV rows of pruned context blocks */
+  ISA_BWD_DQ_FULL = 7,      /* full rows: dQ, or split partials when the key range is split */
+  ISA_BWD_DQ_MERGE = 8,     /* merges the dQ split partials (no-op unsplit) */
+  ISA_BWD_DQ_POOLED = 9     /* Taylor rows: dQ */
 } isa_bwd_stage;
 
 /* Bytes of backward workspace isa_backward needs for *desc. */

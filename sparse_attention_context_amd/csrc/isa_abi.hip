@@ -170,9 +170,10 @@ extern "C" isa_status isa_run_backward_stage(const isa_desc* desc, int stage, co
                               dQ, dK, dV, &L, &W);
   if (st != ISA_OK) return st;
   const isa::BwdBufs B{Q, K, V, O, dO, dQ, dK, dV, (const char*)workspace, (char*)bwd_workspace};
-  static const isa::BwdWhat kWhat[] = {isa::BwdWhat::kDelta,    isa::BwdWhat::kDkvPooled, isa::BwdWhat::kDkvReduce,
-                                       isa::BwdWhat::kDkvFull,  isa::BwdWhat::kZeroPruned, isa::BwdWhat::kDqFull,
-                                       isa::BwdWhat::kDqMerge,  isa::BwdWhat::kDqPooled};
+  static const isa::BwdWhat kWhat[] = {isa::BwdWhat::kDelta,   isa::BwdWhat::kDkPooled,   isa::BwdWhat::kDvPooled,
+                                       isa::BwdWhat::kDkvReduce, isa::BwdWhat::kDkFull,   isa::BwdWhat::kDvFull,
+                                       isa::BwdWhat::kZeroPruned, isa::BwdWhat::kDqFull,  isa::BwdWhat::kDqMerge,
+                                       isa::BwdWhat::kDqPooled};
   ISA_RUN(isa::launch_backward(L, W, B, kWhat[stage], (hipStream_t)stream));
   return ISA_OK;
 }
@@ -188,9 +189,10 @@ extern "C" isa_status isa_backward(const isa_desc* desc, const void* Q, const vo
   const isa::BwdBufs B{Q, K, V, O, dO, dQ, dK, dV, (const char*)workspace, (char*)bwd_workspace};
   hipStream_t s = (hipStream_t)stream;
   // the pooled-key gradients must exist before the full dK/dV epilogue adds them
-  for (isa::BwdWhat w : {isa::BwdWhat::kDelta, isa::BwdWhat::kDkvPooled, isa::BwdWhat::kDkvReduce,
-                         isa::BwdWhat::kDkvFull, isa::BwdWhat::kZeroPruned, isa::BwdWhat::kDqFull,
-                         isa::BwdWhat::kDqMerge, isa::BwdWhat::kDqPooled})
+  for (isa::BwdWhat w : {isa::BwdWhat::kDelta, isa::BwdWhat::kDkPooled, isa::BwdWhat::kDvPooled,
+                         isa::BwdWhat::kDkvReduce, isa::BwdWhat::kDkFull, isa::BwdWhat::kDvFull,
+                         isa::BwdWhat::kZeroPruned, isa::BwdWhat::kDqFull, isa::BwdWhat::kDqMerge,
+                         isa::BwdWhat::kDqPooled})
     ISA_RUN(isa::launch_backward(L, W, B, w, s));
   return ISA_OK;
 }

@@ -16,10 +16,10 @@
 //
 // Kernels (in isa_backward order):
 //   delta       D for every source row
-//   dkdv pooled Taylor rows x kept pooled blocks: per-split partials of dkbar, dvbar
-//   dkv reduce  partials summed in split order
-//   dkdv full   full rows x kept tokens: dK, dV of every source and kept
-//               context row, plus the pooled share of its block
+//   dk, dv pooled  Taylor rows x kept pooled blocks: per-split partials of dkbar, dvbar
+//   dkv reduce     partials summed in split order
+//   dk, dv full    full rows x kept tokens: dK (dV) of every source and kept
+//                  context row, plus the pooled share of its block
 //   zero        dK, dV rows of pruned context blocks
 //   dq full     full rows x kept tokens (split-K like the forward) + merge
 //   dq pooled   Taylor rows x kept pooled blocks
@@ -30,7 +30,7 @@
 //   dq kernel   (rows fixed, keys streamed, 8 waves x 32 rows): S^T = K Q^T and
 //     dP^T = V dO^T put one query per lane, so ds^T is already the B operand
 //     of dQ^T += K^T ds^T, whose A operand K^T comes from LDS transpose reads.
-//   dkdv kernel (keys fixed, rows streamed, 4 waves x 32 keys): S = Q K^T and
+//   dk/dv kernels (keys fixed, rows streamed, 8 waves x 32 keys): S = Q K^T and
 //     dP = dO V^T put one key per lane, so p and ds are the B operands of
 //     dV^T += dO^T p and dK^T += Q^T ds; dO^T and Q^T come from transpose reads.
 // Each tile kept for both plain and transposed reads is stored twice in LDS:
@@ -327,27 +327,37 @@ __global__ __launch_bounds__(256) void isa_bwd_dq_merge_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves x 32 keys (one wave per SIMD), query rows staged 64 at a
-// time (two steps of 32), 2-stage LDS ring.  POOLED: keys are the kept
-// pooled blocks, rows the Taylor route, output per-split partials of
-// (dkbar, dvbar); else keys are the full route's tokens, rows the full route,
-// and the epilogue adds the pooled share and writes dK, dV.
+// dK or dV: 8 waves x 32 keys (2 waves per SIMD), query rows staged 64 at a
+// time (two steps of 32), 2-stage LDS ring.  Each lane owns one key column,
+// so a key past the range only disturbs its own (unwritten) column and needs
+// no mask.  The dK and dV halves are separate kernels: each then keeps one
+// accumulator set and fits two waves per SIMD in plain VGPRs, for the price
+// of computing the logits twice.
+//   DV: S = Q K^T, p = exp2(S sc [+ log2 n_j] - lse), dV^T += dO^T p
+//   DK: S, p as above, dP = dO V^T, ds = p (dP - D), dK^T += Q^T ds
+// POOLED: keys are the kept pooled blocks, rows the Taylor route, output
+// per-split partials of dkbar (dvbar); else keys are the full route's
+// tokens, rows the full route, and the epilogue adds the pooled share of
+// the key's block and writes dK (dV).
 
-template <int D, bool POOLED>
-__global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
+template <int D, bool POOLED, bool DK>
+__global__ __launch_bounds__(512) void isa_bwd_dkdv_kernel(BwdArgs a) {
   typedef bf16x8 Op;
-  constexpr int NW = 4, NTHR = NW * 64, BK = 32 * NW, BR = kBwdRows, ES = 2;
+  constexpr int NW = 8, NTHR = NW * 64, BK = 32 * NW, BR = kBwdRows, ES = 2;
   constexpr int KRB = D * ES, KCPR = KRB / 16;
   constexpr int KRS = KRB + 16, TRS = KRB + 64;
   constexpr int QT = BR * KRS, QTT = BR * TRS;
-  // stage: Q | dO | Q for transpose reads | dO for transpose reads | lse | D
-  constexpr int OFF_G = QT, OFF_QT = 2 * QT, OFF_GT = 2 * QT + QTT, OFF_L = 2 * QT + 2 * QTT;
+  // stage, DK: Q | dO | Q for transpose reads | lse | D;  DV: Q | dO for transpose reads | lse
+  constexpr int OFF_G = QT;
+  constexpr int OFF_T = DK ? 2 * QT : QT;
+  constexpr int OFF_L = OFF_T + QTT;
   constexpr int OFF_D = OFF_L + BR * 4;
-  constexpr int STAGE = OFF_D + BR * 4;
+  constexpr int STAGE = OFF_D + (DK ? BR * 4 : 0);
   constexpr int NSTAGE = 2;
   constexpr int NRC = BR * KCPR / NTHR;   // 16-byte chunks per thread per Q (and dO) tile
   constexpr int NT = D / 32;
   static_assert(NRC >= 1, "tile mapping");
+  static_assert(BK == kBwdKeys, "keys per workgroup");
 
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * STAGE];
 
@@ -365,13 +375,13 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
   bool kvalid;
   const char* Kg;
   const char* Vg;
-  float kbias;
+  float kbias = 0.f;
   if constexpr (POOLED) {
     kvalid = kv < a.mk;
     krow = min(kv, a.mk_pad - 1);
     Kg = (const char*)a.pkhi + ((long long)bh * a.mk_pad + krow) * KRB;
     Vg = (const char*)a.pv + ((long long)bh * a.mk_pad + krow) * KRB;
-    kbias = kvalid ? a.pbias[(long long)bh * a.mk_pad + krow] : -INFINITY;
+    kbias = a.pbias[(long long)bh * a.mk_pad + krow];
   } else {
     const int n_keys = a.Ns + (int)a.ctx_tok;
     if (kv < a.Ns) {
@@ -385,13 +395,12 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
     krow = kvalid ? krow : 0;
     Kg = (const char*)a.K + ((long long)bh * a.Nk + krow) * KRB;
     Vg = (const char*)a.V + ((long long)bh * a.Nk + krow) * KRB;
-    kbias = kvalid ? 0.f : -INFINITY;
   }
-  Op kB[D / 16], kBl[POOLED ? D / 16 : 1], vB[D / 16];
+  Op kB[D / 16], kBl[POOLED ? D / 16 : 1], vB[DK ? D / 16 : 1];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     kB[s] = *(const Op*)(Kg + (16 * s + 8 * h) * ES);
-    vB[s] = *(const Op*)(Vg + (16 * s + 8 * h) * ES);
+    if constexpr (DK) vB[s] = *(const Op*)(Vg + (16 * s + 8 * h) * ES);
     if constexpr (POOLED)
       kBl[s] = *(const Op*)((const char*)a.pklo + ((long long)bh * a.mk_pad + krow) * KRB + (16 * s + 8 * h) * ES);
   }
@@ -414,13 +423,13 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
       st.q[i] = *(const u32x4*)((const bf16_t*)a.Q + off);
       st.g[i] = *(const u32x4*)((const bf16_t*)a.dO + off);
     }
-    st.l = INFINITY;
+    st.l = INFINITY;  // rows off the route: p = 0
     st.d = 0.f;
     if (tid < BR) {
       const int r = route_row(qlist, a.q_k, a.b, a.nb_s, a.Ns, step * BR + tid);
       if (r >= 0) {
         st.l = a.lse[(long long)bh * a.Ns + r];
-        st.d = a.delta[(long long)bh * a.Ns + r];
+        if constexpr (DK) st.d = a.delta[(long long)bh * a.Ns + r];
       }
     }
     return st;
@@ -432,26 +441,27 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
       const int q = tid + NTHR * i;
       const int r = q / KCPR, c = q % KCPR;
       *(u32x4*)(S0 + r * KRS + c * 16) = st.q[i];
-      *(u32x4*)(S0 + OFF_G + r * KRS + c * 16) = st.g[i];
-      *(u32x4*)(S0 + OFF_QT + r * TRS + c * 16) = st.q[i];
-      *(u32x4*)(S0 + OFF_GT + r * TRS + c * 16) = st.g[i];
+      if constexpr (DK) {
+        *(u32x4*)(S0 + OFF_G + r * KRS + c * 16) = st.g[i];
+        *(u32x4*)(S0 + OFF_T + r * TRS + c * 16) = st.q[i];
+      } else {
+        *(u32x4*)(S0 + OFF_T + r * TRS + c * 16) = st.g[i];
+      }
     }
     if (tid < BR) {
       ((float*)(S0 + OFF_L))[tid] = st.l;
-      ((float*)(S0 + OFF_D))[tid] = st.d;
+      if constexpr (DK) ((float*)(S0 + OFF_D))[tid] = st.d;
     }
   };
 
   const int abase = l32 * KRS + 16 * h;
-  const int tbase = (4 * h + ((lane & 15) >> 2)) * TRS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * ES;
+  // transposed reads: rows (queries) 16 s + 4 h + m/4 (+8), d = 32 t + 16 (g%2) + 4 (m%4)
+  const int tbase = OFF_T + (4 * h + ((lane & 15) >> 2)) * TRS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * ES;
   const float sc = a.scale_log2;
 
-  f32x16 dk[NT], dv[NT];
+  f32x16 acc[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    dk[t] = f32x16{};
-    dv[t] = f32x16{};
-  }
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
 
   auto rows_step = [&](int stage) {
     const char* S0 = smem + stage * STAGE;
@@ -464,37 +474,34 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
         const Op qa = *(const Op*)(Qs + 32 * s);
         S = mma32(qa, kB[s], S);
         if constexpr (POOLED) S = mma32(qa, kBl[s], S);
-        P = mma32(*(const Op*)(Qs + OFF_G + 32 * s), vB[s], P);
+        if constexpr (DK) P = mma32(*(const Op*)(Qs + OFF_G + 32 * s), vB[s], P);
       }
       // rows of reg r: qs*32 + 8(r/4) + 4h + r%4
       const float* ls = (const float*)(S0 + OFF_L) + qs * 32 + 4 * h;
       const float* ds = (const float*)(S0 + OFF_D) + qs * 32 + 4 * h;
-      Op pB[2], sB[2];
+      Op oB[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l4 = *(const f32x4*)(ls + 8 * g);
-        const f32x4 d4 = *(const f32x4*)(ds + 8 * g);
+        f32x4 d4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (DK) d4 = *(const f32x4*)(ds + 8 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[r], sc, kbias) - l4[e]);
-          pB[r >> 3][r & 7] = (__bf16)p;
-          sB[r >> 3][r & 7] = (__bf16)(p * (P[r] - d4[e]));
+          const float p = POOLED ? __builtin_amdgcn_exp2f(fmaf(S[r], sc, kbias) - l4[e])
+                                 : __builtin_amdgcn_exp2f(fmaf(S[r], sc, -l4[e]));
+          oB[r >> 3][r & 7] = (__bf16)(DK ? p * (P[r] - d4[e]) : p);
         }
       }
-      const lds_char* Gt = (const lds_char*)S0 + OFF_GT + tbase + qs * 32 * TRS;
-      const lds_char* Qt = (const lds_char*)S0 + OFF_QT + tbase + qs * 32 * TRS;
+      const lds_char* Ts = (const lds_char*)S0 + tbase + qs * 32 * TRS;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const int o = 16 * s * TRS + 32 * t * ES;
-          const s16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Gt + o));
-          const s16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Gt + o + 8 * TRS));
-          dv[t] = mma32(__builtin_bit_cast(Op, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7)), pB[s], dv[t]);
-          const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Qt + o));
-          const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Qt + o + 8 * TRS));
-          dk[t] = mma32(__builtin_bit_cast(Op, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7)), sB[s], dk[t]);
+          const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ts + o));
+          const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ts + o + 8 * TRS));
+          acc[t] = mma32(__builtin_bit_cast(Op, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7)), oB[s], acc[t]);
         }
     }
   };
@@ -511,17 +518,16 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // ---- epilogue: lane holds key kv, d = 32 t + 8 g + 4 h + e
+  const float scale = DK ? a.inv_sqrt_d : 1.0f;
   if constexpr (POOLED) {
     if (kv >= a.mk_pad) return;
-    float* pk = a.part_dkv + (((long long)split * a.BH + bh) * a.mk_pad + kv) * 2 * D;
+    float* pk = a.part_dkv + (((long long)split * a.BH + bh) * a.mk_pad + kv) * 2 * D + (DK ? 0 : D);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * t + 8 * g + 4 * h;
-        *(f32x4*)(pk + d0) = f32x4{dk[t][4 * g], dk[t][4 * g + 1], dk[t][4 * g + 2], dk[t][4 * g + 3]} * a.inv_sqrt_d;
-        *(f32x4*)(pk + D + d0) = f32x4{dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]};
-      }
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(pk + 32 * t + 8 * g + 4 * h) =
+            f32x4{acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]} * scale;
   } else {
     if (!kvalid) return;
     // pooled key of the key's block and its count
@@ -535,24 +541,18 @@ __global__ __launch_bounds__(256) void isa_bwd_dkdv_kernel(BwdArgs a) {
       n = a.kept[(long long)bh * a.kc + u] == a.nb_c - 1 ? a.tail_c : a.b;
     }
     const float inv_n = 1.0f / (float)n;
-    const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D;
-    bf16_t* ok = (bf16_t*)a.dK + ((long long)bh * a.Nk + krow) * D;
-    bf16_t* ov = (bf16_t*)a.dV + ((long long)bh * a.Nk + krow) * D;
+    const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D + (DK ? 0 : D);
+    bf16_t* out = (bf16_t*)(DK ? a.dK : a.dV) + ((long long)bh * a.Nk + krow) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * t + 8 * g + 4 * h;
-        const f32x4 bk = *(const f32x4*)(pb + d0);
-        const f32x4 bv = *(const f32x4*)(pb + D + d0);
-        f32x4 vk, vv;
+        const f32x4 bb = *(const f32x4*)(pb + d0);
+        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vk[e] = fmaf(dk[t][4 * g + e], a.inv_sqrt_d, bk[e] * inv_n);
-          vv[e] = dv[t][4 * g + e] + bv[e] * inv_n;
-        }
-        *(u32x2*)(ok + d0) = u32x2{pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3])};
-        *(u32x2*)(ov + d0) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(acc[t][4 * g + e], scale, bb[e] * inv_n);
+        *(u32x2*)(out + d0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   }
 }
@@ -631,14 +631,18 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       hipLaunchKernelGGL((isa_bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
       break;
     }
-    case BwdWhat::kDkvPooled: {
+    case BwdWhat::kDkPooled:
+    case BwdWhat::kDvPooled: {
       if (L.taylor_rows == 0) return hipSuccess;
       a.q_list = taylq; a.q_k = L.nb_s - L.kq; a.n_rows = L.taylor_rows;
       a.nsplit = W.dkv_splits;
       a.key_tiles = W.dkv_key_tiles;
       const long long nwg = L.BH * a.key_tiles * a.nsplit;
       a.n_wg = (int)nwg;
-      hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, true>), dim3((unsigned)nwg), dim3(256), 0, s, a);
+      if (what == BwdWhat::kDkPooled)
+        hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, true, true>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, true, false>), dim3((unsigned)nwg), dim3(512), 0, s, a);
       break;
     }
     case BwdWhat::kDkvReduce: {
@@ -647,12 +651,16 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       hipLaunchKernelGGL((isa_bwd_dkv_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
       break;
     }
-    case BwdWhat::kDkvFull: {
+    case BwdWhat::kDkFull:
+    case BwdWhat::kDvFull: {
       a.q_list = fullq; a.q_k = L.kq; a.n_rows = L.full_rows;
       a.key_tiles = (int)((L.Ns + L.ctx_tok + kBwdKeys - 1) / kBwdKeys);
       const long long nwg = L.BH * a.key_tiles;
       a.n_wg = (int)nwg;
-      hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false>), dim3((unsigned)nwg), dim3(256), 0, s, a);
+      if (what == BwdWhat::kDkFull)
+        hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, true>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, false>), dim3((unsigned)nwg), dim3(512), 0, s, a);
       break;
     }
     case BwdWhat::kZeroPruned: {

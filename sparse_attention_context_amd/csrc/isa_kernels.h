@@ -69,7 +69,9 @@ struct BwdBufs {
   const char* ws;
   char* bws;
 };
-enum class BwdWhat { kDelta, kDkvPooled, kDkvReduce, kDkvFull, kZeroPruned, kDqFull, kDqMerge, kDqPooled };
+enum class BwdWhat {
+  kDelta, kDkPooled, kDvPooled, kDkvReduce, kDkFull, kDvFull, kZeroPruned, kDqFull, kDqMerge, kDqPooled
+};
 hipError_t launch_backward(const Layout& L, const BwdLayout& W, const BwdBufs& B, BwdWhat what, hipStream_t s);
 
 }  // namespace isa

@@ -49,9 +49,9 @@ struct Layout {
 // Validates *desc and fills *L.  Returns ISA_OK or the error of isa.h.
 isa_status make_layout(const isa_desc* desc, Layout* L);
 
-// Backward pass (bf16): keys per dK/dV workgroup (4 waves x 32) and query
+// Backward pass (bf16): keys per dK/dV workgroup (8 waves x 32) and query
 // rows staged per step.
-constexpr int kBwdKeys = 128;
+constexpr int kBwdKeys = 256;
 constexpr int kBwdRows = 64;
 
 struct BwdLayout {

@@ -32,7 +32,8 @@ STAGE = {name: i for i, name in enumerate(STAGES)}
 ATTENTION_STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "select_q", "full",
                     "full_merge"]
 # isa_bwd_stage values, in the order isa_backward runs them
-BWD_STAGES = ["delta", "dkv_pooled", "dkv_reduce", "dkv_full", "zero_pruned", "dq_full", "dq_merge", "dq_pooled"]
+BWD_STAGES = ["delta", "dk_pooled", "dv_pooled", "dkv_reduce", "dk_full", "dv_full", "zero_pruned", "dq_full",
+              "dq_merge", "dq_pooled"]
 BWD_STAGE = {name: i for i, name in enumerate(BWD_STAGES)}
 
 

@@ -143,7 +143,7 @@ def test_backward_validation_before_launch():
     assert L.isa_backward(D, p, p, p, p, p, ws, need, bws, bneed - 1, p, p, p, nul) == 3
     assert L.isa_backward(D, p, p, p, p, p, ws, need, ctypes.c_void_p(base + 16), bneed, p, p, p, nul) == 3
     assert L.isa_backward(D, p, p, p, p, p, ws, need, nul, bneed, p, p, p, nul) == 1
-    assert L.isa_run_backward_stage(D, 8, p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 1
+    assert L.isa_run_backward_stage(D, 10, p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 1
     assert L.isa_run_backward_stage(D, -1, p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 1
 
 

@@ -122,3 +122,35 @@ def test_backward_stage_sequence_equals_backward():
     torch.cuda.synchronize()
     for g, g2 in zip(grads, (dQ, dK, dV)):
         assert torch.equal(g, g2)
+
+
+def test_backward_video_dit_layer_full_heads():
+    """The benchmarked video-DiT layer (B1 H24 d128, 17550 + 17550 rows, b64,
+    rho .25, gamma .2): every head checked by properties that hold at any size
+    (the keys' gradients sum to zero, the values' to the sum of dO), and two
+    whole heads element by element against the oracle."""
+    from sparse_attention_context_amd.configs import BY_NAME
+    from sparse_attention_context_amd.synth import workload_inputs
+    w = BY_NAME["video_dit_layer"]
+    _report("backward video-DiT layer: inputs")
+    Q, K, V = workload_inputs(w)
+    dO = round_to_bf16(np.random.default_rng(123).standard_normal(Q.shape))
+    Qd, Kd, Vd, dOd = (device_tensor(t, "bf16") for t in (Q, K, V, dO))
+    O, ws = isa.attention(Qd, Kd, Vd, w.b, w.rho, w.gamma)
+    dQ, dK, dV, _ = isa.backward(Qd, Kd, Vd, O, dOd, ws, w.b, w.rho, w.gamma)
+    torch.cuda.synchronize()
+    _report("backward video-DiT layer: GPU done")
+    views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, w.gamma)
+    dKs = dK.float().sum(dim=2)
+    dVs = dV.float().sum(dim=2)
+    dOs = torch.from_numpy(dO).to(dK.device).float().sum(dim=2)
+    kn = dK.float().norm(dim=(2, 3))
+    assert float(((dKs.norm(dim=2)) / kn).max()) <= 5e-2
+    assert float(((dVs - dOs).norm(dim=2) / dOs.norm(dim=2)).max()) <= 2e-2
+    kept = views["kept_ctx"].cpu().numpy()
+    full = views["full_q"].cpu().numpy()
+    for h in (0, w.H - 1):
+        rQ, rK, rV = bwd.oracle_backward_head(Q[0, h], K[0, h], V[0, h], dO[0, h], w.b, kept[0, h], full[0, h])
+        for name, g, r in (("dQ", dQ, rQ), ("dK", dK, rK), ("dV", dV, rV)):
+            maxrel, rel = _assert_grad(name, g[0, h].float().cpu().numpy(), r)
+            _report("  head %d %s max/scale %.2e rel-L2 %.2e" % (h, name, maxrel, rel))
