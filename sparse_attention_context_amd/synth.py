@@ -51,3 +51,28 @@ def workload_inputs(w, heads=None):
     """Inputs of a Workload (configs.py).  heads=None draws all w.H heads."""
     H = w.H if heads is None else heads
     return make_inputs(w.B, H, w.d, w.Ns, w.Nc, w.seed, w.dtype, w.clips, w.sharp)
+
+
+def make_local_inputs(B, H, d, Ns, Nc, b, sigma, seed, sharp=0.2):
+    """Inputs with within-block locality, as tokens of neighbouring video
+    patches have: each block of b rows (cut per segment from its own start,
+    source then context) draws a centre c ~ N(0, I) for K and one for V, and
+    every row is sqrt(1 - sigma^2) c + sigma N(0, I).  sigma = 1 is i.i.d.
+    rows, sigma -> 0 identical rows in a block.  Q ~ N(0, I), and a fraction
+    `sharp` of each head's queries get q += 4 k_t for a random source key t.
+    fp64, no rounding (for the CPU diagnostics)."""
+    rng = np.random.default_rng(seed)
+    a = np.sqrt(max(0.0, 1.0 - sigma * sigma))
+    bounds = [(s, min(s + b, Ns)) for s in range(0, Ns, b)] + [(Ns + s, Ns + min(s + b, Nc)) for s in range(0, Nc, b)]
+    Q = rng.standard_normal((B, H, Ns, d))
+    K = sigma * rng.standard_normal((B, H, Ns + Nc, d))
+    V = sigma * rng.standard_normal((B, H, Ns + Nc, d))
+    nsh = int(sharp * Ns)
+    for x in range(B):
+        for h in range(H):
+            for s, e in bounds:
+                K[x, h, s:e] += a * rng.standard_normal(d)
+                V[x, h, s:e] += a * rng.standard_normal(d)
+            perm = rng.permutation(Ns)[:nsh]
+            Q[x, h, perm] += 4.0 * K[x, h, rng.integers(0, Ns, nsh)]
+    return Q, K, V
