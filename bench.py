@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing isa_backward")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--no-context", action="store_true", help="skip timing the context-token query rows")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter collection: one layer call, one dense call and a 1 GiB elementwise copy "
                          "(the copy calibrates byte counters), no timing")
@@ -284,6 +285,26 @@ def main():
                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                        "note": "4 d FLOP per (query, kept block); the lo half of the split keys is not counted"})
 
+    context = None
+    if not args.no_context and w.dtype == "bf16" and w.Nc > 0:
+        # context-token query rows (dense over all keys): the other half of the in-context layer
+        g = torch.Generator(device=dev).manual_seed(11)
+        Qc = torch.randn((w.B, w.H, w.Nc, w.d), generator=g, device=dev, dtype=torch.float32).to(Qd.dtype)
+        Oc = isa.context_forward(Qc, Kd, Vd)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.dense_steps):
+            isa.context_forward(Qc, Kd, Vd, out=Oc)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / args.dense_steps
+        cflops = 4 * w.d * w.Nc * (w.Ns + w.Nc) * w.B * w.H
+        context = {"ms": round(cms, 4), "tflops": round(cflops / (cms * 1e-3) / 1e12, 2),
+                   "layer_ms_with_isa_source_rows": round(cms + ms, 4),
+                   "note": "isa_context_forward: Nc context query rows, dense over all keys"}
+        log("isa_context_forward: %.3f ms/call" % cms)
+
     backward = None
     if not args.no_backward and w.dtype == "bf16":
         backward = time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream)
@@ -318,6 +339,7 @@ def main():
         "other_rooflines": others,
         "cpu_baseline": cpu,
         "backward": backward,
+        "context_rows": context,
     }
     print(json.dumps(out), flush=True)
 

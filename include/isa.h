@@ -222,6 +222,17 @@ isa_status isa_run_backward_stage(const isa_desc* desc, int stage, const void* Q
                                   void* bwd_workspace, size_t bwd_workspace_bytes, void* dQ, void* dK, void* dV,
                                   void* stream);
 
+/* Context-token query rows (bf16): the other half of the in-context layer.
+ * The pages define pruning and query grouping for the source (editing)
+ * queries only and say nothing of context queries; they are read here as
+ * ordinary attention: every context row attends over all Ns+Nc keys,
+ * softmax(q K^T / sqrt d) V.  Qc and Oc are [B,H,Nc,d] (the context rows of
+ * the concatenated queries), K and V [B,H,Ns+Nc,d].  Same flash kernel as
+ * isa_dense_forward; needs no workspace; Nc = 0 enqueues nothing; f32 gives
+ * ISA_ERR_UNSUPPORTED. */
+isa_status isa_context_forward(const isa_desc* desc, const void* Qc, const void* K, const void* V, void* Oc,
+                               void* stream);
+
 /* Device pointers to the plan held in a workspace (no device access). */
 isa_status isa_plan_views(const isa_desc* desc, void* workspace, size_t workspace_bytes,
                           isa_plan_view* out);

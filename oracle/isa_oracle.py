@@ -38,6 +38,9 @@ R7  Count kept from n at fraction f: ceil(f*n - 1e-9) clipped to [0, n].
 R8  Full route: exact softmax attention over every token of the kept key
     set (all source tokens and the tokens of the kept context blocks).
 R9  Only context blocks are pruned; selection is per (batch, head).
+N2  Context-token query rows (the other half of the in-context layer; the
+    abstract defines pruning and grouping for the source queries only):
+    ordinary attention of each context row over all Ns+Nc keys.
 
 Special cases of the global self-attention formula used as pins are the
 textbook form softmax(q k^T / sqrt(d_head)) v of "深度学习注意力机制：全局与
@@ -167,6 +170,12 @@ def taylor_attention_rows(q, kbar, vbar, n):
     d = q.shape[1]
     P = _weighted_softmax(q @ kbar.T / math.sqrt(d), n)
     return P @ vbar
+
+
+def context_rows_forward(Qc, Kh, Vh):
+    """Outputs of the context-token query rows (reading N2): every context row
+    attends over all Ns+Nc keys, the textbook softmax(q k^T / sqrt d) v."""
+    return full_attention_rows(_as64(Qc), _as64(Kh), _as64(Vh))
 
 
 def dense_attention(Qh, Kh, Vh):

@@ -111,6 +111,19 @@ extern "C" isa_status isa_dense_forward(const isa_desc* desc, const void* Q, con
   return ISA_OK;
 }
 
+extern "C" isa_status isa_context_forward(const isa_desc* desc, const void* Qc, const void* K, const void* V,
+                                          void* Oc, void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if (L.es != 2) return ISA_ERR_UNSUPPORTED;
+  if ((st = check_io(Qc, K, V, Oc, true)) != ISA_OK) return st;
+  if (L.Nc == 0) return ISA_OK;
+  const isa::Bufs B{Qc, K, V, Oc, nullptr};
+  ISA_RUN(isa::launch_flash(L, B, isa::FlashWhat::kContext, (hipStream_t)stream));
+  return ISA_OK;
+}
+
 extern "C" isa_status isa_run_stage(const isa_desc* desc, int stage, const void* Q, const void* K,
                                     const void* V, void* O, void* workspace, size_t workspace_bytes,
                                     void* stream) {

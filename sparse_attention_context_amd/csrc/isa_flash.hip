@@ -472,6 +472,10 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
   switch (what) {
     case FlashWhat::kDense:
       return flash_launch<D, FK_DENSE, FR_IDENTITY, true, false>(a, L.Ns, L.Nk, L.BH, s);
+    case FlashWhat::kContext:
+      // context query rows: Q and O hold Nc rows per head
+      a.Ns = L.Nc;
+      return flash_launch<D, FK_DENSE, FR_IDENTITY, true, false>(a, L.Nc, L.Nk, L.BH, s);
     case FlashWhat::kFull:
       a.q_list = (const int*)(B.ws + L.off_fullq);
       a.q_k = L.kq;

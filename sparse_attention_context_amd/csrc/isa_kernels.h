@@ -51,7 +51,7 @@ hipError_t launch_full_attention(const Layout& L, const Bufs& B, bool dense, hip
 hipError_t launch_full_merge(const Layout& L, const Bufs& B, hipStream_t s);
 
 // The bf16 flash kernel family (isa_flash.hip).
-enum class FlashWhat { kDense, kFull, kFullMerge, kSharpTaylor, kSharp, kTaylor };
+enum class FlashWhat { kDense, kContext, kFull, kFullMerge, kSharpTaylor, kSharp, kTaylor };
 hipError_t launch_flash(const Layout& L, const Bufs& B, FlashWhat what, hipStream_t s);
 
 // Backward pass (isa_flash_bwd.hip): inputs, forward output, its gradient,

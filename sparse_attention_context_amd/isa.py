@@ -22,7 +22,7 @@ STATUS = {0: "ISA_OK", 1: "ISA_ERR_INVALID_ARGUMENT", 2: "ISA_ERR_UNSUPPORTED", 
 
 EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "isa_attention",
            "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_backward_workspace_size", "isa_backward",
-           "isa_run_backward_stage", "isa_status_string", "isa_last_error"]
+           "isa_run_backward_stage", "isa_context_forward", "isa_status_string", "isa_last_error"]
 
 # isa_stage values (include/isa.h)
 STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
@@ -81,6 +81,7 @@ def lib():
         L.isa_dense_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp]
         L.isa_plan_views.argtypes = [P(Desc), vp, sz, P(PlanView)]
         L.isa_run_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
+        L.isa_context_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp]
         L.isa_backward_workspace_size.argtypes = [P(Desc), P(sz)]
         L.isa_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp]
         L.isa_run_backward_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp,
@@ -89,7 +90,7 @@ def lib():
         L.isa_status_string.restype = ctypes.c_char_p
         L.isa_last_error.argtypes = []
         L.isa_last_error.restype = ctypes.c_char_p
-        for fn in EXPORTS[:11]:
+        for fn in EXPORTS[:12]:
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,6 +185,22 @@ def dense_forward(Q, K, V, out=None, stream=None):
     O = torch.empty_like(Q) if out is None else out
     _check("isa_dense_forward", lib().isa_dense_forward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
                                                         _ptr(O), _stream(stream)))
+    return O
+
+
+def context_forward(Qc, K, V, out=None, stream=None):
+    """isa_context_forward: dense attention of the context query rows Qc
+    [B,H,Nc,d] over all keys K, V [B,H,Ns+Nc,d]; returns Oc."""
+    B, H, Nc, d = Qc.shape
+    if K.shape[:2] != (B, H) or K.shape[3] != d or K.shape[2] < Nc or V.shape != K.shape:
+        raise ValueError("Qc [B,H,Nc,d] needs K and V [B,H,Ns+Nc,d]")
+    for t in (Qc, K, V):
+        if t.dtype != Qc.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("Qc, K, V must be contiguous device tensors of one dtype")
+    desc = make_desc(B, H, K.shape[2] - Nc, Nc, d, 1, 1.0, 1.0, Qc.dtype)
+    O = torch.empty_like(Qc) if out is None else out
+    _check("isa_context_forward", lib().isa_context_forward(ctypes.byref(desc), _ptr(Qc), _ptr(K), _ptr(V), _ptr(O),
+                                                            _stream(stream)))
     return O
 
 

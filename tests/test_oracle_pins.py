@@ -362,3 +362,13 @@ def test_batched_entry_points():
             assert plan["full_q"][x, h].tolist() == ph["full_q"].tolist()
             Oh = orc.oracle_forward_head(Q[x, h], K[x, h], V[x, h], 4, ph["kept_ctx"], ph["full_q"])
             np.testing.assert_allclose(O[x, h], Oh, rtol=0, atol=1e-14)
+
+
+def test_context_rows_match_torch_sdpa():
+    # reading N2: context queries attend over every key, as plain attention does
+    rng = np.random.default_rng(17)
+    Qc, K, V = rng.standard_normal((23, 8)), rng.standard_normal((40, 8)), rng.standard_normal((40, 8))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(Qc)[None, None], torch.tensor(K)[None, None], torch.tensor(V)[None, None])[0, 0].numpy()
+    np.testing.assert_allclose(orc.context_rows_forward(Qc, K, V), ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(orc.context_rows_forward(Qc, K, V), brute_dense_head(Qc, K, V), rtol=0, atol=1e-12)
