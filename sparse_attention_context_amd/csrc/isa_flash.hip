@@ -395,10 +395,10 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 // Merges the split-K partials of each full-route query row, in split order.
 template <int D>
 __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
-  constexpr int TPR = D / 4;           // threads per row, 4 elements each
+  constexpr int TPR = D / 8;           // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;       // rows per workgroup
   const long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int e = (threadIdx.x % TPR) * 4;
+  const int e = (threadIdx.x % TPR) * 8;
   const long long rows_head = (long long)a.row_tiles * kFlashRows;
   const long long bh = gid / rows_head;
   const long long vrow = gid - bh * rows_head;
@@ -406,23 +406,38 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   const int qrow = route_row(a.q_list + bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
   if (qrow < 0) return;
   const long long prow = gid * a.nsplit;
+  constexpr int MAXS = kMaxSplits;
+  float2 ml[MAXS];
+  u32x4 po[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < a.nsplit) {
+      ml[s] = *(const float2*)(a.part_ml + (prow + s) * 2);
+      po[s] = *(const u32x4*)(a.part_o + (prow + s) * D + e);
+    }
+  }
   float mstar = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[(prow + s) * 2]);
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < a.nsplit) mstar = fmaxf(mstar, ml[s].x);
   // split s weighs in with its sum rescaled to the common max
-  float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float m = a.part_ml[(prow + s) * 2];
-    if (m == -INFINITY) continue;
-    const float wgt = __builtin_amdgcn_exp2f((m - mstar) * a.scale_log2) * a.part_ml[(prow + s) * 2 + 1];
+  float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s >= a.nsplit || ml[s].x == -INFINITY) continue;
+    const float wgt = __builtin_amdgcn_exp2f((ml[s].x - mstar) * a.scale_log2) * ml[s].y;
     l += wgt;
-    const u32x2 v = *(const u32x2*)(a.part_o + (prow + s) * D + e);
-    o0 += wgt * __uint_as_float(v.x << 16); o1 += wgt * __uint_as_float(v.x & 0xffff0000u);
-    o2 += wgt * __uint_as_float(v.y << 16); o3 += wgt * __uint_as_float(v.y & 0xffff0000u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] += wgt * __uint_as_float(po[s][k] << 16);
+      o[2 * k + 1] += wgt * __uint_as_float(po[s][k] & 0xffff0000u);
+    }
   }
   const float inv = 1.0f / l;
   if (a.lse && e == 0) a.lse[bh * a.Ns + qrow] = mstar * a.scale_log2 + __builtin_log2f(l);
   bf16_t* op = (bf16_t*)a.O + (bh * a.Ns + qrow) * D + e;
-  *(u32x2*)op = u32x2{pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv)};
+  *(u32x4*)op = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                      pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
 }
 
 // ---------------------------------------------------------------------------
@@ -490,7 +505,7 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
       a.n_rows = L.full_rows;
       a.row_tiles = (int)((L.full_rows + kFlashRows - 1) / kFlashRows);
       a.n_wg = (int)L.BH;
-      constexpr int RPB = 256 / (D / 4);
+      constexpr int RPB = 256 / (D / 8);
       const long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
       hipLaunchKernelGGL((isa_flash_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
       return hipGetLastError();

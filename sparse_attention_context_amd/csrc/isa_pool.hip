@@ -73,21 +73,29 @@ __global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int r = rg; r < rows; r += RG) {
-    const uint4 v = *(const uint4*)(base + (long long)r * D * ES);
-    if constexpr (ES == 2) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // BATCH rows per lane are loaded before any is added (bytes in flight);
+  // each lane still adds its rows in increasing order
+  constexpr int BATCH = 16;
+  for (int r0b = rg; r0b < rows; r0b += RG * BATCH) {
+    u32x4 v[BATCH];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += __uint_as_float(w[e] << 16);
-        acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+    for (int i = 0; i < BATCH; ++i) {
+      const int r = r0b + i * RG;
+      v[i] = r < rows ? *(const u32x4*)(base + (long long)r * D * ES) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      if (r0b + i * RG >= rows) break;
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(v[i][e] << 16);
+          acc[2 * e + 1] += __uint_as_float(v[i][e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[i][e]);
       }
-    } else {
-      acc[0] += __uint_as_float(v.x);
-      acc[1] += __uint_as_float(v.y);
-      acc[2] += __uint_as_float(v.z);
-      acc[3] += __uint_as_float(v.w);
     }
   }
 #pragma unroll

@@ -195,8 +195,17 @@ __global__ __launch_bounds__(256) void isa_select_ctx_kernel(SelArgs a) {
   double* sal = a.sal + bh * a.nb_c;
   const double* part = a.salp + bh * (long long)a.sal_tiles * a.nb_c;
   for (int c = tid; c < a.nb_c; c += 256) {
+    // the partials of 8 tiles are loaded before they are added (in tile order)
     double s = 0.0;
-    for (int t = 0; t < a.sal_tiles; ++t) s += part[(long long)t * a.nb_c + c];
+    int t = 0;
+    for (; t + 8 <= a.sal_tiles; t += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(long long)(t + u) * a.nb_c + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; t < a.sal_tiles; ++t) s += part[(long long)t * a.nb_c + c];
     sal[c] = s;
   }
   __syncthreads();
@@ -223,18 +232,18 @@ __global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
   double* sh = a.sh + bh * a.nb_s;
   const float* pk = a.peak + bh * a.Ns;
   // block means of the per-row peaks, rows added in order; the rows of a
-  // block are fetched 8 at a time with independent loads
+  // block are fetched 32 at a time with independent loads
   for (int i = tid; i < a.nb_s; i += 256) {
     const int r0 = i * a.b;
     const int n = min(a.b, a.Ns - r0);
     double s = 0.0;
     int r = 0;
-    for (; r + 8 <= n; r += 8) {
-      float v[8];
+    for (; r + 32 <= n; r += 32) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = pk[r0 + r + u];
+      for (int u = 0; u < 32; ++u) v[u] = pk[r0 + r + u];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += (double)v[u];
+      for (int u = 0; u < 32; ++u) s += (double)v[u];
     }
     for (; r < n; ++r) s += (double)pk[r0 + r];
     sh[i] = s / n;
