@@ -22,6 +22,7 @@ import time
 import numpy as np
 
 METRIC = "ISA attn queries/s + ms vs own dense FA, Ns=Nc=17550 H=24 d=128 bf16"
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -46,6 +47,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip timing isa_backward")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--no-context", action="store_true", help="skip timing the context-token query rows")
+    ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 variant of the full route")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter collection: one layer call, one dense call and a 1 GiB elementwise copy "
                          "(the copy calibrates byte counters), no timing")
@@ -111,6 +113,46 @@ def cpu_baseline(w, Q, K, V, gamma, heads):
     return {"value": w.B * w.Ns / per_layer, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
             "sample": "%d of %d heads of the same inputs (plan + forward, fp64 NumPy), %.1f s, scaled by H/%d"
                       % (heads, w.H, dt, heads)}
+
+
+def time_fp8(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
+    """isa_attention_fp8 (full route in e4m3 on MX-scaled MFMA) on the same
+    layer: whole call, its three full-route stages (HIP events), and the FP8
+    flash kernel against the fp8 MFMA peak at 4 d FLOP per (query, key)."""
+    import torch
+    from sparse_attention_context_amd import isa
+    O8, ws8, fws = isa.attention_fp8(Qd, Kd, Vd, w.b, w.rho, gamma)
+    torch.cuda.synchronize()
+
+    def fstep():
+        isa.attention_fp8(Qd, Kd, Vd, w.b, w.rho, gamma, out=O8, workspace=ws8, fp8_workspace=fws)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(isa.FP8_STAGES) + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        for i, name in enumerate(isa.FP8_STAGES):
+            evs[k][i].record(stream)
+            isa.run_fp8_stage(name, Qd, Kd, Vd, ws8, fws, w.b, w.rho, gamma, out=O8)
+        evs[k][-1].record(stream)
+    torch.cuda.synchronize()
+    st = {name: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) / args.steps
+          for i, name in enumerate(isa.FP8_STAGES)}
+    flops = full_route_flops(views, w, gamma)
+    tf = flops / (st["full"] * 1e-3) / 1e12 if st.get("full") else None
+    log("isa_attention_fp8: %.3f ms/call; full-route stages: %s" % (ms, ", ".join("%s %.3f" % kv for kv in st.items())))
+    return {"ms_per_call": round(ms, 4), "queries_per_s": round(w.B * w.Ns / (ms * 1e-3), 1),
+            "full_route_stage_ms": {k: round(v, 4) for k, v in st.items()},
+            "roofline": None if tf is None else {"kernel": "isa_flash_fp8_kernel", "bound": "mfma",
+                                                 "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                                                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+            "dtype": "e4m3 operands, fp32 accumulation (bf16 in and out)",
+            "error": "3.7-3.8 % rel-L2 of the full-route rows against exact attention (GPU tests)"}
 
 
 def time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
@@ -305,6 +347,10 @@ def main():
                    "note": "isa_context_forward: Nc context query rows, dense over all keys"}
         log("isa_context_forward: %.3f ms/call" % cms)
 
+    fp8 = None
+    if not args.no_fp8 and w.dtype == "bf16":
+        fp8 = time_fp8(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream)
+
     backward = None
     if not args.no_backward and w.dtype == "bf16":
         backward = time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream)
@@ -340,6 +386,7 @@ def main():
         "cpu_baseline": cpu,
         "backward": backward,
         "context_rows": context,
+        "fp8_variant": fp8,
     }
     print(json.dumps(out), flush=True)
 

@@ -233,6 +233,39 @@ isa_status isa_run_backward_stage(const isa_desc* desc, int stage, const void* Q
 isa_status isa_context_forward(const isa_desc* desc, const void* Qc, const void* K, const void* V, void* Oc,
                                void* stream);
 
+/* ---- FP8 variant of the full route (bf16 inputs) ------------------------
+ *
+ * The first page's list of attention speed-ups names 8-bit quantisation.
+ * isa_attention_fp8 runs the same layer as isa_attention, with the full
+ * route's operands in OCP e4m3 under power-of-two block scales (MX: a shared
+ * 2^e per 32 elements, e the smallest with max|x| / 2^e <= 448): Q per (query,
+ * 32 d), K per (key, 32 d), V per (d, 32 consecutive keys of the full
+ * route's key list: source rows, then the tokens of the kept context blocks),
+ * and the probabilities exp2(x - m) unscaled, with the reference maximum m a
+ * whole number in the exp2 domain.  Products on v_mfma_scale_f32_32x32x64_
+ * f8f6f4 with fp32 accumulation; everything else as isa_attention.  The
+ * error against exact attention is that of the rounding (a few percent of
+ * the output norm on N(0,1) data); the plan is identical to isa_attention's.
+ * fp8_workspace: isa_fp8_workspace_size() bytes, 256-byte aligned (the key
+ * list in e4m3 and its scales). */
+typedef enum isa_fp8_stage {
+  ISA_FP8_PACK = 0,         /* quantises the full route's key list into the FP8 workspace */
+  ISA_FP8_FULL = 1,         /* FP8 full attention: O rows, or split partials */
+  ISA_FP8_FULL_MERGE = 2    /* merges the split partials (as ISA_STAGE_FULL_MERGE) */
+} isa_fp8_stage;
+
+isa_status isa_fp8_workspace_size(const isa_desc* desc, size_t* bytes);
+
+isa_status isa_attention_fp8(const isa_desc* desc, const void* Q, const void* K, const void* V, void* O,
+                             void* workspace, size_t workspace_bytes, void* fp8_workspace,
+                             size_t fp8_workspace_bytes, void* stream);
+
+/* One stage of the FP8 full route (after the plan stages of isa_attention,
+ * POOL .. SELECT_Q, have run on the workspace); nothing when kq = 0. */
+isa_status isa_run_fp8_stage(const isa_desc* desc, int stage, const void* Q, const void* K, const void* V, void* O,
+                             void* workspace, size_t workspace_bytes, void* fp8_workspace,
+                             size_t fp8_workspace_bytes, void* stream);
+
 /* Device pointers to the plan held in a workspace (no device access). */
 isa_status isa_plan_views(const isa_desc* desc, void* workspace, size_t workspace_bytes,
                           isa_plan_view* out);

@@ -111,6 +111,59 @@ extern "C" isa_status isa_dense_forward(const isa_desc* desc, const void* Q, con
   return ISA_OK;
 }
 
+namespace {
+
+isa_status fp8_prepare(const isa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                       const void* ws, size_t ws_bytes, const void* fws, size_t fws_bytes, isa::Layout* L,
+                       isa::Fp8Layout* F) {
+  isa_status st = isa::make_layout(desc, L);
+  if (st != ISA_OK) return st;
+  if ((st = isa::make_fp8_layout(*L, F)) != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
+  if ((st = check_ws(*L, ws, ws_bytes)) != ISA_OK) return st;
+  if (!fws) return ISA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)fws % isa::kWsAlign) != 0 || fws_bytes < F->total) return ISA_ERR_WORKSPACE;
+  return ISA_OK;
+}
+
+}  // namespace
+
+extern "C" isa_status isa_attention_fp8(const isa_desc* desc, const void* Q, const void* K, const void* V, void* O,
+                                        void* workspace, size_t workspace_bytes, void* fp8_workspace,
+                                        size_t fp8_workspace_bytes, void* stream) {
+  isa::Layout L;
+  isa::Fp8Layout F;
+  isa_status st = fp8_prepare(desc, Q, K, V, O, workspace, workspace_bytes, fp8_workspace, fp8_workspace_bytes, &L, &F);
+  if (st != ISA_OK) return st;
+  const isa::Bufs B{Q, K, V, O, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = select_context(L, B, s)) != ISA_OK) return st;
+  ISA_RUN(isa::launch_pooled_attention(L, B, L.kq == L.nb_s ? 1 : 0, s));
+  ISA_RUN(isa::launch_select_q(L, B, s));
+  if (L.kq > 0) {
+    ISA_RUN(isa::launch_fp8(L, F, B, (char*)fp8_workspace, true, s));
+    ISA_RUN(isa::launch_fp8(L, F, B, (char*)fp8_workspace, false, s));
+    ISA_RUN(isa::launch_full_merge(L, B, s));
+  }
+  return ISA_OK;
+}
+
+extern "C" isa_status isa_run_fp8_stage(const isa_desc* desc, int stage, const void* Q, const void* K, const void* V,
+                                        void* O, void* workspace, size_t workspace_bytes, void* fp8_workspace,
+                                        size_t fp8_workspace_bytes, void* stream) {
+  if (stage < ISA_FP8_PACK || stage > ISA_FP8_FULL_MERGE) return ISA_ERR_INVALID_ARGUMENT;
+  isa::Layout L;
+  isa::Fp8Layout F;
+  isa_status st = fp8_prepare(desc, Q, K, V, O, workspace, workspace_bytes, fp8_workspace, fp8_workspace_bytes, &L, &F);
+  if (st != ISA_OK) return st;
+  if (L.kq == 0) return ISA_OK;
+  const isa::Bufs B{Q, K, V, O, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  if (stage == ISA_FP8_FULL_MERGE) ISA_RUN(isa::launch_full_merge(L, B, s));
+  else ISA_RUN(isa::launch_fp8(L, F, B, (char*)fp8_workspace, stage == ISA_FP8_PACK, s));
+  return ISA_OK;
+}
+
 extern "C" isa_status isa_context_forward(const isa_desc* desc, const void* Qc, const void* K, const void* V,
                                           void* Oc, void* stream) {
   isa::Layout L;

@@ -69,6 +69,11 @@ struct BwdBufs {
   const char* ws;
   char* bws;
 };
+// FP8 variant of the full route (isa_flash_fp8.hip): pack=true quantises the
+// key list into the FP8 workspace, pack=false runs the attention (O rows, or
+// split partials that the bf16 merge combines).
+hipError_t launch_fp8(const Layout& L, const Fp8Layout& F, const Bufs& B, char* fp8_ws, bool pack, hipStream_t s);
+
 enum class BwdWhat {
   kDelta, kDkPooled, kDvPooled, kDkvReduce, kDkFull, kDvFull, kZeroPruned, kDqFull, kDqMerge, kDqPooled
 };

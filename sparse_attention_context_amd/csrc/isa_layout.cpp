@@ -140,7 +140,39 @@ isa_status make_bwd_layout(const Layout& L, BwdLayout* B) {
   return ISA_OK;
 }
 
+isa_status make_fp8_layout(const Layout& L, Fp8Layout* F) {
+  if (!F) return ISA_ERR_INVALID_ARGUMENT;
+  if (L.es != 2) return ISA_ERR_UNSUPPORTED;
+  const size_t bh = (size_t)L.BH, d = (size_t)L.d;
+  const int64_t nk = (int64_t)L.Ns + L.ctx_tok;
+  F->ntile = (int)((nk + 63) / 64);
+  F->nkp = F->ntile * 64;
+  size_t o = 0;
+  auto take = [&](size_t* off, size_t bytes) {
+    *off = o;
+    o = align_up(o + (bytes ? bytes : 1));
+  };
+  take(&F->off_k8, bh * F->nkp * d);
+  take(&F->off_ks, bh * F->nkp * (d / 32));
+  take(&F->off_v8t, bh * F->ntile * d * 64);
+  take(&F->off_vs, bh * F->ntile * d * 2);
+  F->total = o;
+  return ISA_OK;
+}
+
 }  // namespace isa
+
+extern "C" isa_status isa_fp8_workspace_size(const isa_desc* desc, size_t* bytes) {
+  if (!bytes) return ISA_ERR_INVALID_ARGUMENT;
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  isa::Fp8Layout F;
+  st = isa::make_fp8_layout(L, &F);
+  if (st != ISA_OK) return st;
+  *bytes = F.total;
+  return ISA_OK;
+}
 
 extern "C" isa_status isa_backward_workspace_size(const isa_desc* desc, size_t* bytes) {
   if (!bytes) return ISA_ERR_INVALID_ARGUMENT;

@@ -68,6 +68,20 @@ struct BwdLayout {
 // Fills *B for the layout L (ISA_ERR_UNSUPPORTED unless bf16).
 isa_status make_bwd_layout(const Layout& L, BwdLayout* B);
 
+// FP8 variant of the full route: the key list in e4m3 with its scales.
+struct Fp8Layout {
+  int nkp;             // key list length rounded up to 64
+  int ntile;           // nkp / 64
+  size_t off_k8;       // [BH][nkp][d] e4m3
+  size_t off_ks;       // [BH][nkp][d/32] e8m0
+  size_t off_v8t;      // [BH][ntile][d][64] e4m3, transposed per tile
+  size_t off_vs;       // [BH][ntile][d][2] e8m0
+  size_t total;
+};
+
+// Fills *F for the layout L (ISA_ERR_UNSUPPORTED unless bf16).
+isa_status make_fp8_layout(const Layout& L, Fp8Layout* F);
+
 // Key-range splits for `units` workgroups of `ntiles` key tiles each, on
 // kCUs compute units running one workgroup each: the count that minimises
 // (rounds of workgroups) x (tiles per workgroup + fixed cost), 1 unless a

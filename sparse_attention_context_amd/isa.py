@@ -22,7 +22,8 @@ STATUS = {0: "ISA_OK", 1: "ISA_ERR_INVALID_ARGUMENT", 2: "ISA_ERR_UNSUPPORTED", 
 
 EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "isa_attention",
            "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_backward_workspace_size", "isa_backward",
-           "isa_run_backward_stage", "isa_context_forward", "isa_status_string", "isa_last_error"]
+           "isa_run_backward_stage", "isa_context_forward", "isa_fp8_workspace_size", "isa_attention_fp8",
+           "isa_run_fp8_stage", "isa_status_string", "isa_last_error"]
 
 # isa_stage values (include/isa.h)
 STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
@@ -82,6 +83,9 @@ def lib():
         L.isa_plan_views.argtypes = [P(Desc), vp, sz, P(PlanView)]
         L.isa_run_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
         L.isa_context_forward.argtypes = [P(Desc), vp, vp, vp, vp, vp]
+        L.isa_fp8_workspace_size.argtypes = [P(Desc), P(sz)]
+        L.isa_attention_fp8.argtypes = [P(Desc), vp, vp, vp, vp, vp, sz, vp, sz, vp]
+        L.isa_run_fp8_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, sz, vp, sz, vp]
         L.isa_backward_workspace_size.argtypes = [P(Desc), P(sz)]
         L.isa_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp]
         L.isa_run_backward_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp,
@@ -90,7 +94,7 @@ def lib():
         L.isa_status_string.restype = ctypes.c_char_p
         L.isa_last_error.argtypes = []
         L.isa_last_error.restype = ctypes.c_char_p
-        for fn in EXPORTS[:12]:
+        for fn in EXPORTS[:15]:
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -286,3 +290,34 @@ def run_backward_stage(stage, Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, 
            lib().isa_run_backward_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
                                         _ptr(workspace), workspace.numel(), _ptr(bwd_workspace),
                                         bwd_workspace.numel(), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)))
+
+
+FP8_STAGES = ["pack", "full", "full_merge"]
+
+
+def fp8_workspace_size(desc):
+    n = ctypes.c_size_t()
+    _check("isa_fp8_workspace_size", lib().isa_fp8_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def attention_fp8(Q, K, V, b, rho, gamma, out=None, workspace=None, fp8_workspace=None, stream=None):
+    """isa_attention_fp8: the layer with the full route in e4m3; returns (O, workspace, fp8_workspace)."""
+    _inputs(Q, K, V)
+    desc = desc_for(Q, K, b, rho, gamma)
+    ws = new_workspace(desc, Q.device) if workspace is None else workspace
+    fws = (torch.empty(fp8_workspace_size(desc), dtype=torch.uint8, device=Q.device)
+           if fp8_workspace is None else fp8_workspace)
+    O = torch.empty_like(Q) if out is None else out
+    _check("isa_attention_fp8", lib().isa_attention_fp8(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                                        _ptr(ws), ws.numel(), _ptr(fws), fws.numel(), _stream(stream)))
+    return O, ws, fws
+
+
+def run_fp8_stage(stage, Q, K, V, workspace, fp8_workspace, b, rho, gamma, out=None, stream=None):
+    """isa_run_fp8_stage: one kernel of the FP8 full route (name or isa_fp8_stage value)."""
+    desc = desc_for(Q, K, b, rho, gamma)
+    code = FP8_STAGES.index(stage) if isinstance(stage, str) else int(stage)
+    _check("isa_run_fp8_stage", lib().isa_run_fp8_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
+                                                        _ptr(workspace), workspace.numel(), _ptr(fp8_workspace),
+                                                        fp8_workspace.numel(), _stream(stream)))

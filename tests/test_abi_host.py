@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "isa.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(isa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(isa_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
