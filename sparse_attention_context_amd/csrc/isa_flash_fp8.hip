@@ -32,6 +32,14 @@
 namespace isa {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// two 16-byte LDS reads as one 8-register MFMA operand
+__device__ __forceinline__ v8i lds_operand(const char* lo, const char* hi) {
+  const v4i a = *(const v4i*)lo;
+  const v4i b = *(const v4i*)hi;
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // Smallest e with amax / 2^e <= 448, from the float's bits (exact); e8m0
 // range.  448 = 1.75 * 2^8: amax = 1.f * 2^(E-127) fits 2^(E-135) * 448 when
@@ -308,26 +316,32 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_kernel(Fp8Args a) {
       const char* kp = S0 + krow * KRS + 16 * h;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const u32x4 lo = *(const u32x4*)(kp + 64 * u);
-        const u32x4 hi = *(const u32x4*)(kp + 64 * u + 32);
-        const v8i ka = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const v8i ka = lds_operand(kp + 64 * u, kp + 64 * u + 32);
         const int kscale = (int)((ksw >> (8 * (2 * u + h))) & 0xffu);
         S[half] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qB[u], S[half], 0, 0, 0, kscale, 0, qS[u]);
       }
     }
     // softmax in the exp2 domain; keys past the range (a short kept tail) are masked
+    // raw logits (the scale sc > 0 is applied in the exp2 argument)
     float x[32];
     float mx = -INFINITY;
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = half * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float v = t0 + key < n_valid ? S[half][r] * sc : -INFINITY;
-        x[16 * half + r] = v;
-        mx = fmaxf(mx, v);
+        x[16 * half + r] = S[half][r];
+        mx = fmaxf(mx, x[16 * half + r]);
       }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    if (t0 + BN > n_valid) {  // only the last tile of the range can be partial
+      mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int key = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * h + (i & 3);
+        if (t0 + key >= n_valid) x[i] = -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      }
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * sc;
     const bool move = mx > m_ref + 8.0f;
     if (__ballot(move)) {
       const float m_new = move ? ceilf(mx) : m_ref;
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_kernel(Fp8Args a) {
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(x[4 * g + e] - m_ref);
+        p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + e], sc, -m_ref));
         psum += p[e];
       }
       pB[g] = (int)pack4_fp8(p[0], p[1], p[2], p[3]);
@@ -356,9 +370,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_kernel(Fp8Args a) {
     for (int t = 0; t < NT; ++t) {
       const int d = 32 * t + l32;
       const char* vp = S0 + OFF_V + d * VRS + 32 * h;
-      const u32x4 lo = *(const u32x4*)vp;
-      const u32x4 hi = *(const u32x4*)(vp + 16);
-      const v8i va = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const v8i va = lds_operand(vp, vp + 16);
       const int vscale = (int)((vsw[d] >> (8 * h)) & 0xffu);
       acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pB, acc[t], 0, 0, 0, vscale, 0, 127);
     }
