@@ -16,6 +16,10 @@
 //    softmax, exp2(max - ref) / l, is the query sharpness.  Pooled keys come
 //    as bf16 hi + lo parts (two MFMAs) so the logits carry ~2^-17.
 //
+// Two kernels: isa_flash_kernel (below) runs the pooled pass and d = 64;
+// isa_flash_pp_kernel runs the token modes at d = 128 with the same
+// arithmetic on a ping-pong wave schedule and direct global->LDS loads.
+//
 // Workgroup: NW waves, 32 query rows each; key tiles of 64.  Each wave
 // computes S^T = K Q^T with 32x32x16 MFMAs (lane = one query, 32 keys), the
 // online softmax in fp32 on exp2, and O^T += V^T P^T: P^T is already the
@@ -42,6 +46,8 @@
 // mean of the splits in split order (deterministic).
 #include "isa_device.h"
 #include "isa_kernels.h"
+
+#include <type_traits>
 
 namespace isa {
 
@@ -392,6 +398,390 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   }
 }
 
+// Ping-pong schedule for the token modes (full route, dense, context rows),
+// d = 128.
+//
+// Two groups of four waves (waves w and w+4 share a SIMD) run the same tile
+// loop one phase apart, so that one group's MFMA cluster overlaps the other
+// group's softmax.  Each tile j takes two barrier-separated phases:
+//   X_j  acc += V(j-1)^T P(j-1)^T, then S(j) = K(j) Q^T   (MFMA + LDS reads)
+//   Y_j  direct global->LDS loads of K(j+3) and V(j+2) (and, gathering,
+//        of the row-table entries of tile j+6); softmax of S(j) -> P(j)
+// Group 0 runs X_j in phase 2j and Y_j in 2j+1, group 1 one phase later.
+// Each group loads its own half (32 rows) of every K and V tile with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base
+// + 16 x lane), so no tile passes through registers.  K and V rings have four
+// stages: a stage is refilled (issue in phase 2t-5 or later) only after the
+// last read of its previous tile (phase 2t-7 for K, 2t-5 for V), and each
+// wave waits for its loads of Y_{j-1} before the barrier that closes Y_j, so
+// every tile is in LDS two phases before its first read.
+//
+// LDS rows are 256 bytes, unpadded; the 16-byte chunk c of row r is stored
+// at chunk c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3).  Sixteen
+// consecutive rows at one chunk (the K operand reads) and four consecutive
+// rows at four consecutive chunks (the V^T transpose reads) then fall on
+// distinct banks.  Operand addresses are per-lane offsets computed once.
+// Numerics are those of isa_flash_kernel: the same per-row reference max,
+// sums and bf16 roundings.
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Four direct loads of 16 bytes per lane: rows of K at kbase + kv0/kv1 into
+// LDS at lk0/lk1 + 16 x lane, rows of V at vbase + vv0/vv1 into lv0/lv1.  One
+// asm block, so every offset (and the row-table values behind it) is ready
+// before the first load is issued; the loads are waited for by count.
+__device__ __forceinline__ void dma16x4(unsigned lk0, unsigned lk1, const void* kbase, unsigned kv0, unsigned kv1,
+                                        unsigned lv0, unsigned lv1, const void* vbase, unsigned vv0, unsigned vv1) {
+  unsigned saved;  // m0 is restored, so the asm leaves no register changed behind the compiler's back
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %9\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %9\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lk0), "s"(lk1), "s"(lv0), "s"(lv1), "v"(kv0), "v"(kv1), "v"(vv0), "v"(vv1), "s"(kbase), "s"(vbase)
+      : "memory");
+}
+
+// 4 bytes per lane from base + voff into LDS at lds + 4 x lane.
+__device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned voff) {
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
+template <int KM, int RM>
+__global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
+  typedef bf16x8 Op;
+  constexpr int D = 128;
+  constexpr bool GATHER = KM == FK_GATHER;
+  static_assert(KM != FK_POOLED, "token modes only");
+  constexpr int BN = 64, BM = 256, NST = 4;
+  constexpr int RB = D * 2;                      // row bytes (global and LDS)
+  constexpr int TB = BN * RB;                    // tile bytes
+  constexpr int NT = D / 32;
+  static_assert(BM == kFlashRows, "tile mapping");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TB];   // K ring, then V ring
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int lid = xcd_remap(blockIdx.x, a.n_wg);
+  const int split = lid % a.nsplit;
+  const int rest = lid / a.nsplit;
+  const int bh = rest / a.row_tiles;
+  const int rt = rest - bh * a.row_tiles;
+
+  const long long vrow = (long long)rt * BM + w * 32 + l32;
+  int qrow;
+  if constexpr (RM == FR_TABLE) qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
+  else qrow = vrow < a.Ns ? (int)vrow : -1;
+  Op qB[D / 16];
+  {
+    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
+  }
+
+  int n_keys, n_valid;
+  if constexpr (GATHER) {
+    n_keys = a.Ns + (int)a.ctx_tok;
+    const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
+    n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
+  } else {
+    n_keys = n_valid = a.Nk;
+  }
+  const int ntiles = (n_keys + BN - 1) / BN;
+  const int t_begin = split * a.tiles_per_split;
+  const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
+
+  const char* Kg = (const char*)a.K + (long long)bh * a.Nk * RB;
+  const char* Vg = (const char*)a.V + (long long)bh * a.Nk * RB;
+  const int* crow = GATHER ? a.ctx_rows + (long long)bh * a.ctx_tok : nullptr;
+  const int ctx_last = (int)a.ctx_tok - 1;
+  // (without context rows the table read goes to the first K word: every
+  // row is then a source row and the value is never used)
+  const int* tab = ctx_last >= 0 ? crow : (const int*)Kg;
+  const int tab_last = max(ctx_last, 0);
+
+  // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
+  // tile, one 16-byte chunk each: physical chunk lane%16 of the row, which
+  // holds logical chunk (lane%16) ^ f(row).
+  const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
+  struct Rows { int r[2]; };
+  // Gather: the row-table entries of the wave's 8 rows of tile t come to a
+  // per-wave LDS ring (slot t % 4) by a direct load in step t-6, entry
+  // 2q + i holding row 32*grp + 8*wg + q + 4i, are read into registers in
+  // step t-4 and used in steps t-3 (K) and t-2 (V); so no load result is
+  // waited for inside the tile loop.
+  __shared__ __attribute__((aligned(16))) int stab[GATHER ? 8 : 1][4][64];
+  // (slots are indexed by the tile's position j in this workgroup's range)
+  auto fetch_rows = [&](int j, int tile) {
+    if constexpr (GATHER) {
+      const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
+      const int idx = min(max(tile * BN + 32 * grp + 8 * wg + k - a.Ns, 0), tab_last);
+      dma4(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[w][j & 3][0]), tab, (unsigned)idx * 4u);
+    }
+  };
+  auto rows_of = [&](int j) -> Rows {
+    Rows rows = {};
+    if constexpr (GATHER) {
+      const int2 v = *(const int2*)&stab[w][j & 3][2 * (lane >> 4)];
+      rows.r[0] = v.x;
+      rows.r[1] = v.y;
+    }
+    return rows;
+  };
+  const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
+  const unsigned lds_v = lds_k + NST * TB;
+  auto src_off = [&](Rows rows, int tile, int i) -> unsigned {
+    const int lr = lrow0 + 4 * i;
+    const int t = tile * BN + lr;
+    int r;
+    if constexpr (GATHER) r = t < a.Ns ? t : (t < n_valid && rows.r[i] >= 0 ? rows.r[i] : 0);
+    else r = t < n_valid ? t : 0;
+    return (unsigned)r * RB + (unsigned)(((lane & 15) ^ lds_swz(lr)) * 16);
+  };
+  // LDS base of this wave's i-th load into a ring stage
+  auto dst = [&](unsigned ring, int stage, int i) -> unsigned {
+    return __builtin_amdgcn_readfirstlane(ring + stage * TB + (32 * grp + 8 * wg + 4 * i) * RB);
+  };
+  auto issue = [&](int sk, Rows rk, int tk, int sv, Rows rv, int tv) {
+    dma16x4(dst(lds_k, sk, 0), dst(lds_k, sk, 1), Kg, src_off(rk, tk, 0), src_off(rk, tk, 1),
+            dst(lds_v, sv, 0), dst(lds_v, sv, 1), Vg, src_off(rv, tv, 0), src_off(rv, tv, 1));
+  };
+
+  // operand offsets: K row 32*ti + l32, logical chunk 2s + h; V^T transpose
+  // reads at key rows 16s + 4h + m/4 (+8), d = 32t + 16(g%2) + 4(m%4), with
+  // g = lane/16, m = lane%16 (see isa_flash_kernel)
+  int koff[8], voff[NT][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int m = lane & 15;
+      const int kr = 4 * h + (m >> 2) + 8 * hi;
+      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+      voff[t][hi] = NST * TB + kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
+    }
+
+  struct STile { f32x16 t[2]; };
+  struct PTile { Op p[4]; };
+  auto qk = [&](int stage) -> STile {
+    const lds_char* Ks = (const lds_char*)smem + stage * TB;
+    // operands are read one group (four MFMAs) ahead of their use: the
+    // reads of group g+1 are issued before the MFMAs of group g
+    STile S;
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+    Op kb[2][4];
+    auto rd = [&](int g, Op* b) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = *(const Op*)(Ks + koff[2 * g + (e & 1)] + 32 * (e >> 1) * RB);
+    };
+    rd(0, kb[0]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g < 3) rd(g + 1, kb[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S.t[e >> 1] = mma32(kb[g & 1][e], qB[2 * g + (e & 1)], S.t[e >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return S;
+  };
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+  const float thresh = 8.0f / sc;
+
+  auto pv = [&](int stage, const PTile& P) {
+    const lds_char* Vs = (const lds_char*)smem + stage * TB;
+    // d tile t: four key steps of two transpose reads each; the reads of
+    // tile t+1 are issued before the MFMAs of tile t
+    s16x4 vb[2][8];
+    auto rd = [&](int t, s16x4* b) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        b[2 * s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * s * RB));
+        b[2 * s + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * s * RB));
+      }
+    };
+    rd(0, vb[0]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t + 1 < NT) rd(t + 1, vb[(t + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const s16x8 v = __builtin_shufflevector(vb[t & 1][2 * s], vb[t & 1][2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[t] = mma32(__builtin_bit_cast(Op, v), P.p[s], acc[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto exp_tile = [&](const f32x16* S, PTile& P) -> float {
+    const float msub = m_ref * sc;
+    float psum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, -msub));
+        psum += p;
+        P.p[s][jj] = (__bf16)p;
+      }
+    }
+    return psum;
+  };
+  // Probabilities are first taken against the current reference max.  Any
+  // probability above 2^8 (the point where isa_flash_kernel moves a row's
+  // reference) makes the lane's tile sum exceed 2^7, so only then is the
+  // row maximum formed and the move rule applied, and the tile recomputed:
+  // the same references, sums and roundings as isa_flash_kernel.
+  auto softmax = [&](int j, STile St) -> PTile {
+    f32x16* S = St.t;
+    const int t0 = (t_begin + j) * BN;
+    if (t0 + BN > n_valid) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t0 + 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) S[ti][r] = -INFINITY;
+    }
+    PTile P;
+    float psum = exp_tile(S, P);
+    if (__ballot(!(psum <= 128.f))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const bool move = mx > m_ref + thresh;
+      if (__ballot(move)) {
+        const float m_new = move ? mx : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sc);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        m_ref = m_new;
+        psum = exp_tile(S, P);
+      }
+    }
+    l_run += psum;
+    return P;
+  };
+
+  // Barrier without a memory fence: the direct loads are waited for by
+  // count (s_waitcnt vmcnt), every LDS read has been consumed by an MFMA
+  // before the barrier, and the empty asm keeps the compiler from moving
+  // memory accesses across it.
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- tile loop, unrolled by four so that every ring stage is a
+  // compile-time choice.  Positions past the last tile are clamped to it.
+  auto cl = [&](int j) { return min(j, nt - 1); };
+  auto tl = [&](int j) { return t_begin + cl(j); };
+  if (nt > 0) {
+    Rows rk, rv;   // rows of tiles j+3 (K) and j+2 (V) entering step j
+    {
+      fetch_rows(cl(0), tl(0));
+      fetch_rows(cl(1), tl(1));
+      fetch_rows(cl(2), tl(2));
+      fetch_rows(cl(3), tl(3));
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+      const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1));
+      rv = rows_of(cl(2));
+      rk = rows_of(cl(3));
+      issue(0, r0, tl(0), 0, r0, tl(0));
+      issue(1, r1, tl(1), 1, r1, tl(1));
+      // K(2) (V(2) is loaded again by the first step, into the same stage)
+      issue(2, rv, tl(2), 2, rv, tl(2));
+      fetch_rows(cl(4), tl(4));
+      fetch_rows(cl(5), tl(5));
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the prologue tiles and row entries
+    }
+    phase_barrier();
+    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+    STile S = {};
+    PTile P = {};
+    // Loads past the last tile re-read it (clamped) into the stage that the
+    // schedule frees for tile j+3 / j+2 and are never read, so every step
+    // issues the same loads and waits by the same count.
+    auto step = [&](int j) {
+      const int Z = j & 3;
+      // X_j, at raised wave priority: the MFMA group's instructions issue
+      // ahead of the softmax group's on the shared SIMD
+      __builtin_amdgcn_s_setprio(3);
+      if (j >= 1) pv((Z + 3) & 3, P);
+      if (j < nt) S = qk(Z);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+      // Y_j
+      issue((Z + 3) & 3, rk, tl(j + 3), (Z + 2) & 3, rv, tl(j + 2));
+      const Rows rn = rows_of(cl(j + 4));   // used one step later: its LDS latency is hidden
+      fetch_rows(cl(j + 6), tl(j + 6));
+      if (j < nt) P = softmax(j, S);
+      rv = rk;
+      rk = rn;
+      // the loads of Y_{j-1} have landed before the barrier that closes Y_j
+      if constexpr (GATHER) __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0f74);                    // vmcnt(4)
+      phase_barrier();
+    };
+    for (int j = 0; j <= nt; ++j) step(j);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+  }
+
+  // ---- epilogue (as isa_flash_kernel's)
+  const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+  if (a.nsplit == 1) {
+    if (qrow >= 0) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * t + 8 * g + 4 * h;
+          *(u32x2*)(op + d0) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                                     pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+        }
+      if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref * sc + __builtin_log2f(l_tot);
+    }
+  } else {
+    const long long prow = ((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split;
+    bf16_t* po = a.part_o + prow * D;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(u32x2*)(po + 32 * t + 8 * g + 4 * h) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                                                       pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+    if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref, l_tot};
+  }
+}
+
 // Merges the split-K partials of each full-route query row, in split order.
 template <int D>
 __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
@@ -476,6 +866,10 @@ static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, lo
   const long long nwg = (long long)a.row_tiles * BH * a.nsplit;
   if (nwg == 0) return hipSuccess;
   a.n_wg = (int)nwg;
+  if constexpr (D == 128 && KM != FK_POOLED && WO && !WP && kFlashWaves == 8) {
+    hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((isa_flash_kernel<D, KM, RM, kFlashWaves, WO, WP>), dim3((unsigned)nwg),
                      dim3(kFlashWaves * 64), 0, s, a);
   return hipGetLastError();
