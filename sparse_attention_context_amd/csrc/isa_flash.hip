@@ -49,6 +49,10 @@
 
 #include <type_traits>
 
+#ifndef ISA_PP_LOOKAHEAD
+#define ISA_PP_LOOKAHEAD 5
+#endif
+
 namespace isa {
 
 enum { FK_DENSE = 0, FK_GATHER = 1, FK_POOLED = 2 };
@@ -453,6 +457,18 @@ __device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned vo
                : "memory");
 }
 
+// Issue order of the fused X phase (32 MFMAs: 16 P.V with two operand reads
+// each, then 16 K.Q^T with one): the reads of MFMAs 0..LA-1, then each MFMA
+// followed by the reads of the MFMA LA places later.
+template <int LA, int M = 0>
+__device__ __forceinline__ void pp_issue_order() {
+  constexpr int kMFMA = 0x8, kDSR = 0x100;
+  if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kDSR, LA <= 16 ? 2 * LA : 16 + LA, 0);
+  __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+  if constexpr (M + LA < 32) __builtin_amdgcn_sched_group_barrier(kDSR, M + LA < 16 ? 2 : 1, 0);
+  if constexpr (M + 1 < 32) pp_issue_order<LA, M + 1>();
+}
+
 template <int KM, int RM>
 __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   typedef bf16x8 Op;
@@ -573,30 +589,6 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
 
   struct STile { f32x16 t[2]; };
   struct PTile { Op p[4]; };
-  auto qk = [&](int stage) -> STile {
-    const lds_char* Ks = (const lds_char*)smem + stage * TB;
-    // operands are read one group (four MFMAs) ahead of their use: the
-    // reads of group g+1 are issued before the MFMAs of group g
-    STile S;
-    S.t[0] = f32x16{};
-    S.t[1] = f32x16{};
-    Op kb[2][4];
-    auto rd = [&](int g, Op* b) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = *(const Op*)(Ks + koff[2 * g + (e & 1)] + 32 * (e >> 1) * RB);
-    };
-    rd(0, kb[0]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g < 3) rd(g + 1, kb[(g + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S.t[e >> 1] = mma32(kb[g & 1][e], qB[2 * g + (e & 1)], S.t[e >> 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return S;
-  };
-
   f32x16 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
@@ -604,30 +596,34 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   const float sc = a.scale_log2;
   const float thresh = 8.0f / sc;
 
-  auto pv = [&](int stage, const PTile& P) {
-    const lds_char* Vs = (const lds_char*)smem + stage * TB;
-    // d tile t: four key steps of two transpose reads each; the reads of
-    // tile t+1 are issued before the MFMAs of tile t
-    s16x4 vb[2][8];
-    auto rd = [&](int t, s16x4* b) {
+  // X phase with both products as one pipeline of 32 MFMAs (16 of P.V, then
+  // 16 of K.Q^T); the operand reads of each MFMA are issued LA MFMAs ahead.
+  auto pv_qk = [&](int vstage, const PTile& P, int kstage) -> STile {
+    constexpr int LA = ISA_PP_LOOKAHEAD;
+    const lds_char* Vs = (const lds_char*)smem + vstage * TB;
+    const lds_char* Ks = (const lds_char*)smem + kstage * TB;
+    Op opv[16], opk[16];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        b[2 * s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * s * RB));
-        b[2 * s + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * s * RB));
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * q * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * q * RB));
+        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    };
-    rd(0, vb[0]);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t + 1 < NT) rd(t + 1, vb[(t + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const s16x8 v = __builtin_shufflevector(vb[t & 1][2 * s], vb[t & 1][2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[t] = mma32(__builtin_bit_cast(Op, v), P.p[s], acc[t]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int ti = 0; ti < 2; ++ti) opk[2 * q + ti] = *(const Op*)(Ks + koff[q] + 32 * ti * RB);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], P.p[m & 3], acc[m >> 2]);
+    STile S;
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) S.t[m & 1] = mma32(opk[m], qB[m >> 1], S.t[m & 1]);
+    pp_issue_order<LA>();
+    return S;
   };
   auto exp_tile = [&](const f32x16* S, PTile& P) -> float {
     const float msub = m_ref * sc;
@@ -716,7 +712,11 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
       issue(2, rv, tl(2), 2, rv, tl(2));
       fetch_rows(cl(4), tl(4));
       fetch_rows(cl(5), tl(5));
-      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the prologue tiles and row entries
+      // V stage 3 is first loaded in step 1; step 0 reads it as zeros
+      u32x4* vz = (u32x4*)(smem + NST * TB + 3 * TB);
+#pragma unroll
+      for (int q = 0; q < TB / (16 * 512); ++q) vz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): prologue loads and the zero fill
     }
     phase_barrier();
     if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
@@ -730,8 +730,9 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
       // X_j, at raised wave priority: the MFMA group's instructions issue
       // ahead of the softmax group's on the shared SIMD
       __builtin_amdgcn_s_setprio(3);
-      if (j >= 1) pv((Z + 3) & 3, P);
-      if (j < nt) S = qk(Z);
+      // (step 0 multiplies the zeroed V stage 3 by P = 0, step nt computes
+      // an S that is never used: every step runs the same pipeline)
+      S = pv_qk((Z + 3) & 3, P, Z);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
       phase_barrier();
