@@ -9,7 +9,7 @@
 //     P_ij  = n_j exp(qbar_i . kbar_j / sqrt d) / sum_j' n_j' exp(...)
 //     sal_c = sum_i P_{i, nb_s + c}.
 //
-// One workgroup (4 waves) per 32 pooled queries of one head.  Logits
+// One workgroup (8 waves) per 32 pooled queries of one head.  Logits
 // L^T = Kbar Qbar^T come from 32x32x16 bf16 MFMAs on a two-part split of the
 // fp32 pooled vectors (hi = bf16(x), lo = bf16(x - hi); hi*hi + hi*lo +
 // lo*hi, about 2^-17 relative per product).  Pass 1: each lane keeps the
@@ -52,10 +52,11 @@ __device__ __forceinline__ void split8(const float* src, bf16x8& hi, bf16x8& lo)
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void isa_saliency_kernel(SalArgs a) {
+__global__ __launch_bounds__(512) void isa_saliency_kernel(SalArgs a) {
   constexpr int R = kSalRows;  // 32 pooled queries
-  __shared__ double red_m[4][R], red_s[4][R];
-  __shared__ double pt[4][32][R + 1];  // per wave: [key][query] probabilities
+  constexpr int NW = 8;
+  __shared__ double red_m[NW][R], red_s[NW][R];
+  __shared__ double pt[NW][32][R + 1];  // per wave: [key][query] probabilities
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int tile = blockIdx.x;
@@ -80,23 +81,25 @@ __global__ __launch_bounds__(256) void isa_saliency_kernel(SalArgs a) {
   auto logits = [&](int k0) -> f32x16 {
     const int key = min(k0 + l32, a.M - 1);
     const float* kp = kb + (long long)key * D + 8 * h;
-    f32x16 S = f32x16{};
+    // two accumulators (even and odd d steps) halve the MFMA dependency chain
+    f32x16 S0 = f32x16{}, S1 = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       bf16x8 kh, kl;
       split8(kp + 16 * s, kh, kl);
+      f32x16& S = (s & 1) ? S1 : S0;
       S = mma32(kh, qh[s], S);
       S = mma32(kh, ql[s], S);
       S = mma32(kl, qh[s], S);
     }
-    return S * a.inv_sqrt_d;
+    return (S0 + S1) * a.inv_sqrt_d;
   };
   auto key_of = [&](int k0, int r) { return k0 + 8 * (r >> 2) + 4 * h + (r & 3); };
 
   // ---- pass 1: per-query max and n-weighted sum over every key block
   float m = -INFINITY;
   double s = 0.0;
-  for (int k0 = 32 * w; k0 < a.M; k0 += 128) {
+  for (int k0 = 32 * w; k0 < a.M; k0 += 32 * NW) {
     const f32x16 L = logits(k0);
     float tmax = -INFINITY;
 #pragma unroll
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void isa_saliency_kernel(SalArgs a) {
              (double)__builtin_amdgcn_exp2f((L[r] - m) * 1.4426950408889634f);
     }
   }
-  // combine the two lane halves, then the four waves, in a fixed order
+  // combine the two lane halves, then the waves, in a fixed order
   auto combine = [](float& m1, double& s1, float m2, double s2) {
     const float mm = fmaxf(m1, m2);
     double t = 0.0;
@@ -137,13 +140,13 @@ __global__ __launch_bounds__(256) void isa_saliency_kernel(SalArgs a) {
   float mq = (float)red_m[0][l32];
   double sq = red_s[0][l32];
 #pragma unroll
-  for (int v = 1; v < 4; ++v) combine(mq, sq, (float)red_m[v][l32], red_s[v][l32]);
+  for (int v = 1; v < NW; ++v) combine(mq, sq, (float)red_m[v][l32], red_s[v][l32]);
   const double inv_s = 1.0 / sq;
 
   // ---- pass 2: probabilities on the context blocks, summed over the queries
   double* out = a.salp + (bh * a.sal_tiles + tile) * (long long)a.nb_c;
   const int nct = (a.nb_c + 31) / 32;
-  for (int ct0 = 0; ct0 < nct; ct0 += 4) {
+  for (int ct0 = 0; ct0 < nct; ct0 += NW) {
     const int ct = ct0 + w;
     if (ct < nct) {
       const int k0 = a.nb_s + 32 * ct;
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(256) void isa_saliency_kernel(SalArgs a) {
     }
     __syncthreads();
     // one thread per (wave tile, key): add the 32 queries in order
-    if (tid < 128) {
+    if (tid < 32 * NW) {
       const int v = tid >> 5, kk = tid & 31;
       const int c = 32 * (ct0 + v) + kk;
       if (ct0 + v < nct && c < a.nb_c) {
@@ -182,7 +185,7 @@ static hipError_t launch_sal_t(const Layout& L, const Bufs& B, hipStream_t s) {
   a.nb_s = L.nb_s; a.nb_c = L.nb_c; a.M = L.M; a.b = L.b;
   a.tail_s = L.tail_s; a.tail_c = L.tail_c; a.sal_tiles = L.sal_tiles;
   a.inv_sqrt_d = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((isa_saliency_kernel<D>), dim3(L.sal_tiles, (unsigned)L.BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((isa_saliency_kernel<D>), dim3(L.sal_tiles, (unsigned)L.BH), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -214,14 +214,23 @@ __global__ __launch_bounds__(256) void isa_select_ctx_kernel(SelArgs a) {
   __syncthreads();
   // full-route context key rows: kept block kb covers rows Ns + kb*b + [0, b),
   // -1 past the end of a short last block
+  // (the kept list is staged through LDS 256 entries at a time, so the
+  // loop below issues no dependent global loads)
   const int ntok = a.kc * a.b;
   int* rows = a.ctx_rows + bh * ntok;
   const unsigned ub = (unsigned)a.b;
-  for (int t = tid; t < ntok; t += 256) {
-    const unsigned i = (unsigned)t / ub;
-    const int kb = kept[i];
-    const int r = kb * a.b + (int)((unsigned)t - i * ub);
-    rows[t] = (kb >= 0 && kb < a.nb_c && r < a.Nc) ? a.Ns + r : -1;
+  for (int k0 = 0; k0 < a.kc; k0 += 256) {
+    const int nk = min(256, a.kc - k0);
+    if (tid < nk) sm.idx[tid] = kept[k0 + tid];
+    __syncthreads();
+    const int t0 = k0 * a.b, t1 = (k0 + nk) * a.b;
+    for (int t = t0 + tid; t < t1; t += 256) {
+      const unsigned i = (unsigned)t / ub;
+      const int kb = sm.idx[i - k0];
+      const int r = kb * a.b + (int)((unsigned)t - i * ub);
+      rows[t] = (kb >= 0 && kb < a.nb_c && r < a.Nc) ? a.Ns + r : -1;
+    }
+    __syncthreads();
   }
 }
 

@@ -73,6 +73,7 @@ SMALL = [
     (1, 2, 128, 777, 333, 128, 0.3, 0.5, "bf16"),
     (1, 2, 64, 150, 100, 1, 0.4, 0.3, "bf16"),
     (1, 1, 64, 5000, 4200, 2, 0.3, 0.2, "bf16"),      # > 2048 blocks: radix select
+    (1, 1, 64, 3000, 2600, 2, 0.3, 0.2, "bf16"),      # 1500 and 1300 blocks: bitonic sort near its limit
     (1, 2, 64, 500, 0, 32, 0.5, 0.3, "bf16"),         # no context
     (1, 2, 64, 100, 300, 256, 0.5, 0.5, "bf16"),      # one query block
     (1, 2, 128, 1000, 900, 200, 0.5, 0.5, "bf16"),    # b above the key tile
