@@ -457,16 +457,25 @@ __device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned vo
                : "memory");
 }
 
-// Issue order of the fused X phase (32 MFMAs: 16 P.V with two operand reads
-// each, then 16 K.Q^T with one): the reads of MFMAs 0..LA-1, then each MFMA
+// Issue order of a fused X phase (NPV P.V MFMAs with two operand reads each,
+// then NQK K.Q^T MFMAs with one): the reads of MFMAs 0..LA-1, then each MFMA
 // followed by the reads of the MFMA LA places later.
-template <int LA, int M = 0>
+template <int LA, int NPV = 16, int NQK = 16, int M = 0>
 __device__ __forceinline__ void pp_issue_order() {
   constexpr int kMFMA = 0x8, kDSR = 0x100;
-  if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kDSR, LA <= 16 ? 2 * LA : 16 + LA, 0);
+  if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kDSR, LA <= NPV ? 2 * LA : NPV + LA, 0);
   __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
-  if constexpr (M + LA < 32) __builtin_amdgcn_sched_group_barrier(kDSR, M + LA < 16 ? 2 : 1, 0);
-  if constexpr (M + 1 < 32) pp_issue_order<LA, M + 1>();
+  if constexpr (M + LA < NPV + NQK) __builtin_amdgcn_sched_group_barrier(kDSR, M + LA < NPV ? 2 : 1, 0);
+  if constexpr (M + 1 < NPV + NQK) pp_issue_order<LA, NPV, NQK, M + 1>();
+}
+
+// 16 bytes per lane from base + voff into LDS at lds + 16 x lane.
+__device__ __forceinline__ void dma16(unsigned lds, const void* base, unsigned voff) {
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
 }
 
 template <int KM, int RM>
@@ -783,6 +792,298 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   }
 }
 
+// Ping-pong schedule of the pooled pass (sharpness + Taylor output of every
+// source row over the kept pooled blocks), d = 128, as a persistent kernel.
+// The arithmetic is that of isa_flash_kernel in pooled mode (hi + lo key
+// parts, additive log2 n_j bias, per-row reference max moved past 2^8, true
+// running max for the peak probability).  The key set is short (a few
+// tiles), so each workgroup takes row tiles g, g + G, ... (G workgroups) and
+// runs their key tiles as one sequence of steps j: the loads of the next row
+// tile start while the current one finishes, and a row tile's output is
+// written in the Y phase that starts the next.  Schedule as in
+// isa_flash_pp_kernel, with three-stage rings and every direct load issued
+// by group 0:
+//   X_j  acc += V(j-1)^T P(j-1)^T, then S(j) = Khi(j) Q^T + Klo(j) Q^T
+//   Y_j  [row tile change: output of the finished row tile] bias + softmax
+//        of S(j) -> P(j); group 0 also loads Khi, Klo and the bias of step
+//        j+2 and V of step j+1, then waits for its loads of Y_{j-1}
+// Group 0 runs Y_j in phase 2j+1: K(t) is issued in phase 2t-3 and has
+// landed by the end of 2t-1 (first read in 2t); its stage was last read in
+// X_{t-3} (phase 2t-5).  V(t) is issued in phase 2t-1, lands by 2t+1 and is
+// first read in 2t+2; its stage was last read in X_{t-2} (phase 2t-3).
+// The bias of step t is read in Y_t (phases 2t+1, 2t+2) and its slot was
+// last read in Y_{t-3} (phase 2t-4).  The queries of the next row tile are
+// loaded into spare registers two steps before they are used.
+__global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
+  typedef bf16x8 Op;
+  constexpr int D = 128, BN = 64, BM = 256, NST = 3;
+  constexpr int RB = D * 2, TB = BN * RB, NT = D / 32;
+  static_assert(BM == kFlashRows, "tile mapping");
+  // Khi ring, Klo ring, V ring
+  __shared__ __attribute__((aligned(1024))) char smem[3 * NST * TB];
+  __shared__ __attribute__((aligned(256))) float sbias[NST][BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int G = gridDim.x;
+  const int n_tiles = a.n_wg;                  // row tiles over all heads
+  const int nr = n_tiles > (int)blockIdx.x ? (n_tiles - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const int ntk = a.mk_pad / BN;               // key tiles per row tile (>= 2; padding keys carry bias -inf)
+  const int total = nr * ntk;                  // steps with a key tile
+  auto tile_bh = [&](int ri) { return (int)(blockIdx.x + (unsigned)ri * G) / a.row_tiles; };
+  auto tile_rt = [&](int ri) { return (int)(blockIdx.x + (unsigned)ri * G) % a.row_tiles; };
+  auto query_row = [&](int ri) -> int {
+    const long long v = (long long)tile_rt(ri) * BM + w * 32 + l32;
+    return v < a.Ns ? (int)v : -1;
+  };
+  auto load_q = [&](int ri, Op* q) {
+    const int qr = query_row(ri);
+    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)tile_bh(ri) * a.Ns + (qr < 0 ? 0 : qr)) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) q[s] = *(const Op*)(qp + 16 * s);
+  };
+
+  const unsigned lds_kh = (unsigned)(size_t)(lds_char*)smem;
+  const unsigned lds_kl = lds_kh + NST * TB, lds_v = lds_kh + 2 * NST * TB;
+  const unsigned lds_b = (unsigned)(size_t)(lds_char*)&sbias[0][0];
+  // group 0, wave wg: rows 16*wg + 4*i + lane/16 (i = 0..3) of the key tile of step t
+  auto load_tile = [&](const void* base, unsigned ring, int stage, int t) {
+    const int bh = tile_bh(t / ntk), kt = t % ntk;
+    const char* G0 = (const char*)base + ((long long)bh * a.mk_pad + kt * BN) * RB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 16 * wg + 4 * i + (lane >> 4);
+      dma16(__builtin_amdgcn_readfirstlane(ring + stage * TB + (16 * wg + 4 * i) * RB), G0,
+            (unsigned)lr * RB + (unsigned)(((lane & 15) ^ lds_swz(lr)) * 16));
+    }
+  };
+  auto load_k = [&](int stage, int t) {   // Khi, Klo and the bias (wave 0)
+    load_tile(a.pkhi, lds_kh, stage, t);
+    load_tile(a.pklo, lds_kl, stage, t);
+    if (w == 0) {
+      const float* Bg = a.pbias + (long long)tile_bh(t / ntk) * a.mk_pad + (t % ntk) * BN;
+      dma4(lds_b + stage * BN * 4, Bg, (unsigned)lane * 4u);
+    }
+  };
+
+  const int kb = l32 * RB + ((h ^ lds_swz(l32)) * 16);
+  auto koff = [&](int s) -> int { return kb ^ (32 * s); };
+  int voff[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int m = lane & 15;
+      const int kr = 4 * h + (m >> 2) + 8 * hi;
+      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+      voff[t][hi] = kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
+    }
+
+  struct STile { f32x16 t[2]; };
+  struct PTile { Op p[4]; };
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+  Op qB[D / 16], qN[D / 16];
+
+  // X phase: 16 P.V MFMAs, then 32 K.Q^T MFMAs (hi, lo of each key step),
+  // operand reads issued ISA_PP_LOOKAHEAD MFMAs ahead
+  auto pv_qk = [&](int vstage, const PTile& P, int kstage) -> STile {
+    const lds_char* Vs = (const lds_char*)smem + 2 * NST * TB + vstage * TB;
+    const lds_char* Khs = (const lds_char*)smem + kstage * TB;
+    const lds_char* Kls = (const lds_char*)smem + NST * TB + kstage * TB;
+    Op opv[16], opk[32];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * q * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * q * RB));
+        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        opk[4 * q + 2 * ti] = *(const Op*)(Khs + koff(q) + 32 * ti * RB);
+        opk[4 * q + 2 * ti + 1] = *(const Op*)(Kls + koff(q) + 32 * ti * RB);
+      }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], P.p[m & 3], acc[m >> 2]);
+    STile S;
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < 32; ++m) S.t[(m >> 1) & 1] = mma32(opk[m], qB[m >> 2], S.t[(m >> 1) & 1]);
+    pp_issue_order<ISA_PP_LOOKAHEAD, 16, 32>();
+    return S;
+  };
+  auto softmax = [&](int stage, STile St) -> PTile {
+    f32x16* S = St.t;
+    const float* bs = sbias[stage];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 bb = *(const f32x4*)(bs + 32 * ti + 8 * g + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[ti][4 * g + e] = fmaf(S[ti][4 * g + e], sc, bb[e]);
+      }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    m_true = fmaxf(m_true, mx);
+    const bool move = mx > m_ref + 8.0f;
+    if (__ballot(move)) {
+      const float m_new = move ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+      m_ref = m_new;
+    }
+    PTile P;
+    float psum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float p = __builtin_amdgcn_exp2f(S[s >> 1][8 * (s & 1) + jj] - m_ref);
+        psum += p;
+        P.p[s][jj] = (__bf16)p;
+      }
+    }
+    l_run += psum;
+    return P;
+  };
+  // Output of a finished row tile, then the running state of the next.  The
+  // stores go through buffer descriptors: a row past Ns (or a lane that
+  // does not store) gets an offset beyond the buffer, which the hardware
+  // drops, so every wave issues the same number of stores (kRowStores) and
+  // the load waits below can count them.
+  auto finish_row = [&](int ri) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int qr = query_row(ri);
+    const long long bh = tile_bh(ri);
+    const float inv = 1.0f / l_tot;
+    constexpr unsigned kOut = 0x80000000u;   // beyond every buffer below (Ns * D * 2 < 2^31)
+    const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + bh * a.Ns * D, (short)0, a.Ns * D * 2, 0x00020000);
+    const unsigned oo = qr >= 0 ? (unsigned)qr * D * 2 : kOut;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * t + 8 * g + 4 * h;
+        const u32x2 v = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                              pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rO, oo + 2 * d0, 0, 0);
+      }
+    const unsigned po = (qr >= 0 && h == 0) ? (unsigned)qr * 4 : kOut;
+    const auto rP = __builtin_amdgcn_make_buffer_rsrc(a.peak + bh * a.Ns, (short)0, a.Ns * 4, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_amdgcn_exp2f(m_true - m_ref) * inv), rP, po, 0, 0);
+    if (a.lse) {
+      const auto rL = __builtin_amdgcn_make_buffer_rsrc(a.lse + bh * a.Ns, (short)0, a.Ns * 4, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref + __builtin_log2f(l_tot)), rL, po, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+    m_ref = -INFINITY;
+    m_true = -INFINITY;
+    l_run = 0.f;
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (total > 0) {
+    load_q(0, qB);
+    if (grp == 0) {
+      load_k(0, 0);
+      load_tile(a.pv, lds_v, 0, 0);
+      if (total > 1) load_k(1, 1);
+    }
+    // V stage 2 is first loaded in step 1; step 0 reads it as zeros
+    u32x4* vz = (u32x4*)(smem + 2 * NST * TB + 2 * TB);
+#pragma unroll
+    for (int q = 0; q < TB / (16 * 512); ++q) vz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    phase_barrier();
+    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+    STile S = {};
+    PTile P = {};
+    auto step = [&](auto ph, int j) {
+      constexpr int Z = decltype(ph)::value;   // j % 3
+      const int kt = j % ntk, ri = j / ntk;
+      // X_j at raised wave priority (step `total` computes an S that is not used)
+      if (kt == 0 && j > 0) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) qB[s] = qN[s];
+      }
+      __builtin_amdgcn_s_setprio(3);
+      S = pv_qk((Z + 2) % 3, P, Z);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+      // Y_j
+      if (kt == 0 && j > 0) finish_row(ri - 1);
+      // the queries of the next row tile, two steps ahead of their first use
+      const bool more_q = kt == ntk - 2 && ri + 1 < nr;
+      if (more_q) load_q(ri + 1, qN);
+      if (grp == 0) {
+        const bool more_k = j + 2 < total, more_v = j + 1 < total;
+        if (more_k) load_k((Z + 2) % 3, j + 2);
+        if (more_v) load_tile(a.pv, lds_v, (Z + 1) % 3, j + 1);
+        if (j < total) P = softmax(Z, S);
+        // the loads of Y_{j-1} have landed before the barrier that closes Y_j
+        // (this step's 8 query loads or 17-18 output stores, if any, were
+        // issued before its tiles)
+        if (more_k && kt == 0 && j > 0) {
+          if (a.lse) {
+            if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f7f | (1 << 14));   // vmcnt(31)
+            else __builtin_amdgcn_s_waitcnt(0x0f7e | (1 << 14));          // vmcnt(30)
+          } else {
+            if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f7e | (1 << 14));   // vmcnt(30)
+            else __builtin_amdgcn_s_waitcnt(0x0f7d | (1 << 14));          // vmcnt(29)
+          }
+        } else if (more_k && more_q) {
+          if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f75 | (1 << 14));   // vmcnt(21)
+          else __builtin_amdgcn_s_waitcnt(0x0f74 | (1 << 14));          // vmcnt(20)
+        } else if (more_k) {
+          if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f7d);   // vmcnt(13)
+          else __builtin_amdgcn_s_waitcnt(0x0f7c);          // vmcnt(12)
+        } else if (more_v) {
+          __builtin_amdgcn_s_waitcnt(0x0f74);               // vmcnt(4)
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
+        }
+      } else {
+        if (j < total) P = softmax(Z, S);
+      }
+      phase_barrier();
+    };
+    for (int j = 0; j <= total; j += 3) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 <= total) step(std::integral_constant<int, 1>{}, j + 1);
+      if (j + 2 <= total) step(std::integral_constant<int, 2>{}, j + 2);
+    }
+    // (step `total` wrote the last row tile)
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+  }
+}
+
 // Merges the split-K partials of each full-route query row, in split order.
 template <int D>
 __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
@@ -906,6 +1207,18 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
       return hipGetLastError();
     }
     case FlashWhat::kSharpTaylor:
+      if constexpr (D == 128 && kFlashWaves == 8) {
+        if (L.mk_pad >= 2 * 64 && (long long)L.Ns * D * 2 < (1LL << 31)) {
+          // persistent: one workgroup per compute unit, row tiles dealt round-robin
+          a.n_rows = L.Ns;
+          a.row_tiles = (int)((L.Ns + kFlashRows - 1) / kFlashRows);
+          a.n_wg = (int)(a.row_tiles * L.BH);   // row tiles over all heads
+          if (a.n_wg == 0) return hipSuccess;
+          const int grid = a.n_wg < kCUs ? a.n_wg : kCUs;
+          hipLaunchKernelGGL(isa_flash_pp_pooled_kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
+          return hipGetLastError();
+        }
+      }
       return flash_launch<D, FK_POOLED, FR_IDENTITY, true, true>(a, L.Ns, L.mk_pad, L.BH, s);
     case FlashWhat::kSharp:
       return flash_launch<D, FK_POOLED, FR_IDENTITY, false, true>(a, L.Ns, L.mk_pad, L.BH, s);
