@@ -322,7 +322,7 @@ def main():
     if stage_ms.get("sharp_taylor"):
         mk = nb_s + counts["kc"]
         tf = 4 * w.d * w.Ns * mk * w.B * w.H / (stage_ms["sharp_taylor"] * 1e-3) / 1e12
-        others.append({"kernel": "isa_flash_kernel pooled (sharpness + Taylor)", "bound": "mfma",
+        others.append({"kernel": "isa_flash_pp_pooled_kernel (sharpness + Taylor)", "bound": "mfma",
                        "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                        "note": "4 d FLOP per (query, kept block); the lo half of the split keys is not counted"})
