@@ -79,6 +79,31 @@ __device__ __forceinline__ int swz(int c, int row, int cpr) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS loads (global_load_lds): each lane's bytes land at
+// the wave's LDS base (m0) + size x lane.  The compiler does not see them:
+// callers wait by count (s_waitcnt vmcnt) and keep LDS reads of the target
+// apart with barriers.  m0 is restored, so no register changes behind the
+// compiler's back.
+
+// 16 bytes per lane from base + voff into LDS at lds + 16 x lane.
+__device__ __forceinline__ void dma16(unsigned lds, const void* base, unsigned voff) {
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
+// 4 bytes per lane from base + voff into LDS at lds + 4 x lane.
+__device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned voff) {
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Workgroup id remap so that consecutive logical workgroups (which share a
 // head's keys) land on the same XCD: the hardware deals workgroups to the
 // 8 XCDs round-robin.

@@ -448,15 +448,6 @@ __device__ __forceinline__ void dma16x4(unsigned lk0, unsigned lk1, const void* 
       : "memory");
 }
 
-// 4 bytes per lane from base + voff into LDS at lds + 4 x lane.
-__device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned voff) {
-  unsigned saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"(voff), "s"(base)
-               : "memory");
-}
-
 // Issue order of a fused X phase (NPV P.V MFMAs with two operand reads each,
 // then NQK K.Q^T MFMAs with one): the reads of MFMAs 0..LA-1, then each MFMA
 // followed by the reads of the MFMA LA places later.
@@ -467,15 +458,6 @@ __device__ __forceinline__ void pp_issue_order() {
   __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
   if constexpr (M + LA < NPV + NQK) __builtin_amdgcn_sched_group_barrier(kDSR, M + LA < NPV ? 2 : 1, 0);
   if constexpr (M + 1 < NPV + NQK) pp_issue_order<LA, NPV, NQK, M + 1>();
-}
-
-// 16 bytes per lane from base + voff into LDS at lds + 16 x lane.
-__device__ __forceinline__ void dma16(unsigned lds, const void* base, unsigned voff) {
-  unsigned saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"(voff), "s"(base)
-               : "memory");
 }
 
 template <int KM, int RM>
