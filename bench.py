@@ -148,7 +148,7 @@ def time_fp8(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
     log("isa_attention_fp8: %.3f ms/call; full-route stages: %s" % (ms, ", ".join("%s %.3f" % kv for kv in st.items())))
     return {"ms_per_call": round(ms, 4), "queries_per_s": round(w.B * w.Ns / (ms * 1e-3), 1),
             "full_route_stage_ms": {k: round(v, 4) for k, v in st.items()},
-            "roofline": None if tf is None else {"kernel": "isa_flash_fp8_kernel", "bound": "mfma",
+            "roofline": None if tf is None else {"kernel": "isa_flash_fp8_pp_kernel", "bound": "mfma",
                                                  "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
             "dtype": "e4m3 operands, fp32 accumulation (bf16 in and out)",
