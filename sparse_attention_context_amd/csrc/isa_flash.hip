@@ -65,6 +65,8 @@ struct FlashArgs {
   const void* V;
   const int* ctx_rows;  // gather: [BH][ctx_tok] absolute rows, -1 past a short last block
   const int* kept;      // gather: [BH][kc]
+  const int* key_rows;  // gather, d = 128: [BH][n_keytab] row of every full-route key (0 for padding)
+  int n_keytab;
   long long ctx_tok;
   int kc, nb_c, b, tail_c;
   const void* pkhi;     // pooled: [BH][mk_pad][D]
@@ -433,18 +435,15 @@ __device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 2) | ((r >> 2
 // LDS at lk0/lk1 + 16 x lane, rows of V at vbase + vv0/vv1 into lv0/lv1.  One
 // asm block, so every offset (and the row-table values behind it) is ready
 // before the first load is issued; the loads are waited for by count.
-__device__ __forceinline__ void dma16x4(unsigned lk0, unsigned lk1, const void* kbase, unsigned kv0, unsigned kv1,
-                                        unsigned lv0, unsigned lv1, const void* vbase, unsigned vv0, unsigned vv1) {
+__device__ __forceinline__ void dma16x2(unsigned l0, unsigned l1, const void* base, unsigned v0, unsigned v1) {
   unsigned saved;  // m0 is restored, so the asm leaves no register changed behind the compiler's back
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %9\n\t"
-      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %9\n\t"
-      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
-      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %5\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lk0), "s"(lk1), "s"(lv0), "s"(lv1), "v"(kv0), "v"(kv1), "v"(vv0), "v"(vv1), "s"(kbase), "s"(vbase)
+      : "s"(l0), "s"(l1), "v"(v0), "v"(v1), "s"(base)
       : "memory");
 }
 
@@ -508,30 +507,27 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
 
   const char* Kg = (const char*)a.K + (long long)bh * a.Nk * RB;
   const char* Vg = (const char*)a.V + (long long)bh * a.Nk * RB;
-  const int* crow = GATHER ? a.ctx_rows + (long long)bh * a.ctx_tok : nullptr;
-  const int ctx_last = (int)a.ctx_tok - 1;
-  // (without context rows the table read goes to the first K word: every
-  // row is then a source row and the value is never used)
-  const int* tab = ctx_last >= 0 ? crow : (const int*)Kg;
-  const int tab_last = max(ctx_last, 0);
+  const int* tab = GATHER ? a.key_rows + (long long)bh * a.n_keytab : nullptr;
 
   // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
   // tile, one 16-byte chunk each: physical chunk lane%16 of the row, which
   // holds logical chunk (lane%16) ^ f(row).
   const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
   struct Rows { int r[2]; };
-  // Gather: the row-table entries of the wave's 8 rows of tile t come to a
+  // Gather: the key-row table entries of the wave's 8 rows of tile t come to a
   // per-wave LDS ring (slot t % 4) by a direct load in step t-6, entry
   // 2q + i holding row 32*grp + 8*wg + q + 4i, are read into registers in
   // step t-4 and used in steps t-3 (K) and t-2 (V); so no load result is
   // waited for inside the tile loop.
   __shared__ __attribute__((aligned(16))) int stab[GATHER ? 8 : 1][4][64];
   // (slots are indexed by the tile's position j in this workgroup's range)
+  const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
+                          __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
   auto fetch_rows = [&](int j, int tile) {
     if constexpr (GATHER) {
       const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
-      const int idx = min(max(tile * BN + 32 * grp + 8 * wg + k - a.Ns, 0), tab_last);
-      dma4(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[w][j & 3][0]), tab, (unsigned)idx * 4u);
+      const int idx = tile * BN + 32 * grp + 8 * wg + k;
+      dma4(stab_w + (unsigned)(j & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)idx * 4u);
     }
   };
   auto rows_of = [&](int j) -> Rows {
@@ -545,21 +541,47 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   };
   const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
   const unsigned lds_v = lds_k + NST * TB;
-  auto src_off = [&](Rows rows, int tile, int i) -> unsigned {
-    const int lr = lrow0 + 4 * i;
-    const int t = tile * BN + lr;
-    int r;
-    if constexpr (GATHER) r = t < a.Ns ? t : (t < n_valid && rows.r[i] >= 0 ? rows.r[i] : 0);
-    else r = t < n_valid ? t : 0;
-    return (unsigned)r * RB + (unsigned)(((lane & 15) ^ lds_swz(lr)) * 16);
+  // Lane part of the i-th load: row lrow0 + 4i (its offset within a tile)
+  // and the 16-byte chunk that the swizzle puts at this lane.
+  unsigned lchunk[2], lrowoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
+    lrowoff[i] = (unsigned)(lrow0 + 4 * i) * RB + lchunk[i];
+  }
+  // Global offsets of the wave's two loads of a tile: gathered rows come
+  // from the key-row table (whose padding reads row 0), dense tiles of
+  // valid rows only are a contiguous row range (a uniform branch).
+  auto src_offs = [&](Rows rows, int tile, unsigned* o) {
+    const int t0 = tile * BN;
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) o[i] = (unsigned)rows.r[i] * RB + lchunk[i];
+    } else {
+      if (t0 + BN <= n_valid) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o[i] = (unsigned)t0 * RB + lrowoff[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int t = t0 + lrow0 + 4 * i;
+          o[i] = (unsigned)(t < n_valid ? t : 0) * RB + lchunk[i];
+        }
+      }
+    }
   };
-  // LDS base of this wave's i-th load into a ring stage
-  auto dst = [&](unsigned ring, int stage, int i) -> unsigned {
-    return __builtin_amdgcn_readfirstlane(ring + stage * TB + (32 * grp + 8 * wg + 4 * i) * RB);
+  // LDS base of this wave's first load into a ring stage (the second is 4
+  // rows further)
+  const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, int tile) {
+    unsigned o[2];
+    src_offs(rows, tile, o);
+    const unsigned d0 = ring + wrow + (unsigned)stage * TB;
+    dma16x2(d0, d0 + 4 * RB, base, o[0], o[1]);
   };
   auto issue = [&](int sk, Rows rk, int tk, int sv, Rows rv, int tv) {
-    dma16x4(dst(lds_k, sk, 0), dst(lds_k, sk, 1), Kg, src_off(rk, tk, 0), src_off(rk, tk, 1),
-            dst(lds_v, sv, 0), dst(lds_v, sv, 1), Vg, src_off(rv, tv, 0), src_off(rv, tv, 1));
+    issue_tile(lds_k, sk, Kg, rk, tk);
+    issue_tile(lds_v, sv, Vg, rv, tv);
   };
 
   // operand offsets: K row 32*ti + l32, logical chunk 2s + h; V^T transpose
@@ -1124,6 +1146,7 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
   a.nsplit = 1;
   if (B.ws) {
     a.ctx_rows = (const int*)(B.ws + L.off_ctxrows);
+    a.key_rows = (const int*)(B.ws + L.off_keyrows);
     a.kept = (const int*)(B.ws + L.off_kept);
     a.pkhi = B.ws + L.off_pkhi;
     a.pklo = B.ws + L.off_pklo;
@@ -1135,6 +1158,7 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
     a.lse = (float*)(B.ws + L.off_lse);
   }
   a.ctx_tok = L.ctx_tok;
+  a.n_keytab = L.n_keytab;
   a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;
   a.mk_pad = L.mk_pad;
   a.nb_s = L.nb_s;

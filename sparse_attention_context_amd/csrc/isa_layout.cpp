@@ -76,6 +76,7 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
     const int64_t row_tiles = (L->full_rows + kFlashRows - 1) / kFlashRows;
     const int ntiles = (int)((D.Ns + L->ctx_tok + 63) / 64);
     L->full_splits = L->es == 2 ? choose_splits(bh * row_tiles, ntiles) : 1;
+    L->n_keytab = ntiles * kTileKeys;
   }
 
   const size_t d = (size_t)D.d;
@@ -96,6 +97,7 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   take(&L->off_pv, bh * L->mk_pad * d * pk_es);
   take(&L->off_pbias, bh * L->mk_pad * 4);
   take(&L->off_ctxrows, bh * L->ctx_tok * 4);
+  take(&L->off_keyrows, bh * (size_t)L->n_keytab * 4);
   take(&L->off_peak, bh * D.Ns * 4);
   take(&L->off_sh, bh * L->nb_s * 8);
   take(&L->off_fullq, bh * L->kq * 4);

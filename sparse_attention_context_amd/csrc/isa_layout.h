@@ -37,9 +37,11 @@ struct Layout {
   int64_t full_rows;   // kq*b virtual full-route query rows
   int64_t taylor_rows; // (nb_s-kq)*b virtual Taylor-route query rows
   int full_splits;     // key-range splits of the full-route attention (bf16)
+  int n_keytab;        // full-route key rows per head, rounded up to kTileKeys
   // byte offsets into the workspace
   size_t off_qbar, off_kbar, off_vbar, off_salp, off_sal, off_kept;
   size_t off_pkhi, off_pklo, off_pv, off_pbias, off_ctxrows;
+  size_t off_keyrows;  // [BH][n_keytab] int32: row of K/V of every full-route key (0 for padding)
   size_t off_peak, off_sh, off_fullq, off_taylq;
   size_t off_part_o, off_part_ml;
   size_t off_lse;      // [BH][Ns] log2-domain log-sum-exp of each source row's softmax

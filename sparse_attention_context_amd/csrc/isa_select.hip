@@ -185,7 +185,8 @@ struct SelArgs {
   double* sh;
   int* full_q;
   int* taylor_q;
-  int Ns, Nc, b, nb_s, nb_c, kc, kq, sal_tiles, tail_s;
+  int* key_rows;
+  int Ns, Nc, b, nb_s, nb_c, kc, kq, sal_tiles, tail_s, n_keytab;
 };
 
 __global__ __launch_bounds__(256) void isa_select_ctx_kernel(SelArgs a) {
@@ -261,6 +262,23 @@ __global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
   int* fq = a.full_q + bh * a.kq;
   int* tq = a.taylor_q + bh * (a.nb_s - a.kq);
   select_topk(sh, a.nb_s, a.kq, fq, tq, sm);
+  // K/V row of every key of the full route, four per store: the source
+  // rows, then the context rows (a short last block's -1 and the padding
+  // up to whole tiles read row 0; the attention masks those keys)
+  if (a.kq > 0) {
+    const int ntok = a.kc * a.b;
+    const int* crow = a.ctx_rows + bh * ntok;
+    int4* tab = (int4*)(a.key_rows + bh * a.n_keytab);
+    for (int q = tid; q < a.n_keytab / 4; q += 256) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = 4 * q + u;
+        v[u] = t < a.Ns ? t : (t - a.Ns < ntok ? max(crow[t - a.Ns], 0) : 0);
+      }
+      tab[q] = int4{v[0], v[1], v[2], v[3]};
+    }
+  }
 }
 
 static SelArgs sel_args(const Layout& L, const Bufs& B) {
@@ -273,6 +291,8 @@ static SelArgs sel_args(const Layout& L, const Bufs& B) {
   a.sh = (double*)(B.ws + L.off_sh);
   a.full_q = (int*)(B.ws + L.off_fullq);
   a.taylor_q = (int*)(B.ws + L.off_taylq);
+  a.key_rows = (int*)(B.ws + L.off_keyrows);
+  a.n_keytab = L.n_keytab;
   a.Ns = L.Ns; a.Nc = L.Nc; a.b = L.b; a.nb_s = L.nb_s; a.nb_c = L.nb_c;
   a.kc = L.kc; a.kq = L.kq; a.sal_tiles = L.sal_tiles; a.tail_s = L.tail_s;
   return a;
