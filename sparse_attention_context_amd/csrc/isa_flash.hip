@@ -6,7 +6,8 @@
 // 0-th order Taylor sparse attention, after grouping queries by sharpness.
 //  * full route (FK_GATHER): exact softmax attention over every source token
 //    plus every token of the kept context blocks, K/V rows gathered through
-//    the kept-context row table;
+//    the kept-context row table (d = 64) or the full-route key-row table,
+//    one row per key of the route (d = 128);
 //  * dense (FK_DENSE): every source query over every key row, the global
 //    self-attention softmax(q k^T / sqrt d) v of the intelliparadigm.com page,
 //    section 1 -- the library's own dense baseline;
