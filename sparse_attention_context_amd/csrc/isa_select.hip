@@ -235,10 +235,34 @@ __global__ __launch_bounds__(256) void isa_select_ctx_kernel(SelArgs a) {
   }
 }
 
+// Workgroups (bh, y > 0) of the query selection write chunk y - 1 of the
+// head's full-route key-row table, beside the selection of workgroup (bh, 0):
+// the K/V row of every key of the route, four per store -- the source rows,
+// then the context rows (a short last block's -1 and the padding up to whole
+// tiles read row 0; the attention masks those keys).
+constexpr int kKeyTabChunk = 256 * 4 * 8;
+
 __global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
   __shared__ SelectSmem sm;
   const long long bh = blockIdx.x;
   const int tid = threadIdx.x;
+  if (blockIdx.y > 0) {
+    const int ntok = a.kc * a.b;
+    const int* crow = a.ctx_rows + bh * ntok;
+    int4* tab = (int4*)(a.key_rows + bh * a.n_keytab);
+    const int q0 = (int)(blockIdx.y - 1) * (kKeyTabChunk / 4);
+    const int q1 = min(q0 + kKeyTabChunk / 4, a.n_keytab / 4);
+    for (int q = q0 + tid; q < q1; q += 256) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = 4 * q + u;
+        v[u] = t < a.Ns ? t : (t - a.Ns < ntok ? max(crow[t - a.Ns], 0) : 0);
+      }
+      tab[q] = int4{v[0], v[1], v[2], v[3]};
+    }
+    return;
+  }
   double* sh = a.sh + bh * a.nb_s;
   const float* pk = a.peak + bh * a.Ns;
   // block means of the per-row peaks, rows added in order; the rows of a
@@ -262,23 +286,6 @@ __global__ __launch_bounds__(256) void isa_select_q_kernel(SelArgs a) {
   int* fq = a.full_q + bh * a.kq;
   int* tq = a.taylor_q + bh * (a.nb_s - a.kq);
   select_topk(sh, a.nb_s, a.kq, fq, tq, sm);
-  // K/V row of every key of the full route, four per store: the source
-  // rows, then the context rows (a short last block's -1 and the padding
-  // up to whole tiles read row 0; the attention masks those keys)
-  if (a.kq > 0) {
-    const int ntok = a.kc * a.b;
-    const int* crow = a.ctx_rows + bh * ntok;
-    int4* tab = (int4*)(a.key_rows + bh * a.n_keytab);
-    for (int q = tid; q < a.n_keytab / 4; q += 256) {
-      int v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = 4 * q + u;
-        v[u] = t < a.Ns ? t : (t - a.Ns < ntok ? max(crow[t - a.Ns], 0) : 0);
-      }
-      tab[q] = int4{v[0], v[1], v[2], v[3]};
-    }
-  }
 }
 
 static SelArgs sel_args(const Layout& L, const Bufs& B) {
@@ -305,7 +312,9 @@ hipError_t launch_select_ctx(const Layout& L, const Bufs& B, hipStream_t s) {
 }
 
 hipError_t launch_select_q(const Layout& L, const Bufs& B, hipStream_t s) {
-  hipLaunchKernelGGL(isa_select_q_kernel, dim3((unsigned)L.BH), dim3(256), 0, s, sel_args(L, B));
+  // the key-row table is needed by the full route only
+  const unsigned chunks = L.kq > 0 ? (unsigned)((L.n_keytab + kKeyTabChunk - 1) / kKeyTabChunk) : 0u;
+  hipLaunchKernelGGL(isa_select_q_kernel, dim3((unsigned)L.BH, 1u + chunks), dim3(256), 0, s, sel_args(L, B));
   return hipGetLastError();
 }
 

@@ -81,6 +81,8 @@ SMALL = [
     (1, 2, 128, 640, 577, 64, 1.0, 1.0, "bf16"),      # dense limit
     (1, 2, 128, 333, 271, 32, 0.5, 0.4, "f32"),
     (1, 3, 64, 1111, 999, 48, 0.2, 0.7, "bf16"),
+    (1, 2, 128, 500, 0, 32, 0.5, 0.3, "bf16"),        # no context at d = 128: the key-row table is the source rows
+    (1, 2, 128, 700, 630, 50, 1.0, 0.5, "bf16"),      # short last context block kept; tiles straddle Ns and the gap
 ]
 
 
