@@ -852,24 +852,38 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   const unsigned lds_kh = (unsigned)(size_t)(lds_char*)smem;
   const unsigned lds_kl = lds_kh + NST * TB, lds_v = lds_kh + 2 * NST * TB;
   const unsigned lds_b = (unsigned)(size_t)(lds_char*)&sbias[0][0];
-  // group 0, wave wg: rows 16*wg + 4*i + lane/16 (i = 0..3) of the key tile of step t
-  auto load_tile = [&](const void* base, unsigned ring, int stage, int t) {
-    const int bh = tile_bh(t / ntk), kt = t % ntk;
-    const char* G0 = (const char*)base + ((long long)bh * a.mk_pad + kt * BN) * RB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lr = 16 * wg + 4 * i + (lane >> 4);
-      dma16(__builtin_amdgcn_readfirstlane(ring + stage * TB + (16 * wg + 4 * i) * RB), G0,
-            (unsigned)lr * RB + (unsigned)(((lane & 15) ^ lds_swz(lr)) * 16));
+  // Key tile of step t: a cursor walks the steps in order, so the head of
+  // a row tile (a division) is formed once per row tile, not per load.
+  struct Cursor { int kt, ri; long long row0; };   // row0: first pooled row of the head
+  auto cursor_at = [&](int t) -> Cursor {
+    const int ri = t / ntk;
+    return Cursor{t - ri * ntk, ri, (long long)tile_bh(ri) * a.mk_pad};
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.kt == ntk) {
+      c.kt = 0;
+      ++c.ri;
+      c.row0 = (long long)tile_bh(c.ri) * a.mk_pad;
     }
   };
-  auto load_k = [&](int stage, int t) {   // Khi, Klo and the bias (wave 0)
-    load_tile(a.pkhi, lds_kh, stage, t);
-    load_tile(a.pklo, lds_kl, stage, t);
-    if (w == 0) {
-      const float* Bg = a.pbias + (long long)tile_bh(t / ntk) * a.mk_pad + (t % ntk) * BN;
-      dma4(lds_b + stage * BN * 4, Bg, (unsigned)lane * 4u);
-    }
+  // group 0, wave wg: rows 16*wg + 4*i + lane/16 (i = 0..3) of the key tile
+  const unsigned wrow = __builtin_amdgcn_readfirstlane(16 * wg * RB);
+  unsigned loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = 16 * wg + 4 * i + (lane >> 4);
+    loff[i] = (unsigned)lr * RB + (unsigned)(((lane & 15) ^ lds_swz(lr)) * 16);
+  }
+  auto load_tile = [&](const void* base, unsigned ring, int stage, const Cursor& c) {
+    const char* G0 = (const char*)base + (c.row0 + c.kt * BN) * RB;
+    const unsigned d0 = ring + (unsigned)stage * TB + wrow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(d0 + 4 * i * RB, G0, loff[i]);
+  };
+  auto load_k = [&](int stage, const Cursor& c) {   // Khi, Klo and the bias (wave 0)
+    load_tile(a.pkhi, lds_kh, stage, c);
+    load_tile(a.pklo, lds_kl, stage, c);
+    if (w == 0) dma4(lds_b + stage * BN * 4, a.pbias + c.row0 + c.kt * BN, (unsigned)lane * 4u);
   };
 
   const int kb = l32 * RB + ((h ^ lds_swz(l32)) * 16);
@@ -982,15 +996,28 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     constexpr unsigned kOut = 0x80000000u;   // beyond every buffer below (Ns * D * 2 < 2^31)
     const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + bh * a.Ns * D, (short)0, a.Ns * D * 2, 0x00020000);
     const unsigned oo = qr >= 0 ? (unsigned)qr * D * 2 : kOut;
+    // 16-byte chunk c = d / 8 = 4t + g of the row: lanes l and l + 32 hold
+    // its halves.  For the chunk pair (2k, 2k + 1) one permlane32 swap per
+    // word gives lane l all of chunk 2k and lane l + 32 all of chunk 2k + 1,
+    // so a store writes 32 bytes of each row instead of 16.
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int k = 0; k < 8; ++k) {
+      unsigned x[2], y[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * t + 8 * g + 4 * h;
-        const u32x2 v = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
-                              pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b64(v, rO, oo + 2 * d0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        const int c = 2 * k + u, t = c >> 2, g = c & 3;
+        unsigned* dst = u ? y : x;
+        dst[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+        dst[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
       }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+        x[e] = sw[0];
+        y[e] = sw[1];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{x[0], x[1], y[0], y[1]}, rO, oo + 16 * (2 * k + h), 0, 0);
+    }
     const unsigned po = (qr >= 0 && h == 0) ? (unsigned)qr * 4 : kOut;
     const auto rP = __builtin_amdgcn_make_buffer_rsrc(a.peak + bh * a.Ns, (short)0, a.Ns * 4, 0x00020000);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_amdgcn_exp2f(m_true - m_ref) * inv), rP, po, 0, 0);
@@ -1015,9 +1042,9 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   if (total > 0) {
     load_q(0, qB);
     if (grp == 0) {
-      load_k(0, 0);
-      load_tile(a.pv, lds_v, 0, 0);
-      if (total > 1) load_k(1, 1);
+      load_k(0, cursor_at(0));
+      load_tile(a.pv, lds_v, 0, cursor_at(0));
+      if (total > 1) load_k(1, cursor_at(1));
     }
     // V stage 2 is first loaded in step 1; step 0 reads it as zeros
     u32x4* vz = (u32x4*)(smem + 2 * NST * TB + 2 * TB);
@@ -1028,6 +1055,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
     STile S = {};
     PTile P = {};
+    Cursor ck = cursor_at(2), cv = cursor_at(1);   // K of step j+2, V of step j+1
     auto step = [&](auto ph, int j) {
       constexpr int Z = decltype(ph)::value;   // j % 3
       const int kt = j % ntk, ri = j / ntk;
@@ -1048,19 +1076,19 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
       if (more_q) load_q(ri + 1, qN);
       if (grp == 0) {
         const bool more_k = j + 2 < total, more_v = j + 1 < total;
-        if (more_k) load_k((Z + 2) % 3, j + 2);
-        if (more_v) load_tile(a.pv, lds_v, (Z + 1) % 3, j + 1);
+        if (more_k) load_k((Z + 2) % 3, ck);
+        if (more_v) load_tile(a.pv, lds_v, (Z + 1) % 3, cv);
         if (j < total) P = softmax(Z, S);
         // the loads of Y_{j-1} have landed before the barrier that closes Y_j
-        // (this step's 8 query loads or 17-18 output stores, if any, were
+        // (this step's 8 query loads or 9-10 output stores, if any, were
         // issued before its tiles)
         if (more_k && kt == 0 && j > 0) {
           if (a.lse) {
-            if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f7f | (1 << 14));   // vmcnt(31)
-            else __builtin_amdgcn_s_waitcnt(0x0f7e | (1 << 14));          // vmcnt(30)
+            if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f77 | (1 << 14));   // vmcnt(23)
+            else __builtin_amdgcn_s_waitcnt(0x0f76 | (1 << 14));          // vmcnt(22)
           } else {
-            if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f7e | (1 << 14));   // vmcnt(30)
-            else __builtin_amdgcn_s_waitcnt(0x0f7d | (1 << 14));          // vmcnt(29)
+            if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f76 | (1 << 14));   // vmcnt(22)
+            else __builtin_amdgcn_s_waitcnt(0x0f75 | (1 << 14));          // vmcnt(21)
           }
         } else if (more_k && more_q) {
           if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f75 | (1 << 14));   // vmcnt(21)
@@ -1076,6 +1104,9 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
       } else {
         if (j < total) P = softmax(Z, S);
       }
+      // (outside the group branch, so that the cursors stay scalar)
+      advance(ck);
+      advance(cv);
       phase_barrier();
     };
     for (int j = 0; j <= total; j += 3) {
