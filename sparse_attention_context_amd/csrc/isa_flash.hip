@@ -767,32 +767,40 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
     if (grp == 0) phase_barrier();   // balances group 1's extra barrier
   }
 
-  // ---- epilogue (as isa_flash_kernel's)
+  // ---- epilogue (as isa_flash_kernel's).  16-byte chunk c = d / 8 of a
+  // row has its halves in lanes l and l + 32; for the chunk pair (2k, 2k+1)
+  // one permlane32 swap per word gives lane l all of chunk 2k and lane l + 32
+  // all of chunk 2k + 1, so each store writes 32 bytes of a row, not 16.
+  // (Both lanes of a row are active or inactive together.)
+  auto store_row = [&](bf16_t* rowp, float inv) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      unsigned x[2], y[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 2 * k + u, t = c >> 2, g = c & 3;
+        unsigned* dst = u ? y : x;
+        dst[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+        dst[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+        x[e] = sw[0];
+        y[e] = sw[1];
+      }
+      *(u32x4*)(rowp + 8 * (2 * k + h)) = u32x4{x[0], x[1], y[0], y[1]};
+    }
+  };
   const float l_tot = l_run + wave_shfl_xor(l_run, 32);
   if (a.nsplit == 1) {
     if (qrow >= 0) {
-      const float inv = 1.0f / l_tot;
-      bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * t + 8 * g + 4 * h;
-          *(u32x2*)(op + d0) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
-                                     pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
-        }
+      store_row((bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D, 1.0f / l_tot);
       if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref * sc + __builtin_log2f(l_tot);
     }
   } else {
     const long long prow = ((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split;
-    bf16_t* po = a.part_o + prow * D;
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2*)(po + 32 * t + 8 * g + 4 * h) = u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
-                                                       pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+    store_row(a.part_o + prow * D, l_tot > 0.f ? 1.0f / l_tot : 0.f);
     if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref, l_tot};
   }
 }
