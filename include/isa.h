@@ -122,11 +122,13 @@ typedef enum isa_stage {
   ISA_STAGE_POOL = 0,         /* block means: source Q, every K block, source V (pooling) */
   ISA_STAGE_SALIENCY = 1,     /* per-workgroup column sums of the pooled softmax (saliency) */
   ISA_STAGE_SELECT_CTX = 2,   /* sal, kept_ctx (top-rho) and the context key-row table */
-  ISA_STAGE_POOL_KEPT_V = 3,  /* block means of V for the kept context blocks */
-  ISA_STAGE_PACK = 4,         /* kept pooled keys (bf16 hi/lo), values and log2 n_j */
+  ISA_STAGE_POOL_KEPT_V = 3,  /* block means of V for the kept context blocks, and in the same
+                                 launch the packed kept set: pooled keys (bf16 hi/lo), values, log2 n_j */
+  ISA_STAGE_PACK = 4,         /* no work of its own (the packing runs with POOL_KEPT_V); kept so that
+                                 stage sequences stay valid */
   ISA_STAGE_SHARP_TAYLOR = 5, /* per-row peak probability + Taylor output of every row into O */
   ISA_STAGE_SHARP = 6,        /* per-row peak probability only (sharpness) */
-  ISA_STAGE_SELECT_Q = 7,     /* sh and full_q / taylor_q (top-gamma) */
+  ISA_STAGE_SELECT_Q = 7,     /* sh, full_q / taylor_q (top-gamma) and the full-route key-row table */
   ISA_STAGE_TAYLOR = 8,       /* Taylor output of the Taylor-route rows into O */
   ISA_STAGE_FULL = 9,         /* full attention of the full-route rows: into O, or into
                                  split partials when the key range is split */

@@ -35,13 +35,13 @@ isa_status check_ws(const isa::Layout& L, const void* ws, size_t bytes) {
     if (st_ != ISA_OK) return st_;                \
   } while (0)
 
-// Pooling, saliency, context pre-selection and packing of the kept set.
+// Pooling, saliency, context pre-selection and packing of the kept set
+// (with the pooling of the kept context blocks' V).
 isa_status select_context(const isa::Layout& L, const isa::Bufs& B, hipStream_t s) {
-  ISA_RUN(isa::launch_pool(L, B, 0, s));
+  ISA_RUN(isa::launch_pool(L, B, s));
   ISA_RUN(isa::launch_saliency(L, B, s));
   ISA_RUN(isa::launch_select_ctx(L, B, s));
-  if (L.kc > 0) ISA_RUN(isa::launch_pool(L, B, 1, s));
-  ISA_RUN(isa::launch_pack(L, B, s));
+  ISA_RUN(isa::launch_pool_pack(L, B, s));
   return ISA_OK;
 }
 
@@ -191,11 +191,11 @@ extern "C" isa_status isa_run_stage(const isa_desc* desc, int stage, const void*
   const isa::Bufs B{Q, K, V, O, (char*)workspace};
   hipStream_t s = (hipStream_t)stream;
   switch (stage) {
-    case ISA_STAGE_POOL: ISA_RUN(isa::launch_pool(L, B, 0, s)); break;
+    case ISA_STAGE_POOL: ISA_RUN(isa::launch_pool(L, B, s)); break;
     case ISA_STAGE_SALIENCY: ISA_RUN(isa::launch_saliency(L, B, s)); break;
     case ISA_STAGE_SELECT_CTX: ISA_RUN(isa::launch_select_ctx(L, B, s)); break;
-    case ISA_STAGE_POOL_KEPT_V: if (L.kc > 0) ISA_RUN(isa::launch_pool(L, B, 1, s)); break;
-    case ISA_STAGE_PACK: ISA_RUN(isa::launch_pack(L, B, s)); break;
+    case ISA_STAGE_POOL_KEPT_V: ISA_RUN(isa::launch_pool_pack(L, B, s)); break;
+    case ISA_STAGE_PACK: break;   // packed by the launch of ISA_STAGE_POOL_KEPT_V
     case ISA_STAGE_SHARP_TAYLOR: ISA_RUN(isa::launch_pooled_attention(L, B, 0, s)); break;
     case ISA_STAGE_SHARP: ISA_RUN(isa::launch_pooled_attention(L, B, 1, s)); break;
     case ISA_STAGE_SELECT_Q: ISA_RUN(isa::launch_select_q(L, B, s)); break;

@@ -17,9 +17,14 @@ struct Bufs {
   char* ws;
 };
 
-// Block mean-pool.  pass 0: source query blocks, every key block and the
-// source value blocks; pass 1: value blocks of the kept context blocks.
-hipError_t launch_pool(const Layout& L, const Bufs& B, int pass, hipStream_t s);
+// Block mean-pool of the source query blocks, every key block and the
+// source value blocks.
+hipError_t launch_pool(const Layout& L, const Bufs& B, hipStream_t s);
+
+// After the context selection: block means of V for the kept context
+// blocks, and the packed kept key set of the pooled attention (keys as bf16
+// hi/lo, values, log2 n_j; padding rows zero with bias -inf).
+hipError_t launch_pool_pack(const Layout& L, const Bufs& B, hipStream_t s);
 
 // Context saliency partial column sums, one workgroup per kSalRows pooled
 // queries of one head.
@@ -28,9 +33,6 @@ hipError_t launch_saliency(const Layout& L, const Bufs& B, hipStream_t s);
 // Context top-rho: sums the partials into sal, selects kept_ctx and writes
 // the full-route context row table.
 hipError_t launch_select_ctx(const Layout& L, const Bufs& B, hipStream_t s);
-
-// Packs the kept pooled blocks for the pooled-attention kernel.
-hipError_t launch_pack(const Layout& L, const Bufs& B, hipStream_t s);
 
 // Query top-gamma: block means of the per-row peaks into sh, selects full_q /
 // taylor_q and writes both query row tables.

@@ -8,6 +8,11 @@
 // One wave per block.  A row of d elements is CPR 16-byte chunks; the 64
 // lanes cover 64/CPR rows at a time, each lane summing one chunk column in
 // fp32, then a fixed xor-shuffle tree adds the row groups (deterministic).
+//
+// Two launches: the pooling pass (source Q, every K block, source V) before
+// the saliency, and, after the context selection, the packing pass, which
+// pools V of the kept context blocks and writes the packed kept key set of
+// the pooled attention in the same wave.
 #include "isa_device.h"
 #include "isa_kernels.h"
 
@@ -20,57 +25,27 @@ struct PoolArgs {
   float* qbar;
   float* kbar;
   float* vbar;
-  const int* kept;  // pass 1
-  int Ns, Nc, Nk, b, nb_s, nb_c, M, kc;
+  const int* kept;  // packing pass: [BH][kc]
+  void* pkhi;       // packing pass: [BH][mk_pad][D] in the input type
+  bf16_t* pklo;     // (bf16 inputs only)
+  void* pv;
+  float* pbias;     // [BH][mk_pad]
+  int Ns, Nc, Nk, b, nb_s, nb_c, M, kc, mk, mk_pad, tail_s, tail_c;
   int tasks_per_head;
-  int pass;
   long long total_tasks;
 };
 
+// Mean of `rows` rows of d elements from `base` (16-byte chunk column c =
+// lane % CPR of each row): every lane of column c ends with the sums.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
+__device__ __forceinline__ void pool_rows(const char* base, int rows, float* acc) {
   constexpr int ES = sizeof(T);
   constexpr int CPR = D * ES / 16;     // 16-byte chunks per row
   constexpr int RG = 64 / CPR;         // rows in flight per wave
   constexpr int EPC = 16 / ES;         // elements per chunk
   const int lane = threadIdx.x & 63;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= a.total_tasks) return;
-  const long long bh = task / a.tasks_per_head;
-  int t = (int)(task - bh * a.tasks_per_head);
-
-  // task -> (tensor, block)
-  const void* src;
-  float* dst;
-  int rows, blk;
-  long long nrows_head;
-  if (a.pass == 0) {
-    if (t < a.nb_s) {
-      src = a.Q; dst = a.qbar + (bh * a.nb_s + t) * D; blk = t; nrows_head = a.Ns;
-    } else if (t < a.nb_s + a.M) {
-      blk = t - a.nb_s; src = a.K; dst = a.kbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
-    } else {
-      blk = t - a.nb_s - a.M; src = a.V; dst = a.vbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
-    }
-  } else {
-    const int kc_blk = a.kept[bh * a.kc + t];
-    if (kc_blk < 0 || kc_blk >= a.nb_c) return;  // never for a well-formed list
-    blk = a.nb_s + kc_blk;
-    src = a.V; dst = a.vbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
-  }
-  int r0;
-  if (blk < a.nb_s) {
-    r0 = blk * a.b;
-    rows = min(a.b, a.Ns - r0);
-  } else {
-    const int c = blk - a.nb_s;
-    r0 = a.Ns + c * a.b;
-    rows = min(a.b, a.Nc - c * a.b);
-  }
-
   const int c = lane % CPR, rg = lane / CPR;
-  const char* base = (const char*)src + ((bh * nrows_head + r0) * D) * ES + c * 16;
-  float acc[EPC];
+  base += c * 16;
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
   // BATCH rows per lane are loaded before any is added (bytes in flight);
@@ -102,35 +77,175 @@ __global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
   for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] += wave_shfl_xor(acc[e], off);
-  if (rg == 0) {
-    const float n = (float)rows;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) dst[c * EPC + e] = acc[e] / n;
+}
+
+// First row and row count of pooled block blk (source blocks, then context).
+__device__ __forceinline__ void block_rows(const PoolArgs& a, int blk, int* r0, int* rows) {
+  if (blk < a.nb_s) {
+    *r0 = blk * a.b;
+    *rows = min(a.b, a.Ns - *r0);
+  } else {
+    const int c = blk - a.nb_s;
+    *r0 = a.Ns + c * a.b;
+    *rows = min(a.b, a.Nc - c * a.b);
   }
 }
 
+// Pooling pass: task t of a head is source query block t (t < nb_s), key
+// block t - nb_s (every one of the M blocks) or source value block
+// t - nb_s - M.
 template <typename T, int D>
-static hipError_t launch_pool_t(const Layout& L, const Bufs& B, int pass, hipStream_t s) {
+__global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int CPR = D * ES / 16;
+  constexpr int EPC = 16 / ES;
+  const int lane = threadIdx.x & 63;
+  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= a.total_tasks) return;
+  const long long bh = task / a.tasks_per_head;
+  const int t = (int)(task - bh * a.tasks_per_head);
+  const void* src;
+  float* dst;
+  int blk;
+  long long nrows_head;
+  if (t < a.nb_s) {
+    src = a.Q; dst = a.qbar + (bh * a.nb_s + t) * D; blk = t; nrows_head = a.Ns;
+  } else if (t < a.nb_s + a.M) {
+    blk = t - a.nb_s; src = a.K; dst = a.kbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
+  } else {
+    blk = t - a.nb_s - a.M; src = a.V; dst = a.vbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
+  }
+  int r0, rows;
+  block_rows(a, blk, &r0, &rows);
+  float acc[EPC];
+  pool_rows<T, D>((const char*)src + ((bh * nrows_head + r0) * D) * ES, rows, acc);
+  if (lane < CPR) {
+    const float n = (float)rows;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) dst[lane * EPC + e] = acc[e] / n;
+  }
+}
+
+// Packing pass: task p of a head is row p of the packed kept key set of the
+// pooled (Taylor / sharpness) attention -- source block p (p < nb_s), kept
+// context block kept[p - nb_s] (p < mk), or padding (zero, bias -inf).  A
+// kept context block's V rows are pooled here (its K was pooled in the
+// first pass); source blocks take both from the first pass.  The bias is
+// log2 n_j, the count weight of the n-weighted softmax in the exp2 domain.
+// bf16 inputs store each pooled key as hi = bf16(k) and lo = bf16(k - hi):
+// the two bf16 products with a bf16 query carry the logit to about 2^-17
+// relative, well inside what the sharpness selection needs.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void isa_pool_pack_kernel(PoolArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int CPR = D * ES / 16;
+  constexpr int EPC = 16 / ES;
+  const int lane = threadIdx.x & 63;
+  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= a.total_tasks) return;
+  const long long bh = task / a.mk_pad;
+  const int p = (int)(task - bh * a.mk_pad);
+  int j = -1;   // pooled block of the row
+  if (p < a.nb_s) {
+    j = p;
+  } else if (p < a.mk) {
+    const int c = a.kept[bh * a.kc + (p - a.nb_s)];
+    j = (c >= 0 && c < a.nb_c) ? a.nb_s + c : -1;   // (always, for a well-formed list)
+  }
+  float v[EPC], k[EPC];
+  int rows = 0;
+  if (j >= 0) {
+    int r0;
+    block_rows(a, j, &r0, &rows);
+    const float* vb = a.vbar + (bh * a.M + j) * D;
+    if (j >= a.nb_s) {
+      float acc[EPC];
+      pool_rows<T, D>((const char*)a.V + ((bh * a.Nk + r0) * D) * ES, rows, acc);
+      const float n = (float)rows;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) v[e] = acc[e] / n;
+      if (lane < CPR) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ((float*)vb)[lane * EPC + e] = v[e];
+      }
+    } else if (lane < CPR) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) v[e] = vb[lane * EPC + e];
+    }
+    if (lane < CPR) {
+      const float* kb = a.kbar + (bh * a.M + j) * D;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) k[e] = kb[lane * EPC + e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) v[e] = k[e] = 0.f;
+  }
+  if (lane < CPR) {
+    const long long dst = (bh * a.mk_pad + p) * D + lane * EPC;
+    if constexpr (ES == 2) {
+      u32x4 hi, lo, vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16_t h0 = to_bf16(k[2 * e]), h1 = to_bf16(k[2 * e + 1]);
+        hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[e] = pack_bf16x2(k[2 * e] - to_f32(h0), k[2 * e + 1] - to_f32(h1));
+        vv[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+      }
+      *(u32x4*)((bf16_t*)a.pkhi + dst) = hi;
+      *(u32x4*)(a.pklo + dst) = lo;
+      *(u32x4*)((bf16_t*)a.pv + dst) = vv;
+    } else {
+      *(f32x4*)((float*)a.pkhi + dst) = f32x4{k[0], k[1], k[2], k[3]};
+      *(f32x4*)((float*)a.pv + dst) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  if (lane == 0) {
+    float bias = -INFINITY;
+    if (j >= 0) {
+      const int n = j < a.nb_s ? (j == a.nb_s - 1 ? a.tail_s : a.b) : ((j - a.nb_s) == a.nb_c - 1 ? a.tail_c : a.b);
+      bias = log2f((float)n);
+    }
+    a.pbias[bh * a.mk_pad + p] = bias;
+  }
+}
+
+static PoolArgs pool_args(const Layout& L, const Bufs& B) {
   PoolArgs a;
   a.Q = B.Q; a.K = B.K; a.V = B.V;
   a.qbar = (float*)(B.ws + L.off_qbar);
   a.kbar = (float*)(B.ws + L.off_kbar);
   a.vbar = (float*)(B.ws + L.off_vbar);
   a.kept = (const int*)(B.ws + L.off_kept);
+  a.pkhi = B.ws + L.off_pkhi;
+  a.pklo = (bf16_t*)(B.ws + L.off_pklo);
+  a.pv = B.ws + L.off_pv;
+  a.pbias = (float*)(B.ws + L.off_pbias);
   a.Ns = L.Ns; a.Nc = L.Nc; a.Nk = L.Nk; a.b = L.b;
-  a.nb_s = L.nb_s; a.nb_c = L.nb_c; a.M = L.M; a.kc = L.kc;
-  a.pass = pass;
-  a.tasks_per_head = pass == 0 ? (2 * L.nb_s + L.M) : L.kc;
+  a.nb_s = L.nb_s; a.nb_c = L.nb_c; a.M = L.M; a.kc = L.kc; a.mk = L.mk; a.mk_pad = L.mk_pad;
+  a.tail_s = L.tail_s; a.tail_c = L.tail_c;
+  return a;
+}
+
+template <typename T, int D>
+static hipError_t launch_pool_t(const Layout& L, const Bufs& B, bool pack, hipStream_t s) {
+  PoolArgs a = pool_args(L, B);
+  a.tasks_per_head = pack ? L.mk_pad : 2 * L.nb_s + L.M;
   a.total_tasks = (long long)a.tasks_per_head * L.BH;
   if (a.total_tasks == 0) return hipSuccess;
   const long long grid = (a.total_tasks + 3) / 4;
-  hipLaunchKernelGGL((isa_pool_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (pack) hipLaunchKernelGGL((isa_pool_pack_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((isa_pool_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_pool(const Layout& L, const Bufs& B, int pass, hipStream_t s) {
-  if (L.es == 2) return L.d == 128 ? launch_pool_t<bf16_t, 128>(L, B, pass, s) : launch_pool_t<bf16_t, 64>(L, B, pass, s);
-  return L.d == 128 ? launch_pool_t<float, 128>(L, B, pass, s) : launch_pool_t<float, 64>(L, B, pass, s);
+static hipError_t launch_pool_any(const Layout& L, const Bufs& B, bool pack, hipStream_t s) {
+  if (L.es == 2) return L.d == 128 ? launch_pool_t<bf16_t, 128>(L, B, pack, s) : launch_pool_t<bf16_t, 64>(L, B, pack, s);
+  return L.d == 128 ? launch_pool_t<float, 128>(L, B, pack, s) : launch_pool_t<float, 64>(L, B, pack, s);
 }
+
+hipError_t launch_pool(const Layout& L, const Bufs& B, hipStream_t s) { return launch_pool_any(L, B, false, s); }
+
+hipError_t launch_pool_pack(const Layout& L, const Bufs& B, hipStream_t s) { return launch_pool_any(L, B, true, s); }
 
 }  // namespace isa

@@ -318,84 +318,4 @@ hipError_t launch_select_q(const Layout& L, const Bufs& B, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Packing of the kept key set for the pooled (Taylor / sharpness) attention:
-// row p < nb_s is source block p, row nb_s + i is context block kept[i],
-// rows mk..mk_pad-1 are zero with bias -inf.  The bias is log2(n_j), the
-// count weight of the n-weighted softmax in the exp2 domain.  bf16 inputs
-// store each pooled key as hi = bf16(k) and lo = bf16(k - hi): the two
-// bf16 products with a bf16 query carry the logit to about 2^-17 relative,
-// well inside what the sharpness selection needs.
-
-struct PackArgs {
-  const float* kbar;
-  const float* vbar;
-  const int* kept;
-  void* pkhi;
-  bf16_t* pklo;
-  void* pv;
-  float* pbias;
-  int nb_s, nb_c, M, kc, mk, mk_pad, b, tail_s, tail_c;
-};
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void isa_pack_kernel(PackArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long long bh = blockIdx.y;
-  if (p >= a.mk_pad) return;
-  int j = -1;
-  if (p < a.nb_s) j = p;
-  else if (p < a.mk) {
-    const int c = a.kept[bh * a.kc + (p - a.nb_s)];
-    j = (c >= 0 && c < a.nb_c) ? a.nb_s + c : -1;
-  }
-  const long long src = (bh * a.M + (j < 0 ? 0 : j)) * D;
-  const long long dst = (bh * a.mk_pad + p) * D;
-  for (int e = lane; e < D; e += 64) {
-    const float k = j >= 0 ? a.kbar[src + e] : 0.f;
-    const float v = j >= 0 ? a.vbar[src + e] : 0.f;
-    if constexpr (sizeof(T) == 2) {
-      const bf16_t hi = to_bf16(k);
-      ((bf16_t*)a.pkhi)[dst + e] = hi;
-      a.pklo[dst + e] = to_bf16(k - to_f32(hi));
-      ((bf16_t*)a.pv)[dst + e] = to_bf16(v);
-    } else {
-      ((float*)a.pkhi)[dst + e] = k;
-      ((float*)a.pv)[dst + e] = v;
-    }
-  }
-  if (lane == 0) {
-    float bias = -INFINITY;
-    if (j >= 0) {
-      int n;
-      if (j < a.nb_s) n = j == a.nb_s - 1 ? a.tail_s : a.b;
-      else n = (j - a.nb_s) == a.nb_c - 1 ? a.tail_c : a.b;
-      bias = log2f((float)n);
-    }
-    a.pbias[bh * a.mk_pad + p] = bias;
-  }
-}
-
-template <typename T, int D>
-static hipError_t launch_pack_t(const Layout& L, const Bufs& B, hipStream_t s) {
-  PackArgs a;
-  a.kbar = (const float*)(B.ws + L.off_kbar);
-  a.vbar = (const float*)(B.ws + L.off_vbar);
-  a.kept = (const int*)(B.ws + L.off_kept);
-  a.pkhi = B.ws + L.off_pkhi;
-  a.pklo = (bf16_t*)(B.ws + L.off_pklo);
-  a.pv = B.ws + L.off_pv;
-  a.pbias = (float*)(B.ws + L.off_pbias);
-  a.nb_s = L.nb_s; a.nb_c = L.nb_c; a.M = L.M; a.kc = L.kc; a.mk = L.mk; a.mk_pad = L.mk_pad;
-  a.b = L.b; a.tail_s = L.tail_s; a.tail_c = L.tail_c;
-  hipLaunchKernelGGL((isa_pack_kernel<T, D>), dim3((L.mk_pad + 3) / 4, (unsigned)L.BH), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_pack(const Layout& L, const Bufs& B, hipStream_t s) {
-  if (L.es == 2) return L.d == 128 ? launch_pack_t<bf16_t, 128>(L, B, s) : launch_pack_t<bf16_t, 64>(L, B, s);
-  return L.d == 128 ? launch_pack_t<float, 128>(L, B, s) : launch_pack_t<float, 64>(L, B, s);
-}
-
 }  // namespace isa
