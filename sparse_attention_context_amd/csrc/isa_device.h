@@ -103,6 +103,36 @@ __device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned vo
                : "memory");
 }
 
+// Swizzle of the 256-byte LDS rows of the ping-pong kernels: 16-byte chunk
+// c of row r sits at chunk c ^ lds_swz(r).
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Two direct loads of 16 bytes per lane from base + v0 / v1 into LDS at
+// l0 / l1 + 16 x lane, in one asm block; waited for by count.
+__device__ __forceinline__ void dma16x2(unsigned l0, unsigned l1, const void* base, unsigned v0, unsigned v1) {
+  unsigned saved;  // m0 is restored, so the asm leaves no register changed behind the compiler's back
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(l0), "s"(l1), "v"(v0), "v"(v1), "s"(base)
+      : "memory");
+}
+
+// Issue order of a fused X phase (NPV P.V MFMAs with two operand reads each,
+// then NQK K.Q^T MFMAs with one): the reads of MFMAs 0..LA-1, then each MFMA
+// followed by the reads of the MFMA LA places later.
+template <int LA, int NPV = 16, int NQK = 16, int M = 0>
+__device__ __forceinline__ void pp_issue_order() {
+  constexpr int kMFMA = 0x8, kDSR = 0x100;
+  if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kDSR, LA <= NPV ? 2 * LA : NPV + LA, 0);
+  __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+  if constexpr (M + LA < NPV + NQK) __builtin_amdgcn_sched_group_barrier(kDSR, M + LA < NPV ? 2 : 1, 0);
+  if constexpr (M + 1 < NPV + NQK) pp_issue_order<LA, NPV, NQK, M + 1>();
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup id remap so that consecutive logical workgroups (which share a
 // head's keys) land on the same XCD: the hardware deals workgroups to the

@@ -430,35 +430,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 // distinct banks.  Operand addresses are per-lane offsets computed once.
 // Numerics are those of isa_flash_kernel: the same per-row reference max,
 // sums and bf16 roundings.
-__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// Four direct loads of 16 bytes per lane: rows of K at kbase + kv0/kv1 into
-// LDS at lk0/lk1 + 16 x lane, rows of V at vbase + vv0/vv1 into lv0/lv1.  One
-// asm block, so every offset (and the row-table values behind it) is ready
-// before the first load is issued; the loads are waited for by count.
-__device__ __forceinline__ void dma16x2(unsigned l0, unsigned l1, const void* base, unsigned v0, unsigned v1) {
-  unsigned saved;  // m0 is restored, so the asm leaves no register changed behind the compiler's back
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
-      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %5\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(l0), "s"(l1), "v"(v0), "v"(v1), "s"(base)
-      : "memory");
-}
-
-// Issue order of a fused X phase (NPV P.V MFMAs with two operand reads each,
-// then NQK K.Q^T MFMAs with one): the reads of MFMAs 0..LA-1, then each MFMA
-// followed by the reads of the MFMA LA places later.
-template <int LA, int NPV = 16, int NQK = 16, int M = 0>
-__device__ __forceinline__ void pp_issue_order() {
-  constexpr int kMFMA = 0x8, kDSR = 0x100;
-  if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kDSR, LA <= NPV ? 2 * LA : NPV + LA, 0);
-  __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
-  if constexpr (M + LA < NPV + NQK) __builtin_amdgcn_sched_group_barrier(kDSR, M + LA < NPV ? 2 : 1, 0);
-  if constexpr (M + 1 < NPV + NQK) pp_issue_order<LA, NPV, NQK, M + 1>();
-}
+// (lds_swz, dma16x2 and pp_issue_order are in isa_device.h)
 
 template <int KM, int RM>
 __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {

@@ -41,6 +41,11 @@
 
 namespace isa {
 
+#ifndef ISA_BWD_DV_PP
+#define ISA_BWD_DV_PP 1
+#endif
+constexpr bool kUseDvPP = ISA_BWD_DV_PP;
+
 static_assert(kFlashRows == 256, "the dQ kernel and its merge use 256-row tiles");
 
 struct BwdArgs {
@@ -76,17 +81,39 @@ struct BwdArgs {
   long long BH;
   float scale_log2;      // log2(e)/sqrt(d)
   float inv_sqrt_d;
+  const int* key_rows;   // [BH][n_keytab] row of every full-route key (0 for padding)
+  int n_keytab;
+  int* rrow;             // [BH][n_rowtab] full route in row order: source row (0 for padding),
+  float* rlse;           //   log-sum-exp (+inf for padding) and
+  float* rdel;           //   D (0 for padding)
+  int n_rowtab;
+  long long delta_wgs;   // workgroups of the delta launch that cover the source rows
 };
 
 // ---------------------------------------------------------------------------
 // D_i = dO_i . O_i, 8 elements per lane, D/8 lanes per row.
 
+// Workgroups past delta_wgs write the full route in row order (rrow, rlse,
+// rdel: one entry per virtual row, padding to whole tiles of 64), with D
+// formed by the same code as for the source rows.
 template <int D>
 __global__ __launch_bounds__(256) void isa_bwd_delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8, RPB = 256 / LPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
   const int e = (threadIdx.x % LPR) * 8;
-  const bool ok = row < a.BH * a.Ns;
+  long long row;
+  bool ok;
+  long long rv = -1;   // route entry (bh * n_rowtab + v) of the route workgroups
+  if ((long long)blockIdx.x < a.delta_wgs) {
+    row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    ok = row < a.BH * a.Ns;
+  } else {
+    rv = ((long long)blockIdx.x - a.delta_wgs) * RPB + threadIdx.x / LPR;
+    const long long bh = rv / a.n_rowtab;
+    const int r = bh < a.BH ? route_row(a.q_list + bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, rv - bh * a.n_rowtab) : -1;
+    ok = r >= 0;
+    row = bh * a.Ns + (r < 0 ? 0 : r);
+    if (bh >= a.BH) rv = -1;
+  }
   float s = 0.f;
   if (ok) {
     const u32x4 o = *(const u32x4*)((const bf16_t*)a.O + row * D + e);
@@ -98,7 +125,14 @@ __global__ __launch_bounds__(256) void isa_bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
-  if (ok && e == 0) a.delta[row] = s;
+  if (rv < 0) {
+    if (ok && e == 0) a.delta[row] = s;
+  } else if (e == 0) {
+    const long long bh = rv / a.n_rowtab;
+    a.rrow[rv] = ok ? (int)(row - bh * a.Ns) : 0;
+    a.rlse[rv] = ok ? a.lse[row] : INFINITY;
+    a.rdel[rv] = ok ? s : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -557,6 +591,256 @@ __global__ __launch_bounds__(512) void isa_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dV of the full route at d = 128 on the ping-pong schedule of the forward
+// flash kernel, with the roles of rows and keys exchanged: a workgroup holds
+// 256 keys (8 waves x 32, one key per lane, K of the key in registers) and
+// streams the route's rows in tiles of 64; Q and dO tiles come by direct
+// loads into four-stage LDS rings (swizzled rows, as in the forward), their
+// source rows and log-sum-exps from the row-ordered route arrays.
+//   X_j  dV^T += dO(j-1)^T P(j-1), then S(j) = Q(j) K^T      (MFMA)
+//   Y_j  loads of Q(j+3), dO(j+2), lse(j+3) and the row table of tile j+6;
+//        P(j) = exp2(S(j) log2(e)/sqrt(d) - lse) in bf16       (VALU)
+// Group 0 (waves 0-3) runs X_j in phase 2j and Y_j in 2j+1, group 1 one
+// phase later; a stage is refilled only after the last read of its previous
+// tile, and every tile is in LDS two phases before its first read (the
+// phase arithmetic of the forward kernel, with Q in the place of K and dO
+// in the place of V).  The lse tile of step t is loaded by wave 0 in Y_{t-3}
+// into slot t % 4 and read in Y_t by both groups.  Padding rows have
+// lse = +inf (p = 0).  The arithmetic is that of isa_bwd_dkdv_kernel.
+#ifndef ISA_BWD_LOOKAHEAD
+#define ISA_BWD_LOOKAHEAD 5
+#endif
+__global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
+  typedef bf16x8 Op;
+  constexpr int D = 128, BN = 64, NST = 4, ES = 2;
+  constexpr int RB = D * 2, TB = BN * RB, NT = D / 32;
+  static_assert(kBwdKeys == 256, "keys per workgroup");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TB];   // Q ring, then dO ring
+  __shared__ __attribute__((aligned(16))) int stab[8][4][64];         // per-wave row-table ring
+  __shared__ __attribute__((aligned(256))) float slse[NST][BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int lid = xcd_remap(blockIdx.x, a.n_wg);
+  const int bh = lid / a.key_tiles;
+  const int kt = lid - bh * a.key_tiles;
+
+  // ---- this lane's key: row of K/V and validity (as isa_bwd_dkdv_kernel)
+  const int kv = kt * kBwdKeys + w * 32 + l32;
+  const int n_keys = a.Ns + (int)a.ctx_tok;
+  int krow;
+  if (kv < a.Ns) krow = kv;
+  else if (kv < n_keys) krow = a.ctx_rows[(long long)bh * a.ctx_tok + (kv - a.Ns)];
+  else krow = -1;
+  const bool kvalid = krow >= 0;
+  krow = kvalid ? krow : 0;
+  Op kB[D / 16];
+  {
+    const char* Kg = (const char*)a.K + ((long long)bh * a.Nk + krow) * RB;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kB[s] = *(const Op*)(Kg + (16 * s + 8 * h) * ES);
+  }
+
+  const int nt = a.n_rowtab / BN;   // row tiles of the route
+  const char* Qg = (const char*)a.Q + (long long)bh * a.Ns * RB;
+  const char* Gg = (const char*)a.dO + (long long)bh * a.Ns * RB;
+  const int* tab = a.rrow + (long long)bh * a.n_rowtab;
+  const float* lseg = a.rlse + (long long)bh * a.n_rowtab;
+
+  // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
+  // tile; the row-table entries of its 8 rows of tile t come to slot t % 4 of
+  // its LDS ring by a direct load in step t-6 and are read in step t-4.
+  const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
+  struct Rows { int r[2]; };
+  const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
+                          __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
+  auto fetch_rows = [&](int j, int tile) {
+    const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
+    dma4(stab_w + (unsigned)(j & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)(tile * BN + 32 * grp + 8 * wg + k) * 4u);
+  };
+  auto rows_of = [&](int j) -> Rows {
+    const int2 v = *(const int2*)&stab[w][j & 3][2 * (lane >> 4)];
+    return Rows{{v.x, v.y}};
+  };
+  const unsigned lds_q = (unsigned)(size_t)(lds_char*)smem;
+  const unsigned lds_g = lds_q + NST * TB;
+  const unsigned lds_l = (unsigned)(size_t)(lds_char*)&slse[0][0];
+  unsigned lchunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
+  const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows) {
+    const unsigned d0 = ring + wrow + (unsigned)stage * TB;
+    dma16x2(d0, d0 + 4 * RB, base, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+  };
+  auto issue_lse = [&](int slot, int tile) {
+    if (w == 0) dma4(lds_l + (unsigned)slot * BN * 4, lseg + tile * BN, (unsigned)lane * 4u);
+  };
+
+  // operand offsets (as the forward kernel): Q row 32*ti + l32, chunk 2s + h;
+  // dO^T transpose reads at rows 16s + 4h + m/4 (+8), d = 32t + 16(g%2) + 4(m%4)
+  int koff[8], voff[NT][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int m = lane & 15;
+      const int kr = 4 * h + (m >> 2) + 8 * hi;
+      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+      voff[t][hi] = NST * TB + kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
+    }
+
+  struct STile { f32x16 t[2]; };
+  struct PTile { Op p[4]; };
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  const float sc = a.scale_log2;
+
+  // X phase: 16 MFMAs of dO^T P, then 16 of Q K^T, reads LA MFMAs ahead
+  auto x_phase = [&](int gstage, const PTile& P, int qstage) -> STile {
+    constexpr int LA = ISA_BWD_LOOKAHEAD;
+    const lds_char* Gs = (const lds_char*)smem + gstage * TB;
+    const lds_char* Qs = (const lds_char*)smem + qstage * TB;
+    Op opv[16], opk[16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Gs + voff[t][0] + 16 * q * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Gs + voff[t][1] + 16 * q * RB));
+        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) opk[2 * q + ti] = *(const Op*)(Qs + koff[q] + 32 * ti * RB);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], P.p[m & 3], acc[m >> 2]);
+    STile S;
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) S.t[m & 1] = mma32(opk[m], kB[m >> 1], S.t[m & 1]);
+    pp_issue_order<LA>();
+    return S;
+  };
+  // P = exp2(S sc - lse_row); rows of reg r of tile ti: 32 ti + 8 (r/4) + 4h + r%4
+  auto probs = [&](int slot, const STile& S) -> PTile {
+    PTile P;
+    const float* ls = slse[slot];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const f32x4*)(ls + 32 * ti + 8 * g + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          P.p[2 * ti + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S.t[ti][r], sc, -l4[e]));
+        }
+      }
+    return P;
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto cl = [&](int j) { return min(j, nt - 1); };
+  if (nt > 0) {
+    Rows rk, rv;   // rows of tiles j+3 (Q) and j+2 (dO) entering step j
+    {
+      fetch_rows(cl(0), cl(0));
+      fetch_rows(cl(1), cl(1));
+      fetch_rows(cl(2), cl(2));
+      fetch_rows(cl(3), cl(3));
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+      const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1));
+      rv = rows_of(cl(2));
+      rk = rows_of(cl(3));
+      issue_tile(lds_q, 0, Qg, r0);
+      issue_tile(lds_g, 0, Gg, r0);
+      issue_tile(lds_q, 1, Qg, r1);
+      issue_tile(lds_g, 1, Gg, r1);
+      issue_tile(lds_q, 2, Qg, rv);   // (dO(2) is loaded by the first step)
+      issue_lse(0, cl(0));
+      issue_lse(1, cl(1));
+      issue_lse(2, cl(2));
+      fetch_rows(cl(4), cl(4));
+      fetch_rows(cl(5), cl(5));
+      // dO stage 3 is first loaded in step 1; step 0 reads it as zeros
+      u32x4* vz = (u32x4*)(smem + NST * TB + 3 * TB);
+#pragma unroll
+      for (int q = 0; q < TB / (16 * 512); ++q) vz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    }
+    phase_barrier();
+    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+    STile S = {};
+    PTile P = {};
+    auto step = [&](int j) {
+      const int Z = j & 3;
+      __builtin_amdgcn_s_setprio(3);
+      S = x_phase((Z + 3) & 3, P, Z);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+      // Y_j
+      issue_tile(lds_q, (Z + 3) & 3, Qg, rk);
+      issue_tile(lds_g, (Z + 2) & 3, Gg, rv);
+      issue_lse((Z + 3) & 3, cl(j + 3));
+      const Rows rn = rows_of(cl(j + 4));
+      fetch_rows(cl(j + 6), cl(j + 6));
+      if (j < nt) P = probs(Z, S);
+      rv = rk;
+      rk = rn;
+      // the loads of Y_{j-1} have landed before the barrier that closes Y_j
+      if (w == 0) __builtin_amdgcn_s_waitcnt(0x0f76);   // vmcnt(6)
+      else __builtin_amdgcn_s_waitcnt(0x0f75);          // vmcnt(5)
+      phase_barrier();
+    };
+    for (int j = 0; j <= nt; ++j) step(j);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+  }
+
+  // ---- epilogue: dV of the key plus the pooled share of its block (as
+  // isa_bwd_dkdv_kernel); lane holds key kv, d = 32 t + 8 g + 4 h + e
+  if (!kvalid) return;
+  int j, n;
+  if (kv < a.Ns) {
+    j = kv / a.b;
+    n = j == a.nb_s - 1 ? a.tail_s : a.b;
+  } else {
+    const int u = (kv - a.Ns) / a.b;
+    j = a.nb_s + u;
+    n = a.kept[(long long)bh * a.kc + u] == a.nb_c - 1 ? a.tail_c : a.b;
+  }
+  const float inv_n = 1.0f / (float)n;
+  const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D + D;
+  bf16_t* out = (bf16_t*)a.dV + ((long long)bh * a.Nk + krow) * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * t + 8 * g + 4 * h;
+      const f32x4 bb = *(const f32x4*)(pb + d0);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(acc[t][4 * g + e], 1.0f, bb[e] * inv_n);
+      *(u32x2*)(out + d0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+}
+
 // dkbar, dvbar = sum of the pooled partials over splits, in split order
 // (zero when there are no Taylor rows: nsplit = 0).
 template <int D>
@@ -616,6 +900,12 @@ static BwdArgs bwd_args(const Layout& L, const BwdLayout& W, const BwdBufs& B) {
   a.BH = L.BH;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)L.d));
   a.inv_sqrt_d = (float)(1.0 / sqrt((double)L.d));
+  a.key_rows = (const int*)(B.ws + L.off_keyrows);
+  a.n_keytab = L.n_keytab;
+  a.rrow = (int*)(B.bws + W.off_rrow);
+  a.rlse = (float*)(B.bws + W.off_rlse);
+  a.rdel = (float*)(B.bws + W.off_rdel);
+  a.n_rowtab = W.n_rowtab;
   return a;
 }
 
@@ -628,7 +918,10 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
     case BwdWhat::kDelta: {
       constexpr int RPB = 256 / (D / 8);
       const long long rows = L.BH * L.Ns;
-      hipLaunchKernelGGL((isa_bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
+      a.delta_wgs = (rows + RPB - 1) / RPB;
+      a.q_list = fullq; a.q_k = L.kq;
+      const long long rwgs = (L.BH * W.n_rowtab + RPB - 1) / RPB;
+      hipLaunchKernelGGL((isa_bwd_delta_kernel<D>), dim3((unsigned)(a.delta_wgs + rwgs)), dim3(256), 0, s, a);
       break;
     }
     case BwdWhat::kDkPooled:
@@ -659,6 +952,8 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       a.n_wg = (int)nwg;
       if (what == BwdWhat::kDkFull)
         hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, true>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+      else if (D == 128 && kUseDvPP)
+        hipLaunchKernelGGL(isa_bwd_dv_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
       else
         hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, false>), dim3((unsigned)nwg), dim3(512), 0, s, a);
       break;

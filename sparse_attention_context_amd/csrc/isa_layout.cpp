@@ -138,6 +138,10 @@ isa_status make_bwd_layout(const Layout& L, BwdLayout* B) {
     const int64_t prow = L.full_splits > 1 ? (int64_t)bh * ((L.full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L.full_splits : 0;
     take(&B->off_part_dq, prow * d * 4);
   }
+  B->n_rowtab = (int)((L.full_rows + 63) / 64 * 64);
+  take(&B->off_rrow, bh * (size_t)B->n_rowtab * 4);
+  take(&B->off_rlse, bh * (size_t)B->n_rowtab * 4);
+  take(&B->off_rdel, bh * (size_t)B->n_rowtab * 4);
   B->total = o;
   return ISA_OK;
 }

@@ -64,6 +64,10 @@ struct BwdLayout {
   size_t off_part_dkv; // [dkv_splits][BH][mk_pad][2][d] fp32 pooled-key gradient partials
   size_t off_dkvbar;   // [BH][mk_pad][2][d] fp32: pooled-key gradients (dkbar, dvbar)
   size_t off_part_dq;  // [BH][full row tiles * kFlashRows][full_splits][d] fp32 split-K partials of dQ
+  int n_rowtab;        // full-route virtual rows per head, rounded up to 64
+  size_t off_rrow;     // [BH][n_rowtab] int32: source row of each full-route row (0 for padding)
+  size_t off_rlse;     // [BH][n_rowtab] fp32: its forward log-sum-exp (+inf for padding)
+  size_t off_rdel;     // [BH][n_rowtab] fp32: its D = dO . O (0 for padding)
   size_t total;
 };
 
