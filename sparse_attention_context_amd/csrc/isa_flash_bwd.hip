@@ -45,6 +45,10 @@ namespace isa {
 #define ISA_BWD_DV_PP 1
 #endif
 constexpr bool kUseDvPP = ISA_BWD_DV_PP;
+#ifndef ISA_BWD_DK_PP
+#define ISA_BWD_DK_PP 1
+#endif
+constexpr bool kUseDkPP = ISA_BWD_DK_PP;
 
 static_assert(kFlashRows == 256, "the dQ kernel and its merge use 256-row tiles");
 
@@ -841,6 +845,262 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
     }
 }
 
+// dK of the full route at d = 128, on the schedule of isa_bwd_dv_pp_kernel
+// with K and V of the key in registers:
+//   X_j  dK^T += Q(j-1)^T dS(j-1), then S(j) = Q(j) K^T and dP(j) = dO(j) V^T
+//   Y_j  loads of Q(j+3), dO(j+3), lse and D of tile j+3 and the row table of
+//        tile j+6; dS(j) = P(j) (dP(j) - D) in bf16, P = exp2(S sc - lse)
+// Q(t) is read in X_t and X_{t+1}, so its ring has five stages (stage t % 5,
+// refilled in Y_{t-3} after the last read of Q(t-5) in X_{t-4}); dO(t) is
+// read in X_t only (four stages, as K in the forward kernel).  lse and D of
+// tile t come to slot t % 4 by waves 0 and 1 in Y_{t-3}.
+#ifndef ISA_BWD_DK_LOOKAHEAD
+#define ISA_BWD_DK_LOOKAHEAD 3
+#endif
+__global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
+  typedef bf16x8 Op;
+  constexpr int D = 128, BN = 64, NQ = 5, NG = 4, ES = 2;
+  constexpr int RB = D * 2, TB = BN * RB, NT = D / 32;
+  static_assert(kBwdKeys == 256, "keys per workgroup");
+
+  __shared__ __attribute__((aligned(1024))) char smem[(NQ + NG) * TB];   // Q ring, then dO ring
+  __shared__ __attribute__((aligned(16))) int stab[8][4][64];            // per-wave row-table ring
+  __shared__ __attribute__((aligned(256))) float sld[2][4][BN];          // lse, D rings
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int lid = xcd_remap(blockIdx.x, a.n_wg);
+  const int bh = lid / a.key_tiles;
+  const int kt = lid - bh * a.key_tiles;
+
+  // ---- this lane's key (as isa_bwd_dkdv_kernel)
+  const int kv = kt * kBwdKeys + w * 32 + l32;
+  const int n_keys = a.Ns + (int)a.ctx_tok;
+  int krow;
+  if (kv < a.Ns) krow = kv;
+  else if (kv < n_keys) krow = a.ctx_rows[(long long)bh * a.ctx_tok + (kv - a.Ns)];
+  else krow = -1;
+  const bool kvalid = krow >= 0;
+  krow = kvalid ? krow : 0;
+  Op kB[D / 16], vB[D / 16];
+  {
+    const char* Kg = (const char*)a.K + ((long long)bh * a.Nk + krow) * RB;
+    const char* Vg = (const char*)a.V + ((long long)bh * a.Nk + krow) * RB;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kB[s] = *(const Op*)(Kg + (16 * s + 8 * h) * ES);
+      vB[s] = *(const Op*)(Vg + (16 * s + 8 * h) * ES);
+    }
+  }
+
+  const int nt = a.n_rowtab / BN;
+  const char* Qg = (const char*)a.Q + (long long)bh * a.Ns * RB;
+  const char* Gg = (const char*)a.dO + (long long)bh * a.Ns * RB;
+  const int* tab = a.rrow + (long long)bh * a.n_rowtab;
+  const float* lseg = a.rlse + (long long)bh * a.n_rowtab;
+  const float* delg = a.rdel + (long long)bh * a.n_rowtab;
+
+  const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
+  struct Rows { int r[2]; };
+  const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
+                          __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
+  auto fetch_rows = [&](int j, int tile) {
+    const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
+    dma4(stab_w + (unsigned)(j & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)(tile * BN + 32 * grp + 8 * wg + k) * 4u);
+  };
+  auto rows_of = [&](int j) -> Rows {
+    const int2 v = *(const int2*)&stab[w][j & 3][2 * (lane >> 4)];
+    return Rows{{v.x, v.y}};
+  };
+  const unsigned lds_q = (unsigned)(size_t)(lds_char*)smem;
+  const unsigned lds_g = lds_q + NQ * TB;
+  const unsigned lds_ld = (unsigned)(size_t)(lds_char*)&sld[0][0][0];
+  unsigned lchunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
+  const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows) {
+    const unsigned d0 = ring + wrow + (unsigned)stage * TB;
+    dma16x2(d0, d0 + 4 * RB, base, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+  };
+  auto issue_ld = [&](int slot, int tile) {   // lse by wave 0, D by wave 1
+    if (w == 0) dma4(lds_ld + (unsigned)slot * BN * 4, lseg + tile * BN, (unsigned)lane * 4u);
+    if (w == 1) dma4(lds_ld + (unsigned)(4 + slot) * BN * 4, delg + tile * BN, (unsigned)lane * 4u);
+  };
+
+  // operand offsets within a tile: rows 32*ti + l32, chunk 2s + h (Q, dO);
+  // Q^T transpose reads at rows 16s + 4h + m/4 (+8), d = 32t + 16(g%2) + 4(m%4)
+  int koff[8], voff[NT][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int m = lane & 15;
+      const int kr = 4 * h + (m >> 2) + 8 * hi;
+      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+      voff[t][hi] = kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
+    }
+
+  struct STile { f32x16 t[2]; };
+  struct PTile { Op p[4]; };
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  const float sc = a.scale_log2;
+
+  // X phase: 16 MFMAs of Q^T dS, then 16 of Q K^T and 16 of dO V^T
+  auto x_phase = [&](int qprev, const PTile& dS, int qcur, int gcur, STile& S, STile& dP) {
+    constexpr int LA = ISA_BWD_DK_LOOKAHEAD;
+    const lds_char* Ts = (const lds_char*)smem + qprev * TB;
+    const lds_char* Qs = (const lds_char*)smem + qcur * TB;
+    const lds_char* Gs = (const lds_char*)smem + (NQ + gcur) * TB;
+    Op opv[16], opk[32];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ts + voff[t][0] + 16 * q * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ts + voff[t][1] + 16 * q * RB));
+        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        opk[2 * q + ti] = *(const Op*)(Qs + koff[q] + 32 * ti * RB);
+        opk[16 + 2 * q + ti] = *(const Op*)(Gs + koff[q] + 32 * ti * RB);
+      }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], dS.p[m & 3], acc[m >> 2]);
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+    dP.t[0] = f32x16{};
+    dP.t[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) S.t[m & 1] = mma32(opk[m], kB[m >> 1], S.t[m & 1]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) dP.t[m & 1] = mma32(opk[16 + m], vB[m >> 1], dP.t[m & 1]);
+    pp_issue_order<LA, 16, 32>();
+  };
+  // dS = P (dP - D), P = exp2(S sc - lse); rows of reg r of tile ti: 32 ti + 8 (r/4) + 4h + r%4
+  auto dsoft = [&](int slot, const STile& S, const STile& dP) -> PTile {
+    PTile dS;
+    const float* ls = sld[0][slot];
+    const float* ds = sld[1][slot];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const f32x4*)(ls + 32 * ti + 8 * g + 4 * h);
+        const f32x4 d4 = *(const f32x4*)(ds + 32 * ti + 8 * g + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(S.t[ti][r], sc, -l4[e]));
+          dS.p[2 * ti + (r >> 3)][r & 7] = (__bf16)(p * (dP.t[ti][r] - d4[e]));
+        }
+      }
+    return dS;
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto cl = [&](int j) { return min(j, nt - 1); };
+  if (nt > 0) {
+    Rows rk;   // rows of tile j+3 entering step j
+    {
+      fetch_rows(cl(0), cl(0));
+      fetch_rows(cl(1), cl(1));
+      fetch_rows(cl(2), cl(2));
+      fetch_rows(cl(3), cl(3));
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+      const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1)), r2 = rows_of(cl(2));
+      rk = rows_of(cl(3));
+      issue_tile(lds_q, 0, Qg, r0);
+      issue_tile(lds_g, 0, Gg, r0);
+      issue_tile(lds_q, 1, Qg, r1);
+      issue_tile(lds_g, 1, Gg, r1);
+      issue_tile(lds_q, 2, Qg, r2);
+      issue_tile(lds_g, 2, Gg, r2);
+      issue_ld(0, cl(0));
+      issue_ld(1, cl(1));
+      issue_ld(2, cl(2));
+      fetch_rows(cl(4), cl(4));
+      fetch_rows(cl(5), cl(5));
+      // Q stage 4 is first loaded in step 1; step 0 reads it as zeros
+      u32x4* qz = (u32x4*)(smem + 4 * TB);
+#pragma unroll
+      for (int q = 0; q < TB / (16 * 512); ++q) qz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    }
+    phase_barrier();
+    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+    STile S = {}, dP = {};
+    PTile dS = {};
+    int q_prev = 4, q_cur = 0;   // Q stages of tiles j-1 and j
+    for (int j = 0; j <= nt; ++j) {
+      const int Z = j & 3;
+      __builtin_amdgcn_s_setprio(3);
+      x_phase(q_prev, dS, q_cur, Z, S, dP);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+      // Y_j
+      const int q3 = q_cur + 3 < NQ ? q_cur + 3 : q_cur + 3 - NQ;   // (j + 3) % 5
+      issue_tile(lds_q, q3, Qg, rk);
+      issue_tile(lds_g, (Z + 3) & 3, Gg, rk);
+      issue_ld((Z + 3) & 3, cl(j + 3));
+      const Rows rn = rows_of(cl(j + 4));
+      fetch_rows(cl(j + 6), cl(j + 6));
+      if (j < nt) dS = dsoft(Z, S, dP);
+      rk = rn;
+      q_prev = q_cur;
+      q_cur = q_cur + 1 < NQ ? q_cur + 1 : 0;
+      // the loads of Y_{j-1} have landed before the barrier that closes Y_j
+      if (w < 2) __builtin_amdgcn_s_waitcnt(0x0f76);   // vmcnt(6)
+      else __builtin_amdgcn_s_waitcnt(0x0f75);         // vmcnt(5)
+      phase_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+  }
+
+  // ---- epilogue: dK of the key (scaled by 1/sqrt d) plus the pooled share
+  // of its block (as isa_bwd_dkdv_kernel); lane holds key kv, d = 32 t + 8 g + 4 h + e
+  if (!kvalid) return;
+  int j, n;
+  if (kv < a.Ns) {
+    j = kv / a.b;
+    n = j == a.nb_s - 1 ? a.tail_s : a.b;
+  } else {
+    const int u = (kv - a.Ns) / a.b;
+    j = a.nb_s + u;
+    n = a.kept[(long long)bh * a.kc + u] == a.nb_c - 1 ? a.tail_c : a.b;
+  }
+  const float inv_n = 1.0f / (float)n;
+  const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D;
+  bf16_t* out = (bf16_t*)a.dK + ((long long)bh * a.Nk + krow) * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * t + 8 * g + 4 * h;
+      const f32x4 bb = *(const f32x4*)(pb + d0);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(acc[t][4 * g + e], a.inv_sqrt_d, bb[e] * inv_n);
+      *(u32x2*)(out + d0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+}
+
 // dkbar, dvbar = sum of the pooled partials over splits, in split order
 // (zero when there are no Taylor rows: nsplit = 0).
 template <int D>
@@ -950,7 +1210,9 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       a.key_tiles = (int)((L.Ns + L.ctx_tok + kBwdKeys - 1) / kBwdKeys);
       const long long nwg = L.BH * a.key_tiles;
       a.n_wg = (int)nwg;
-      if (what == BwdWhat::kDkFull)
+      if (what == BwdWhat::kDkFull && D == 128 && kUseDkPP)
+        hipLaunchKernelGGL(isa_bwd_dk_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
+      else if (what == BwdWhat::kDkFull)
         hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, true>), dim3((unsigned)nwg), dim3(512), 0, s, a);
       else if (D == 128 && kUseDvPP)
         hipLaunchKernelGGL(isa_bwd_dv_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
