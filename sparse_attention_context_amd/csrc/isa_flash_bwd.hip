@@ -49,6 +49,10 @@ constexpr bool kUseDvPP = ISA_BWD_DV_PP;
 #define ISA_BWD_DK_PP 1
 #endif
 constexpr bool kUseDkPP = ISA_BWD_DK_PP;
+#ifndef ISA_BWD_DQ_PP
+#define ISA_BWD_DQ_PP 1
+#endif
+constexpr bool kUseDqPP = ISA_BWD_DQ_PP;
 
 static_assert(kFlashRows == 256, "the dQ kernel and its merge use 256-row tiles");
 
@@ -1101,6 +1105,254 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
     }
 }
 
+// dQ of the full route at d = 128 on the ping-pong schedule of the forward
+// flash kernel (rows fixed: 8 waves x 32 query rows, Q, dO, lse and D of
+// the row in registers; key tiles of 64 streamed, split-K as the forward):
+//   X_j  dQ^T += K(j-1)^T dS(j-1)^T, then S(j)^T = K(j) Q^T and
+//        dP(j)^T = V(j) dO^T
+//   Y_j  loads of K(j+3), V(j+3) and the key-row table of tile j+6;
+//        dS = P (dP - D), P = exp2(S log2(e)/sqrt(d) - lse) (one fma, as the
+//        dK and dV kernels; isa_bwd_dq_kernel rounds the product first),
+//        keys past the route's last valid key masked
+// K(t) is read in X_t and X_{t+1} (five-stage ring, as Q in the dK kernel);
+// V(t) in X_t only (four stages).
+#ifndef ISA_BWD_DQ_LOOKAHEAD
+#define ISA_BWD_DQ_LOOKAHEAD 3
+#endif
+__global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
+  typedef bf16x8 Op;
+  constexpr int D = 128, BN = 64, BM = 256, NK = 5, NV = 4, ES = 2;
+  constexpr int RB = D * 2, TB = BN * RB, NT = D / 32;
+  static_assert(BM == kFlashRows, "tile mapping");
+
+  __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * TB];   // K ring, then V ring
+  __shared__ __attribute__((aligned(16))) int stab[8][4][64];            // per-wave key-table ring
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int lid = xcd_remap(blockIdx.x, a.n_wg);
+  const int split = lid % a.nsplit;
+  const int rest = lid / a.nsplit;
+  const int bh = rest / a.row_tiles;
+  const int rt = rest - bh * a.row_tiles;
+
+  const long long vrow = (long long)rt * BM + w * 32 + l32;
+  const int qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
+  Op qB[D / 16], gB[D / 16];
+  float lse_r = INFINITY, del_r = 0.f;  // rows off the route: p = 0
+  {
+    const long long r = (long long)bh * a.Ns + (qrow < 0 ? 0 : qrow);
+    const bf16_t* qp = (const bf16_t*)a.Q + r * D + 8 * h;
+    const bf16_t* gp = (const bf16_t*)a.dO + r * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qB[s] = *(const Op*)(qp + 16 * s);
+      gB[s] = *(const Op*)(gp + 16 * s);
+    }
+    if (qrow >= 0) {
+      lse_r = a.lse[r];
+      del_r = a.delta[r];
+    }
+  }
+
+  const int n_keys = a.Ns + (int)a.ctx_tok;
+  const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
+  const int n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
+  const int ntiles = (n_keys + BN - 1) / BN;
+  const int t_begin = split * a.tiles_per_split;
+  const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
+
+  const char* Kg = (const char*)a.K + (long long)bh * a.Nk * RB;
+  const char* Vg = (const char*)a.V + (long long)bh * a.Nk * RB;
+  const int* tab = a.key_rows + (long long)bh * a.n_keytab;
+
+  const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
+  struct Rows { int r[2]; };
+  const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
+                          __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
+  auto fetch_rows = [&](int j, int tile) {
+    const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
+    dma4(stab_w + (unsigned)(j & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)(tile * BN + 32 * grp + 8 * wg + k) * 4u);
+  };
+  auto rows_of = [&](int j) -> Rows {
+    const int2 v = *(const int2*)&stab[w][j & 3][2 * (lane >> 4)];
+    return Rows{{v.x, v.y}};
+  };
+  const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
+  const unsigned lds_v = lds_k + NK * TB;
+  unsigned lchunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
+  const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows) {
+    const unsigned d0 = ring + wrow + (unsigned)stage * TB;
+    dma16x2(d0, d0 + 4 * RB, base, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+  };
+
+  int koff[8], voff[NT][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int m = lane & 15;
+      const int kr = 4 * h + (m >> 2) + 8 * hi;
+      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+      voff[t][hi] = kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
+    }
+
+  struct STile { f32x16 t[2]; };
+  struct PTile { Op p[4]; };
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  const float sc = a.scale_log2;
+
+  auto x_phase = [&](int kprev, const PTile& dS, int kcur, int vcur, STile& S, STile& dP) {
+    constexpr int LA = ISA_BWD_DQ_LOOKAHEAD;
+    const lds_char* Ts = (const lds_char*)smem + kprev * TB;
+    const lds_char* Ks = (const lds_char*)smem + kcur * TB;
+    const lds_char* Vs = (const lds_char*)smem + (NK + vcur) * TB;
+    Op opv[16], opk[32];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ts + voff[t][0] + 16 * q * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ts + voff[t][1] + 16 * q * RB));
+        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        opk[2 * q + ti] = *(const Op*)(Ks + koff[q] + 32 * ti * RB);
+        opk[16 + 2 * q + ti] = *(const Op*)(Vs + koff[q] + 32 * ti * RB);
+      }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], dS.p[m & 3], acc[m >> 2]);
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+    dP.t[0] = f32x16{};
+    dP.t[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) S.t[m & 1] = mma32(opk[m], qB[m >> 1], S.t[m & 1]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) dP.t[m & 1] = mma32(opk[16 + m], gB[m >> 1], dP.t[m & 1]);
+    pp_issue_order<LA, 16, 32>();
+  };
+  // dS = P (dP - D) with P = exp2(S sc - lse); keys of reg r of tile ti:
+  // 32 ti + 8 (r/4) + 4h + r%4
+  auto dsoft = [&](int j, STile& S, const STile& dP) -> PTile {
+    const int t0 = (t_begin + j) * BN;
+    if (t0 + BN > n_valid) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t0 + 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) S.t[ti][r] = -INFINITY;
+    }
+    PTile dS;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(S.t[ti][r], sc, -lse_r));
+        dS.p[2 * ti + (r >> 3)][r & 7] = (__bf16)(p * (dP.t[ti][r] - del_r));
+      }
+    return dS;
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto cl = [&](int j) { return min(j, nt - 1); };
+  auto tl = [&](int j) { return t_begin + cl(j); };
+  if (nt > 0) {
+    Rows rk;   // rows of tile j+3 entering step j
+    {
+      fetch_rows(cl(0), tl(0));
+      fetch_rows(cl(1), tl(1));
+      fetch_rows(cl(2), tl(2));
+      fetch_rows(cl(3), tl(3));
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+      const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1)), r2 = rows_of(cl(2));
+      rk = rows_of(cl(3));
+      issue_tile(lds_k, 0, Kg, r0);
+      issue_tile(lds_v, 0, Vg, r0);
+      issue_tile(lds_k, 1, Kg, r1);
+      issue_tile(lds_v, 1, Vg, r1);
+      issue_tile(lds_k, 2, Kg, r2);
+      issue_tile(lds_v, 2, Vg, r2);
+      fetch_rows(cl(4), tl(4));
+      fetch_rows(cl(5), tl(5));
+      // K stage 4 is first loaded in step 1; step 0 reads it as zeros
+      u32x4* kz = (u32x4*)(smem + 4 * TB);
+#pragma unroll
+      for (int q = 0; q < TB / (16 * 512); ++q) kz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    }
+    phase_barrier();
+    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+    STile S = {}, dP = {};
+    PTile dS = {};
+    int k_prev = 4, k_cur = 0;   // K stages of tiles j-1 and j
+    for (int j = 0; j <= nt; ++j) {
+      const int Z = j & 3;
+      __builtin_amdgcn_s_setprio(3);
+      x_phase(k_prev, dS, k_cur, Z, S, dP);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+      // Y_j
+      const int k3 = k_cur + 3 < NK ? k_cur + 3 : k_cur + 3 - NK;   // (j + 3) % 5
+      issue_tile(lds_k, k3, Kg, rk);
+      issue_tile(lds_v, (Z + 3) & 3, Vg, rk);
+      const Rows rn = rows_of(cl(j + 4));
+      fetch_rows(cl(j + 6), tl(j + 6));
+      if (j < nt) dS = dsoft(j, S, dP);
+      rk = rn;
+      k_prev = k_cur;
+      k_cur = k_cur + 1 < NK ? k_cur + 1 : 0;
+      // the loads of Y_{j-1} have landed before the barrier that closes Y_j
+      __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
+      phase_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+  }
+
+  // ---- epilogue (as isa_bwd_dq_kernel)
+  if (qrow < 0 && a.nsplit == 1) return;
+  if (a.nsplit == 1) {
+    bf16_t* op = (bf16_t*)a.dQ + ((long long)bh * a.Ns + qrow) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& c = acc[t];
+        const float sd = a.inv_sqrt_d;
+        *(u32x2*)(op + 32 * t + 8 * g + 4 * h) = u32x2{pack_bf16x2(c[4 * g] * sd, c[4 * g + 1] * sd),
+                                                       pack_bf16x2(c[4 * g + 2] * sd, c[4 * g + 3] * sd)};
+      }
+  } else {
+    float* pp = a.part_dq + (((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& c = acc[t];
+        *(f32x4*)(pp + 32 * t + 8 * g + 4 * h) = f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+      }
+  }
+}
+
 // dkbar, dvbar = sum of the pooled partials over splits, in split order
 // (zero when there are no Taylor rows: nsplit = 0).
 template <int D>
@@ -1240,7 +1492,9 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       a.tiles_per_split = (ntiles + a.nsplit - 1) / a.nsplit;
       const long long nwg = (long long)a.row_tiles * L.BH * a.nsplit;
       a.n_wg = (int)nwg;
-      if (full)
+      if (full && D == 128 && kUseDqPP)
+        hipLaunchKernelGGL(isa_bwd_dq_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
+      else if (full)
         hipLaunchKernelGGL((isa_bwd_dq_kernel<D, false>), dim3((unsigned)nwg), dim3(512), 0, s, a);
       else
         hipLaunchKernelGGL((isa_bwd_dq_kernel<D, true>), dim3((unsigned)nwg), dim3(512), 0, s, a);

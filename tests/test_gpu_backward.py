@@ -72,6 +72,9 @@ CASES = [
     (1, 2, 128, 640, 577, 64, 1.0, 1.0),        # dense limit: no Taylor rows
     (1, 2, 128, 1000, 900, 200, 0.5, 0.5),      # short kept tail block inside a key tile
     (1, 1, 128, 3000, 2500, 64, 0.25, 0.2),     # several dQ splits and dK/dV key tiles
+    (1, 2, 128, 150, 100, 1, 0.4, 0.3),         # b = 1 at d = 128: route rows one by one
+    (1, 2, 128, 500, 0, 32, 0.5, 0.3),          # no context at d = 128
+    (1, 2, 128, 700, 630, 50, 1.0, 0.5),        # short last context block kept; row tiles straddle blocks
 ]
 
 
