@@ -191,8 +191,8 @@ def time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
     log("isa_backward: %.3f ms/call; stages: %s" % (ms, ", ".join("%s %.3f" % kv for kv in st.items())))
     pairs = full_route_flops(views, w, gamma) // (4 * w.d)
     # per (query, key) pair of the full route: dK kernel S, dP, dK (6 d); dV kernel S, dV (4 d); dQ kernel S, dP, dQ (6 d)
-    kernels = {"dk_full": ("isa_bwd_dkdv_kernel dK (full route)", 6), "dv_full": ("isa_bwd_dkdv_kernel dV (full route)", 4),
-               "dq_full": ("isa_bwd_dq_kernel (full route)", 6)}
+    kernels = {"dk_full": ("isa_bwd_dk_pp_kernel (full route)", 6), "dv_full": ("isa_bwd_dv_pp_kernel (full route)", 4),
+               "dq_full": ("isa_bwd_dq_pp_kernel (full route)", 6)}
     rooflines = []
     for key, (label, per) in kernels.items():
         if st.get(key):
