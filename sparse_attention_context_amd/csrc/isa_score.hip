@@ -25,6 +25,8 @@
 
 namespace isa {
 
+constexpr int kSalCtxCache = 512;   // context blocks whose logits pass 2 takes from LDS
+
 struct SalArgs {
   const float* qbar;
   const float* kbar;
@@ -57,6 +59,10 @@ __global__ __launch_bounds__(512) void isa_saliency_kernel(SalArgs a) {
   constexpr int NW = 8;
   __shared__ double red_m[NW][R], red_s[NW][R];
   __shared__ double pt[NW][32][R + 1];  // per wave: [key][query] probabilities
+  // context logits of pass 1, [context block][query], reused by pass 2 when
+  // they fit (nb_c <= kSalCtxCache); otherwise pass 2 recomputes them
+  __shared__ float lctx[kSalCtxCache][R];
+  const bool cache = a.nb_c <= kSalCtxCache;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int tile = blockIdx.x;
@@ -105,6 +111,13 @@ __global__ __launch_bounds__(512) void isa_saliency_kernel(SalArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (key_of(k0, r) < a.M) tmax = fmaxf(tmax, L[r]);
+    if (cache && k0 + 32 > a.nb_s) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = key_of(k0, r);
+        if (j >= a.nb_s && j < a.M) lctx[j - a.nb_s][l32] = L[r];
+      }
+    }
     if (tmax > m) {
       if (m != -INFINITY) s *= (double)__builtin_amdgcn_exp2f((m - tmax) * 1.4426950408889634f);
       m = tmax;
@@ -150,7 +163,16 @@ __global__ __launch_bounds__(512) void isa_saliency_kernel(SalArgs a) {
     const int ct = ct0 + w;
     if (ct < nct) {
       const int k0 = a.nb_s + 32 * ct;
-      const f32x16 L = logits(k0);
+      f32x16 L;
+      if (cache) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = key_of(k0, r);
+          L[r] = j < a.M ? lctx[j - a.nb_s][l32] : 0.f;
+        }
+      } else {
+        L = logits(k0);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = key_of(k0, r);
