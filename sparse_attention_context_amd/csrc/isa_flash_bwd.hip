@@ -124,8 +124,9 @@ __global__ __launch_bounds__(256) void isa_bwd_delta_kernel(BwdArgs a) {
   }
   float s = 0.f;
   if (ok) {
-    const u32x4 o = *(const u32x4*)((const bf16_t*)a.O + row * D + e);
-    const u32x4 g = *(const u32x4*)((const bf16_t*)a.dO + row * D + e);
+    // (non-temporal: a streaming read of O and dO)
+    const u32x4 o = __builtin_nontemporal_load((const u32x4*)((const bf16_t*)a.O + row * D + e));
+    const u32x4 g = __builtin_nontemporal_load((const u32x4*)((const bf16_t*)a.dO + row * D + e));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       s += __uint_as_float(o[i] << 16) * __uint_as_float(g[i] << 16) +

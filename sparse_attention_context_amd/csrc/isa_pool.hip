@@ -36,8 +36,10 @@ struct PoolArgs {
 };
 
 // Mean of `rows` rows of d elements from `base` (16-byte chunk column c =
-// lane % CPR of each row): every lane of column c ends with the sums.
-template <typename T, int D>
+// lane % CPR of each row): every lane of column c ends with the sums.  NT:
+// non-temporal loads (the streaming pass reads every input row once; the
+// hint keeps its 0.4 GB from cycling through the caches).
+template <typename T, int D, bool NT>
 __device__ __forceinline__ void pool_rows(const char* base, int rows, float* acc) {
   constexpr int ES = sizeof(T);
   constexpr int CPR = D * ES / 16;     // 16-byte chunks per row
@@ -56,7 +58,9 @@ __device__ __forceinline__ void pool_rows(const char* base, int rows, float* acc
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       const int r = r0b + i * RG;
-      v[i] = r < rows ? *(const u32x4*)(base + (long long)r * D * ES) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4* src = (const u32x4*)(base + (long long)r * D * ES);
+      if constexpr (NT) v[i] = r < rows ? __builtin_nontemporal_load(src) : u32x4{0u, 0u, 0u, 0u};
+      else v[i] = r < rows ? *src : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
   int r0, rows;
   block_rows(a, blk, &r0, &rows);
   float acc[EPC];
-  pool_rows<T, D>((const char*)src + ((bh * nrows_head + r0) * D) * ES, rows, acc);
+  pool_rows<T, D, true>((const char*)src + ((bh * nrows_head + r0) * D) * ES, rows, acc);
   if (lane < CPR) {
     const float n = (float)rows;
 #pragma unroll
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256) void isa_pool_pack_kernel(PoolArgs a) {
     const float* vb = a.vbar + (bh * a.M + j) * D;
     if (j >= a.nb_s) {
       float acc[EPC];
-      pool_rows<T, D>((const char*)a.V + ((bh * a.Nk + r0) * D) * ES, rows, acc);
+      pool_rows<T, D, false>((const char*)a.V + ((bh * a.Nk + r0) * D) * ES, rows, acc);
       const float n = (float)rows;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) v[e] = acc[e] / n;
