@@ -53,8 +53,13 @@
 #ifndef ISA_PP_LOOKAHEAD
 #define ISA_PP_LOOKAHEAD 5
 #endif
+#ifndef ISA_FLASH_PPS
+#define ISA_FLASH_PPS 1
+#endif
 
 namespace isa {
+
+constexpr bool kUsePps = ISA_FLASH_PPS;
 
 enum { FK_DENSE = 0, FK_GATHER = 1, FK_POOLED = 2 };
 enum { FR_IDENTITY = 0, FR_TABLE = 1 };
@@ -777,6 +782,388 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   }
 }
 
+// Persistent form of the full-route ping-pong kernel: one workgroup per CU
+// takes the work items (row tile, key split) g, g + G, g + 2G, ... (G
+// workgroups; item ids through xcd_remap as the one-item-per-workgroup
+// launch, so an item runs on the XCD it would run on there) and runs the
+// key tiles of all its items as one sequence of steps s: the rings, the
+// row-table ring and the wait counts are those of isa_flash_pp_kernel with
+// the step index s in place of the tile index, and at an item boundary the
+// pipeline does not drain.  Step s0, the first of item r + 1: X_{s0} ends
+// the P.V sum of item r and starts S of item r + 1 (its queries were loaded
+// in Y_{s0-1}); Y_{s0} writes item r's output (the same normalisation and
+// stores as the epilogue of isa_flash_pp_kernel, through buffer stores, so
+// that every wave issues the same nine stores and the load waits can count
+// them), resets the running state and takes the softmax of item r + 1's
+// first tile.  Used when every item has at least kPpsMinTiles key tiles and
+// a workgroup has at most kPpsMaxItems items; the output is that of
+// isa_flash_pp_kernel bit for bit.
+constexpr int kPpsMaxItems = 8;
+constexpr int kPpsMinTiles = 8;
+__global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
+  typedef bf16x8 Op;
+  constexpr int D = 128, BN = 64, BM = 256, NST = 4;
+  constexpr int RB = D * 2, TB = BN * RB, NT = D / 32;
+  static_assert(BM == kFlashRows, "tile mapping");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TB];   // K ring, then V ring
+  __shared__ __attribute__((aligned(16))) int stab[8][4][64];         // per-wave key-table ring
+  __shared__ int sq[8][kPpsMaxItems][64];                             // query row of each lane and item
+  __shared__ int snv[kPpsMaxItems];                                   // valid keys of each item's head
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int G = gridDim.x;
+  const int n_items = a.n_wg;
+  const int nr = n_items > (int)blockIdx.x ? (n_items - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const int n_keys = a.Ns + (int)a.ctx_tok;
+  const int ntiles = (n_keys + BN - 1) / BN;
+
+  struct Item { int bh, rt, split, t_begin, nt; };
+  auto item_of = [&](int r) -> Item {
+    const int lid = xcd_remap((int)blockIdx.x + r * G, n_items);
+    const int split = lid % a.nsplit;
+    const int rest = lid / a.nsplit;
+    const int bh = rest / a.row_tiles;
+    const int tb = split * a.tiles_per_split;
+    return Item{bh, rest - bh * a.row_tiles, split, tb, min(a.tiles_per_split, ntiles - tb)};
+  };
+  // per item: each lane's query row and the head's valid key count
+  for (int r = 0; r < nr; ++r) {
+    const Item it = item_of(r);
+    const long long vrow = (long long)it.rt * BM + w * 32 + l32;
+    sq[w][r][lane] = route_row(a.q_list + (long long)it.bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
+    if (tid == 0) {
+      const bool tail_kept = a.kc > 0 && a.kept[(long long)it.bh * a.kc + a.kc - 1] == a.nb_c - 1;
+      snv[r] = n_keys - (tail_kept ? a.b - a.tail_c : 0);
+    }
+  }
+  __syncthreads();
+
+  // Positions of the step sequence: a cursor walks (item, tile) and stops at
+  // the last tile, so that loads past the end re-read it (never used).
+  struct Cursor { int r, k; Item it; };
+  auto cursor0 = [&]() { return Cursor{0, 0, item_of(0)}; };
+  auto advance = [&](Cursor& c) {
+    if (c.k + 1 < c.it.nt) {
+      ++c.k;
+    } else if (c.r + 1 < nr) {
+      ++c.r;
+      c.k = 0;
+      c.it = item_of(c.r);
+    }
+  };
+
+  Op qB[D / 16];
+  auto load_q = [&](int r, int bh) {
+    const int qrow = sq[w][r][lane];
+    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
+  };
+
+  const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
+  struct Rows { int r[2]; };
+  const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
+                          __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
+  // key-table entries of the wave's 8 rows of the tile at cursor c into slot pos % 4
+  auto fetch_rows = [&](int pos, const Cursor& c) {
+    const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
+    const int* tab = a.key_rows + (long long)c.it.bh * a.n_keytab;
+    const int idx = (c.it.t_begin + c.k) * BN + 32 * grp + 8 * wg + k;
+    dma4(stab_w + (unsigned)(pos & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)idx * 4u);
+  };
+  auto rows_of = [&](int pos) -> Rows {
+    const int2 v = *(const int2*)&stab[w][pos & 3][2 * (lane >> 4)];
+    return Rows{{v.x, v.y}};
+  };
+  const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
+  const unsigned lds_v = lds_k + NST * TB;
+  unsigned lchunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
+  const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+  auto issue_tile = [&](unsigned ring, int stage, const void* base, int bh, Rows rows) {
+    const char* G0 = (const char*)base + (long long)bh * a.Nk * RB;
+    const unsigned d0 = ring + wrow + (unsigned)stage * TB;
+    dma16x2(d0, d0 + 4 * RB, G0, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+  };
+
+  int koff[8], voff[NT][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int m = lane & 15;
+      const int kr = 4 * h + (m >> 2) + 8 * hi;
+      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+      voff[t][hi] = NST * TB + kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
+    }
+
+  struct STile { f32x16 t[2]; };
+  struct PTile { Op p[4]; };
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+  const float thresh = 8.0f / sc;
+
+  auto pv_qk = [&](int vstage, const PTile& P, int kstage) -> STile {
+    constexpr int LA = ISA_PP_LOOKAHEAD;
+    const lds_char* Vs = (const lds_char*)smem + vstage * TB;
+    const lds_char* Ks = (const lds_char*)smem + kstage * TB;
+    Op opv[16], opk[16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * q * RB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * q * RB));
+        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) opk[2 * q + ti] = *(const Op*)(Ks + koff[q] + 32 * ti * RB);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], P.p[m & 3], acc[m >> 2]);
+    STile S;
+    S.t[0] = f32x16{};
+    S.t[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) S.t[m & 1] = mma32(opk[m], qB[m >> 1], S.t[m & 1]);
+    pp_issue_order<LA>();
+    return S;
+  };
+  auto exp_tile = [&](const f32x16* S, PTile& P) -> float {
+    const float msub = m_ref * sc;
+    float psum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, -msub));
+        psum += p;
+        P.p[s][jj] = (__bf16)p;
+      }
+    }
+    return psum;
+  };
+  // the softmax rule of isa_flash_pp_kernel; t0: first key of the tile
+  auto softmax = [&](int t0, int n_valid, STile St) -> PTile {
+    f32x16* S = St.t;
+    if (t0 + BN > n_valid) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t0 + 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) S[ti][r] = -INFINITY;
+    }
+    PTile P;
+    float psum = exp_tile(S, P);
+    if (__ballot(!(psum <= 128.f))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const bool move = mx > m_ref + thresh;
+      if (__ballot(move)) {
+        const float m_new = move ? mx : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sc);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+        m_ref = m_new;
+        psum = exp_tile(S, P);
+      }
+    }
+    l_run += psum;
+    return P;
+  };
+  // Output of item r (as the epilogue of isa_flash_pp_kernel) through
+  // buffer stores: a lane with nothing to store gets an offset past its
+  // buffer, which the hardware drops, so every wave issues 8 + 1 stores.
+  constexpr unsigned kOut = 0x80000000u;
+  // 16-byte chunk c = d / 8 of a row: lanes l and l + 32 hold its halves;
+  // one permlane32 swap per word gives each lane a whole chunk
+  auto store_rows = [&](__amdgpu_buffer_rsrc_t rs, unsigned off, float inv) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      unsigned x[2], y[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 2 * k + u, t = c >> 2, g = c & 3;
+        unsigned* dst = u ? y : x;
+        dst[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+        dst[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+        x[e] = sw[0];
+        y[e] = sw[1];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{x[0], x[1], y[0], y[1]}, rs,
+                                            off == kOut ? kOut : off + 16 * (2 * k + h), 0, 0);
+    }
+  };
+  auto finish = [&](int r, const Item& it) {
+    const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+    const int qrow = sq[w][r][lane];
+    if (a.nsplit == 1) {
+      const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + (long long)it.bh * a.Ns * D, (short)0,
+                                                        a.Ns * D * 2, 0x00020000);
+      store_rows(rO, qrow >= 0 ? (unsigned)qrow * RB : kOut, 1.0f / l_tot);
+      const auto rL = __builtin_amdgcn_make_buffer_rsrc(a.lse ? a.lse + (long long)it.bh * a.Ns : a.lse, (short)0,
+                                                        a.lse ? a.Ns * 4 : 0, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref * sc + __builtin_log2f(l_tot)), rL,
+                                           (qrow >= 0 && h == 0) ? (unsigned)qrow * 4 : kOut, 0, 0);
+    } else {
+      const long long prow0 = (long long)it.bh * a.row_tiles * BM * a.nsplit;   // first partial row of the head
+      const int nrow = a.row_tiles * BM * a.nsplit;
+      const int prow = (it.rt * BM + w * 32 + l32) * a.nsplit + it.split;
+      const auto rP = __builtin_amdgcn_make_buffer_rsrc(a.part_o + prow0 * D, (short)0, nrow * RB, 0x00020000);
+      store_rows(rP, (unsigned)prow * RB, l_tot > 0.f ? 1.0f / l_tot : 0.f);
+      const auto rM = __builtin_amdgcn_make_buffer_rsrc(a.part_ml + prow0 * 2, (short)0, nrow * 8, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_ref), __float_as_uint(l_tot)}, rM,
+                                           h == 0 ? (unsigned)prow * 8 : kOut, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+    m_ref = -INFINITY;
+    l_run = 0.f;
+  };
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nr == 0) return;   // (never: the grid has at most n_items workgroups)
+  int total = 0;
+  for (int r = 0; r < nr; ++r) total += item_of(r).nt;
+  const Item it0 = item_of(0);
+  load_q(0, it0.bh);
+  auto cp = [&](int s) { return min(s, total - 1); };   // slot positions past the end clamp
+  // cursors: compute (step s), K (s + 3), V (s + 2), table (s + 6)
+  Cursor cc = cursor0(), ck = cursor0(), cv = cursor0(), ct = cursor0();
+  Rows rk, rv;
+  {
+    // tables of positions 0..3, then K(0..2), V(0..1), tables of 4, 5
+    fetch_rows(0, ct); advance(ct);
+    fetch_rows(1, ct); advance(ct);
+    fetch_rows(2, ct); advance(ct);
+    fetch_rows(3, ct); advance(ct);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    const Rows r0 = rows_of(0), r1 = rows_of(1);
+    rv = rows_of(2);
+    rk = rows_of(3);
+    issue_tile(lds_k, 0, a.K, ck.it.bh, r0); advance(ck);
+    issue_tile(lds_v, 0, a.V, cv.it.bh, r0); advance(cv);
+    issue_tile(lds_k, 1, a.K, ck.it.bh, r1); advance(ck);
+    issue_tile(lds_v, 1, a.V, cv.it.bh, r1); advance(cv);
+    issue_tile(lds_k, 2, a.K, ck.it.bh, rv); advance(ck);   // (V(2) is loaded by the first step)
+    fetch_rows(4, ct); advance(ct);
+    fetch_rows(5, ct); advance(ct);
+    u32x4* vz = (u32x4*)(smem + NST * TB + 3 * TB);
+#pragma unroll
+    for (int q = 0; q < TB / (16 * 512); ++q) vz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  }
+  phase_barrier();
+  if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+  STile S = {};
+  PTile P = {};
+  Item fin = it0;   // the item whose output the next boundary writes
+  int fin_r = 0;
+  // One step.  FIRST: the first tile of an item (after item 0, the previous
+  // item's output is written); LAST: its last tile (the next item's queries
+  // are loaded for the step after it); INNER: a tile whose K, V and table
+  // positions (s + 3, s + 2, s + 6) lie in the same item, so that they are
+  // offsets from the compute cursor and the other cursors are not moved
+  // (they are set again after the inner run).  nv: valid keys of the item's
+  // head, kept in a register for the item.
+  auto step = [&](int s, auto first_c, auto last_c, auto inner_c, int nv) {
+    constexpr bool FIRST = decltype(first_c)::value, LAST = decltype(last_c)::value;
+    constexpr bool INNER = decltype(inner_c)::value;
+    const int Z = s & 3;
+    __builtin_amdgcn_s_setprio(3);
+    S = pv_qk((Z + 3) & 3, P, Z);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+    // Y_s
+    const bool boundary = FIRST && s > 0;
+    if (boundary) {
+      finish(fin_r, fin);
+      fin = cc.it;
+      fin_r = cc.r;
+    }
+    if constexpr (INNER) {
+      issue_tile(lds_k, (Z + 3) & 3, a.K, cc.it.bh, rk);
+      issue_tile(lds_v, (Z + 2) & 3, a.V, cc.it.bh, rv);
+      const Rows rn = rows_of(s + 4);
+      fetch_rows(s + 6, Cursor{cc.r, cc.k + 6, cc.it});
+      P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
+      rv = rk;
+      rk = rn;
+      ++cc.k;
+      __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
+    } else {
+      issue_tile(lds_k, (Z + 3) & 3, a.K, ck.it.bh, rk);
+      issue_tile(lds_v, (Z + 2) & 3, a.V, cv.it.bh, rv);
+      const Rows rn = rows_of(cp(s + 4));
+      fetch_rows(cp(s + 6), ct);
+      if (s < total) P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
+      rv = rk;
+      rk = rn;
+      const bool next_item = LAST && cc.r + 1 < nr;
+      if (next_item) load_q(cc.r + 1, item_of(cc.r + 1).bh);
+      advance(cc);
+      advance(ck);
+      advance(cv);
+      advance(ct);
+      // the loads of Y_{s-1} have landed before the barrier that closes Y_s
+      // (this step's output stores or query loads were issued too)
+      if (boundary) __builtin_amdgcn_s_waitcnt(0x0f7e);         // vmcnt(14)
+      else if (next_item) __builtin_amdgcn_s_waitcnt(0x0f7d);   // vmcnt(13)
+      else __builtin_amdgcn_s_waitcnt(0x0f75);                  // vmcnt(5)
+    }
+    phase_barrier();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int s = 0;
+  for (int r = 0; r < nr; ++r) {
+    const int ntr = cc.it.nt;   // >= kPpsMinTiles
+    const int nv = snv[r];
+    step(s++, T_{}, F_{}, F_{}, nv);
+    // K, V and table positions stay in the item while k + 6 < ntr
+    for (int k = 1; k + 6 < ntr; ++k) step(s++, F_{}, F_{}, T_{}, nv);
+    ck = cc; advance(ck); advance(ck); advance(ck);
+    cv = cc; advance(cv); advance(cv);
+    ct = cc;
+#pragma unroll 1
+    for (int j = 0; j < 6; ++j) advance(ct);
+#pragma unroll 1
+    for (int k = ntr - 6; k < ntr - 1; ++k) step(s++, F_{}, F_{}, F_{}, nv);
+    step(s++, F_{}, T_{}, F_{}, nv);
+  }
+  step(s, F_{}, F_{}, F_{}, 0);   // s == total: the last P.V (no softmax)
+  finish(fin_r, fin);
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+  if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+}
+
 // Ping-pong schedule of the pooled pass (sharpness + Taylor output of every
 // source row over the kept pooled blocks), d = 128, as a persistent kernel.
 // The arithmetic is that of isa_flash_kernel in pooled mode (hi + lo key
@@ -1187,6 +1574,19 @@ static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, lo
   if (nwg == 0) return hipSuccess;
   a.n_wg = (int)nwg;
   if constexpr (D == 128 && KM != FK_POOLED && WO && !WP && kFlashWaves == 8) {
+    if constexpr (KM == FK_GATHER && RM == FR_TABLE) {
+      // persistent form when every work item has enough key tiles
+      const int ntiles = (int)((keys + 63) / 64);
+      const int last = ntiles - (a.nsplit - 1) * a.tiles_per_split;
+      const long long grid = nwg < kCUs ? nwg : kCUs;
+      const long long prows = (long long)a.row_tiles * kFlashRows * a.nsplit;
+      if (kUsePps && a.tiles_per_split >= kPpsMinTiles && last >= kPpsMinTiles &&
+          (nwg + grid - 1) / grid <= kPpsMaxItems && (long long)a.Ns * D * 2 < (1LL << 31) &&
+          prows * D * 2 < (1LL << 31)) {
+        hipLaunchKernelGGL(isa_flash_pps_kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM>), dim3((unsigned)nwg), dim3(512), 0, s, a);
     return hipGetLastError();
   }

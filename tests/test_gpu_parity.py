@@ -83,6 +83,10 @@ SMALL = [
     (1, 3, 64, 1111, 999, 48, 0.2, 0.7, "bf16"),
     (1, 2, 128, 500, 0, 32, 0.5, 0.3, "bf16"),        # no context at d = 128: the key-row table is the source rows
     (1, 2, 128, 700, 630, 50, 1.0, 0.5, "bf16"),      # short last context block kept; tiles straddle Ns and the gap
+    # more row tiles than compute units: the persistent full-route kernel,
+    # 3 or 4 work items per workgroup, three key splits (the last one shorter)
+    (1, 40, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),
+    (2, 32, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),   # the same with one split: 2 items per workgroup, lse written
 ]
 
 
