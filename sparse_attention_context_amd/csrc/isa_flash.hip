@@ -890,6 +890,20 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     dma16x2(d0, d0 + 4 * RB, G0, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
   };
 
+  // the loads of step s (stage Z = s mod 4): K tile s + 3 (head kbh, rows
+  // rk), V tile s + 2 (head vbh, rows rv), key-table entries of position
+  // pos (cursor c)
+  Rows rk, rv;
+  auto issue_step = [&](int Z, int kbh, int vbh, int pos, const Cursor& c) {
+    const int kt = 4 * (lane & 1) + ((lane >> 1) & 3);
+    const int* tab = a.key_rows + (long long)c.it.bh * a.n_keytab;
+    const int idx = (c.it.t_begin + c.k) * BN + 32 * grp + 8 * wg + kt;
+    dma_kvt(lds_k + wrow + (unsigned)((Z + 3) & 3) * TB, lds_v + wrow + (unsigned)((Z + 2) & 3) * TB,
+            (const char*)a.K + (long long)kbh * a.Nk * RB, (const char*)a.V + (long long)vbh * a.Nk * RB,
+            (unsigned)rk.r[0], (unsigned)rk.r[1], (unsigned)rv.r[0], (unsigned)rv.r[1], lchunk[0], lchunk[1],
+            stab_w + (unsigned)(pos & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)idx * 4u);
+  };
+
   int koff[8], voff[NT][2];
 #pragma unroll
   for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
@@ -941,13 +955,13 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   };
   auto exp_tile = [&](const f32x16* S, PTile& P) -> float {
     const float msub = m_ref * sc;
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, -msub));
-        psum += p;
+        psum = s + jj == 0 ? p : psum + p;   // (p >= 0: the same sum as from 0)
         P.p[s][jj] = (__bf16)p;
       }
     }
@@ -1056,7 +1070,6 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   auto cp = [&](int s) { return min(s, total - 1); };   // slot positions past the end clamp
   // cursors: compute (step s), K (s + 3), V (s + 2), table (s + 6)
   Cursor cc = cursor0(), ck = cursor0(), cv = cursor0(), ct = cursor0();
-  Rows rk, rv;
   {
     // tables of positions 0..3, then K(0..2), V(0..1), tables of 4, 5
     fetch_rows(0, ct); advance(ct);
@@ -1109,20 +1122,16 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       fin_r = cc.r;
     }
     if constexpr (INNER) {
-      issue_tile(lds_k, (Z + 3) & 3, a.K, cc.it.bh, rk);
-      issue_tile(lds_v, (Z + 2) & 3, a.V, cc.it.bh, rv);
+      issue_step(Z, cc.it.bh, cc.it.bh, s + 6, Cursor{cc.r, cc.k + 6, cc.it});
       const Rows rn = rows_of(s + 4);
-      fetch_rows(s + 6, Cursor{cc.r, cc.k + 6, cc.it});
       P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
       rv = rk;
       rk = rn;
       ++cc.k;
       __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
     } else {
-      issue_tile(lds_k, (Z + 3) & 3, a.K, ck.it.bh, rk);
-      issue_tile(lds_v, (Z + 2) & 3, a.V, cv.it.bh, rv);
+      issue_step(Z, ck.it.bh, cv.it.bh, cp(s + 6), ct);
       const Rows rn = rows_of(cp(s + 4));
-      fetch_rows(cp(s + 6), ct);
       if (s < total) P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
       rv = rk;
       rk = rn;
