@@ -87,6 +87,7 @@ SMALL = [
     # 3 or 4 work items per workgroup, three key splits (the last one shorter)
     (1, 40, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),
     (2, 32, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),   # the same with one split: 2 items per workgroup, lse written
+    (1, 8, 128, 1500, 1024, 32, 1.0, 1.0, "bf16"),    # persistent kernel with the fewest key tiles it takes (8 per split)
 ]
 
 
@@ -219,6 +220,27 @@ def test_dense_forward_video_dit_sampled():
         ref = orc.full_attention_rows(Q[0, h][rows].astype(np.float64), K[0, h].astype(np.float64),
                                       V[0, h].astype(np.float64))
         assert_output(Oh[0, h][rows], ref, w.dtype)
+
+
+@pytest.mark.timeout(600)
+def test_persistent_full_route_eight_items_per_workgroup():
+    """2048 work items on 256 workgroups: the most the persistent full-route
+    kernel takes (its per-item query-row table holds 8); sampled rows of every
+    head against the oracle."""
+    B, H, d, Ns, Nc, b, rho, gamma = 2, 128, 128, 2048, 0, 64, 0.5, 1.0
+    _report("case %s" % ((B, H, d, Ns, Nc, b, rho, gamma),))
+    Q, K, V = make_inputs(B, H, d, Ns, Nc, seed=77, dtype="bf16")
+    Qd, Kd, Vd = (device_tensor(t, "bf16") for t in (Q, K, V))
+    O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
+    torch.cuda.synchronize()
+    views = isa.plan_views(Qd, Kd, ws, b, rho, gamma)
+    Oh = O.float().cpu().numpy()
+    rng = np.random.default_rng(5)
+    for x in range(B):
+        for h in range(H):
+            rows = np.array(sorted(set(rng.choice(Ns, 12, replace=False).tolist()) | {0, Ns - 1}))
+            _compare_head(Q[x, h], K[x, h], V[x, h], b, rho, gamma, views, x, h, "bf16", O_gpu=Oh[x, h], rows=rows,
+                          check_pool=(h < 2))
 
 
 def test_stage_sequence_matches_one_call():
