@@ -9,6 +9,12 @@
 //
 // One workgroup (4 waves) per (batch, head).  Scores are fp64 mapped to
 // order-preserving 64-bit keys, so the selection itself is integer work:
+//   n <= kRankMax: each wave sorts 128 (key, index) pairs in registers under
+//                  the total order above (a bitonic network, partners
+//                  exchanged by lane shuffles); a pair's rank is its
+//                  position in its wave's run plus, for each other run, the
+//                  number of pairs ahead of it (a binary search); the pairs
+//                  of rank < k are selected;
 //   n <= kSortMax: bitonic sort of (key, index) pairs in LDS under the total
 //                  order above; the first k sorted positions are selected;
 //   larger n:      MSB-first radix select, 8 passes of 8 bits with an LDS
@@ -22,6 +28,18 @@
 namespace isa {
 
 constexpr int kSortMax = 2048;
+constexpr int kRankMax = 512;   // 4 waves x 64 lanes x 2 pairs
+
+// (ka, ia) comes before (kb, ib): key descending, then index ascending
+__device__ __forceinline__ bool first_before(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)v, m, 64);
+  const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
 
 __device__ __forceinline__ uint64_t order_key(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
@@ -79,15 +97,84 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* wtot) {
 // when rest is non-null the others go ascending to rest[0..n-k).
 __device__ void select_topk(const double* sc, int n, int k, int* sel, int* rest, SelectSmem& sm) {
   const int tid = threadIdx.x;
-  int mode;  // 0: none, 1: all, 2: sort, 3: radix
+  int mode;  // 0: none, 1: all, 2: sort, 3: radix, 4: rank
   if (k <= 0) mode = 0;
   else if (k >= n) mode = 1;
+  else if (n <= kRankMax) mode = 4;
   else if (n <= kSortMax) mode = 2;
   else mode = 3;
 
   uint64_t T = 0;
   int need = 0;
-  if (mode == 2) {
+  if (mode == 4) {
+    // wave wv holds pairs 128 wv + 64 r + lane (r = 0, 1); padding pairs come last
+    const int lane = tid & 63, wv = tid >> 6;
+    uint64_t key[2];
+    int id[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = 128 * wv + 64 * r + lane;
+      key[r] = e < n ? order_key(sc[e]) : 0ull;
+      id[r] = e < n ? e : 0x7fffffff;
+    }
+    for (int i = tid; i < n; i += 256) sm.chosen[i] = 0;
+    // bitonic network over run position p = 64 r + lane: the run of length
+    // `size` holding p is sorted first-to-last when (p & size) == 0
+#pragma unroll
+    for (int size = 2; size <= 128; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        if (stride == 64) {   // (size 128: the whole run in one direction)
+          if (first_before(key[1], id[1], key[0], id[0])) {
+            const uint64_t tk = key[0];
+            const int ti = id[0];
+            key[0] = key[1]; id[0] = id[1];
+            key[1] = tk; id[1] = ti;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const uint64_t pk = shfl_xor_u64(key[r], stride);
+            const int pi = __shfl_xor(id[r], stride, 64);
+            // the lower position of a pair keeps the pair's first entry in a
+            // first-to-last run, its last entry otherwise
+            const bool keep_first = ((lane & stride) == 0) == (((64 * r + lane) & size) == 0);
+            if (first_before(pk, pi, key[r], id[r]) == keep_first) {
+              key[r] = pk;
+              id[r] = pi;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      sm.keys[128 * wv + 64 * r + lane] = key[r];
+      sm.idx[128 * wv + 64 * r + lane] = id[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (id[r] < n) {
+        // pairs ahead of this one in each other run: the three searches interleaved
+        int lo[3] = {0, 0, 0}, hi[3] = {128, 128, 128};
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            const int w2 = q + (q >= wv ? 1 : 0);
+            if (lo[q] < hi[q]) {
+              const int mid = (lo[q] + hi[q]) >> 1;
+              if (first_before(sm.keys[128 * w2 + mid], sm.idx[128 * w2 + mid], key[r], id[r])) lo[q] = mid + 1;
+              else hi[q] = mid;
+            }
+          }
+        }
+        if (64 * r + lane + lo[0] + lo[1] + lo[2] < k) sm.chosen[id[r]] = 1;
+      }
+    }
+    __syncthreads();
+  } else if (mode == 2) {
     // bitonic sort, descending by (key, then lower index first), padded to a
     // power of two with entries that sort last
     int np = 1;
@@ -152,7 +239,7 @@ __device__ void select_topk(const double* sc, int n, int k, int* sel, int* rest,
     bool f = false;
     if (mode == 1) {
       f = valid;
-    } else if (mode == 2) {
+    } else if (mode == 2 || mode == 4) {
       f = valid && sm.chosen[i];
     } else if (mode == 3) {
       const uint64_t key = valid ? order_key(sc[i]) : 0;
