@@ -128,22 +128,24 @@ __device__ __forceinline__ void dma16x2(unsigned l0, unsigned l1, const void* ba
 // r * 256 + c), then 4 bytes per lane of the key-row table from tb + toff
 // into lt + 4 x lane.  Each row address is formed between the m0 write and
 // its load, which gives the load the wait state it needs after m0 changes.
+// Only s_mov writes scalar registers here (SCC is left alone).
 __device__ __forceinline__ void dma_kvt(unsigned lk, unsigned lv, const void* kb, const void* vb, unsigned rk0,
                                         unsigned rk1, unsigned rv0, unsigned rv1, unsigned c0, unsigned c1,
                                         unsigned lt, const void* tb, unsigned toff) {
   unsigned saved, t0, t1, t2, t3;
+  const unsigned lk1 = lk + 1024u, lv1 = lv + 1024u;
   asm volatile(
       "s_mov_b32 %[sv], m0\n\t"
       "s_mov_b32 m0, %[lk]\n\t"
       "v_lshl_or_b32 %[t0], %[rk0], 8, %[c0]\n\t"
       "global_load_lds_dwordx4 %[t0], %[kb]\n\t"
-      "s_add_u32 m0, %[lk], 0x400\n\t"
+      "s_mov_b32 m0, %[lk1]\n\t"
       "v_lshl_or_b32 %[t1], %[rk1], 8, %[c1]\n\t"
       "global_load_lds_dwordx4 %[t1], %[kb]\n\t"
       "s_mov_b32 m0, %[lv]\n\t"
       "v_lshl_or_b32 %[t2], %[rv0], 8, %[c0]\n\t"
       "global_load_lds_dwordx4 %[t2], %[vb]\n\t"
-      "s_add_u32 m0, %[lv], 0x400\n\t"
+      "s_mov_b32 m0, %[lv1]\n\t"
       "v_lshl_or_b32 %[t3], %[rv1], 8, %[c1]\n\t"
       "global_load_lds_dwordx4 %[t3], %[vb]\n\t"
       "s_mov_b32 m0, %[lt]\n\t"
@@ -151,7 +153,7 @@ __device__ __forceinline__ void dma_kvt(unsigned lk, unsigned lv, const void* kb
       "global_load_lds_dword %[toff], %[tb]\n\t"
       "s_mov_b32 m0, %[sv]"
       : [sv] "=&s"(saved), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
-      : [lk] "s"(lk), [lv] "s"(lv), [kb] "s"(kb), [vb] "s"(vb), [rk0] "v"(rk0), [rk1] "v"(rk1), [rv0] "v"(rv0),
+      : [lk] "s"(lk), [lk1] "s"(lk1), [lv] "s"(lv), [lv1] "s"(lv1), [kb] "s"(kb), [vb] "s"(vb), [rk0] "v"(rk0), [rk1] "v"(rk1), [rv0] "v"(rv0),
         [rv1] "v"(rv1), [c0] "v"(c0), [c1] "v"(c1), [lt] "s"(lt), [tb] "s"(tb), [toff] "v"(toff)
       : "memory");
 }
