@@ -115,11 +115,15 @@ def test_small_shapes_elementwise(case):
     assert torch.equal(O, O2)
 
 
-def test_exact_ties_go_to_the_lower_index():
+@pytest.mark.parametrize("shape", [(640, 600, 32),    # context tail of 24 rows
+                                   (400, 300, 1)],    # 400 and 300 blocks: ties across the four sorted runs
+                         ids=lambda c: "Ns%d_Nc%d_b%d" % c)
+def test_exact_ties_go_to_the_lower_index(shape):
     """Exact ties in both scores: zero context keys make every full-size
     context block equally salient; zero queries make every query block
     equally sharp.  The kept and full-route lists must be the lowest indices."""
-    B, H, d, Ns, Nc, b = 1, 2, 64, 640, 600, 32      # context tail of 24 rows
+    Ns, Nc, b = shape
+    B, H, d = 1, 2, 64
     Q, K, V = make_inputs(B, H, d, Ns, Nc, seed=3, dtype="bf16")
     K[:, :, Ns:] = 0.0
     Q[:] = 0.0
