@@ -88,6 +88,8 @@ SMALL = [
     (1, 40, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),
     (2, 32, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),   # the same with one split: 2 items per workgroup, lse written
     (1, 8, 128, 1500, 1024, 32, 1.0, 1.0, "bf16"),    # persistent kernel with the fewest key tiles it takes (8 per split)
+    (1, 2, 64, 400, 300, 1, 0.003, 0.997, "bf16"),    # k = 1 of 300 context blocks, k = n - 1 of 400 query blocks
+    (1, 2, 64, 400, 300, 1, 0.995, 0.0025, "bf16"),   # k = n - 1 of 300, k = 1 of 400
 ]
 
 
