@@ -53,9 +53,10 @@
 #ifndef ISA_PP_LOOKAHEAD
 #define ISA_PP_LOOKAHEAD 5
 #endif
-// the persistent full-route kernel: 4 measured 0.6 % faster than 5 there
+// the persistent full-route kernel: 3 measured about 1 % faster than 5 there
+// (4 in between, 2 no better than 3)
 #ifndef ISA_PPS_LOOKAHEAD
-#define ISA_PPS_LOOKAHEAD 4
+#define ISA_PPS_LOOKAHEAD 3
 #endif
 #ifndef ISA_FLASH_PPS
 #define ISA_FLASH_PPS 1
