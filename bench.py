@@ -3,11 +3,15 @@
 
 One step = one call of isa_attention (pool, saliency, context top-rho,
 pack, sharpness + Taylor, query top-gamma, full attention and merge) over one
-batch of seeded synthetic inputs already resident in HBM.  Prints one JSON
-line: the metric (queries/s), ms per layer call, the library's own dense
-flash attention on the same inputs, per-stage times from HIP events placed
-between the stages of the same stream, the roofline of the dominant kernel
-(full attention, bf16 MFMA) and the CPU oracle timed on a bounded sample.
+batch of seeded synthetic inputs already resident in HBM.  Each timed step is
+bracketed by HIP events on the launch stream and preceded, outside the timed
+region, by a 1 GiB write that flushes the L2 and the Infinity Cache; the
+headline is the median step (p10 and p90 beside it), and a warm-cache median
+of back-to-back steps is reported too.  Prints one JSON line: the metric
+(queries/s), ms per layer call, the library's own dense flash attention on
+the same inputs, per-stage times from HIP events placed between the stages of
+the same stream, the roofline of the dominant kernel (full attention, bf16
+MFMA), the other workload shapes, and the CPU oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gamma G]
 """
@@ -48,6 +52,8 @@ def parse():
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--no-context", action="store_true", help="skip timing the context-token query rows")
     ap.add_argument("--no-fp8", action="store_true", help="skip timing the FP8 variant of the full route")
+    ap.add_argument("--no-others", action="store_true", help="skip timing the other workload shapes")
+    ap.add_argument("--other-steps", type=int, default=10, help="timed steps per other workload shape")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter collection: one layer call, one dense call and a 1 GiB elementwise copy "
                          "(the copy calibrates byte counters), no timing")
@@ -95,24 +101,63 @@ def counted_traffic(kernel_label):
     return None
 
 
-def cpu_baseline(w, Q, K, V, gamma, heads):
-    """The fp64 oracle on `heads` heads of the same inputs, scaled to the layer."""
-    from oracle import isa_oracle as orc
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: single-threaded BLAS assumed
-        cores = 1
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_head(args):
+    from oracle import isa_oracle as orc
+    Qh, Kh, Vh, b, rho, gamma = args
+    p = orc.oracle_plan_head(Qh, Kh, Vh, b, rho, gamma)
+    orc.oracle_forward_head(Qh, Kh, Vh, b, p["kept_ctx"], p["full_q"])
+
+
+def _oracle_heads(jobs, workers):
+    """Wall time of the oracle (plan + forward) on every (batch, head) job,
+    `workers` threads, one BLAS thread each (NumPy releases the GIL in its
+    array kernels, so the heads run side by side)."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        if workers == 1:
+            for j in jobs:
+                _oracle_head(j)
+        else:
+            with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+                list(ex.map(_oracle_head, jobs))
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, Q, K, V, gamma, heads):
+    """The fp64 oracle on `heads` heads of the same inputs, one worker per
+    host core visible to the process (at most 16, the host share of one GPU),
+    scaled to the layer; plus the one-core wall time of the two small
+    workloads (every head)."""
+    from sparse_attention_context_amd.configs import BY_NAME
+    from sparse_attention_context_amd.synth import workload_inputs
+    visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(visible, 16))
     heads = w.H if heads <= 0 else min(heads, w.H)
-    t0 = time.perf_counter()
-    for h in range(heads):
-        p = orc.oracle_plan_head(Q[0, h], K[0, h], V[0, h], w.b, w.rho, gamma)
-        orc.oracle_forward_head(Q[0, h], K[0, h], V[0, h], w.b, p["kept_ctx"], p["full_q"])
-    dt = time.perf_counter() - t0
+    jobs = [(Q[0, h], K[0, h], V[0, h], w.b, w.rho, gamma) for h in range(heads)]
+    dt = _oracle_heads(jobs, workers)
     per_layer = dt / heads * w.H * w.B
-    return {"value": w.B * w.Ns / per_layer, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
-            "sample": "%d of %d heads of the same inputs (plan + forward, fp64 NumPy), %.1f s, scaled by H/%d"
-                      % (heads, w.H, dt, heads)}
+    one_core = {}
+    for name in ("tiny_isa_check", "small_video_layer"):
+        s = BY_NAME[name]
+        q, k, v = workload_inputs(s)
+        t = _oracle_heads([(q[x, h], k[x, h], v[x, h], s.b, s.rho, s.gamma) for x in range(s.B) for h in range(s.H)], 1)
+        one_core[name] = {"s": round(t, 3), "queries_per_s": round(s.B * s.Ns / t, 1)}
+    return {"value": w.B * w.Ns / per_layer, "unit": "queries/s", "cores": workers, "kind": "oracle",
+            "sample": "%d of %d heads of the same inputs (plan + forward, fp64 NumPy), %.1f s on %d threads, "
+                      "scaled by H/%d" % (heads, w.H, dt, workers, heads),
+            "cores_visible": visible, "cpu_model": cpu_model(), "one_core": one_core}
 
 
 def time_fp8(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
@@ -207,6 +252,98 @@ def time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
             "data": "dO seeded N(0,1) in bf16; plan of the timed forward"}
 
 
+def time_steps(fn, steps, stream, flush):
+    """Per-step milliseconds of `steps` calls of fn, each bracketed by HIP
+    events on `stream`.  flush (a device tensor) is overwritten before every
+    step, outside the events, so each step starts with cold caches; None
+    times the steps back to back (warm caches).  The events are read after
+    one synchronisation at the end."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k, (e0, e1) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(float(k))
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def summary(ms_list):
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4), "n": int(a.size)}
+
+
+def time_other_workloads(args, stream, flush):
+    """isa_attention and the dense baseline on the other workload shapes
+    (inputs drawn on the device by the same recipe): flushed median, p10,
+    p90, warm median, dense ratio and the full-route stage."""
+    import torch
+    from sparse_attention_context_amd import isa
+    from sparse_attention_context_amd.configs import ALL
+    from sparse_attention_context_amd.synth import make_inputs_device
+    dev = torch.device("cuda:0")
+    out = []
+    for w in ALL:
+        if w.name == args.workload:
+            continue
+        Qd, Kd, Vd = make_inputs_device(w.B, w.H, w.d, w.Ns, w.Nc, w.seed, dev, w.dtype, w.clips, w.sharp)
+        O = torch.empty_like(Qd)
+        dense = None
+        if w.dtype == "bf16":
+            isa.dense_forward(Qd, Kd, Vd, out=O)
+            dense = float(np.median(time_steps(lambda: isa.dense_forward(Qd, Kd, Vd, out=O), 3, stream, flush)))
+        for g in (w.gammas or (w.gamma,)):
+            desc = isa.desc_for(Qd, Kd, w.b, w.rho, g)
+            ws = isa.new_workspace(desc, dev)
+
+            def step():
+                isa.attention(Qd, Kd, Vd, w.b, w.rho, g, out=O, workspace=ws)
+
+            step()
+            step()
+            cold = time_steps(step, args.other_steps, stream, flush)
+            warm = time_steps(step, args.other_steps, stream, None)
+            views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, g)
+            full_ms = None
+            if views["counts"]["kq"] > 0:
+                names = list(isa.ATTENTION_STAGES)
+                if views["counts"]["kq"] == views["counts"]["nb_s"]:
+                    names[names.index("sharp_taylor")] = "sharp"
+                per = []
+                for _ in range(3):
+                    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                    for i, name in enumerate(names):
+                        evs[i].record(stream)
+                        isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, g, out=O)
+                    evs[-1].record(stream)
+                    torch.cuda.synchronize()
+                    per.append(evs[names.index("full")].elapsed_time(evs[names.index("full") + 1]))
+                full_ms = float(np.median(per))
+            c = summary(cold)
+            rec = {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Ns": w.Ns, "Nc": w.Nc, "b": w.b, "rho": w.rho,
+                   "gamma": g, "dtype": w.dtype, "kc": views["counts"]["kc"], "kq": views["counts"]["kq"],
+                   "ms": c, "warm_median_ms": round(float(np.median(warm)), 4),
+                   "queries_per_s": round(w.B * w.Ns / (c["median_ms"] * 1e-3), 1),
+                   "dense_ms": None if dense is None else round(dense, 4),
+                   "dense_over_isa": None if dense is None else round(dense / c["median_ms"], 3)}
+            if full_ms:
+                fl = full_route_flops(views, w, g)
+                rec["full_route_ms"] = round(full_ms, 4)
+                rec["full_route_tflops"] = round(fl / (full_ms * 1e-3) / 1e12, 1)
+            out.append(rec)
+            log("other workload %s gamma=%g: %.3f ms (p10 %.3f p90 %.3f, warm %.3f), dense %s"
+                % (w.name, g, c["median_ms"], c["p10_ms"], c["p90_ms"], rec["warm_median_ms"],
+                   "-" if dense is None else "%.3f ms" % dense))
+            del ws
+        del Qd, Kd, Vd, O
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,17 +389,15 @@ def main():
         log("profile pass done (copy probe: 1 GiB read + 1 GiB written by the elementwise mul kernel)")
         return
 
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: more than L2 + Infinity Cache
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    log("isa_attention: %.3f ms/call" % ms)
+    cold = time_steps(step, args.steps, stream, flush)
+    warm = time_steps(step, args.steps, stream, None)
+    ms = float(np.median(cold))
+    log("isa_attention: %.3f ms/call (median of %d flushed steps; p10 %.3f, p90 %.3f; warm median %.3f)"
+        % (ms, len(cold), np.percentile(cold, 10), np.percentile(cold, 90), np.median(warm)))
     views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, gamma)
     counts = views["counts"]
 
@@ -286,15 +421,9 @@ def main():
     dense_ms = None
     if not args.no_dense and w.dtype == "bf16":
         isa.dense_forward(Qd, Kd, Vd, out=O)
-        torch.cuda.synchronize()
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for _ in range(args.dense_steps):
-            isa.dense_forward(Qd, Kd, Vd, out=O)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = d0.elapsed_time(d1) / args.dense_steps
-        log("isa_dense_forward: %.3f ms/call" % dense_ms)
+        dense_ms = float(np.median(time_steps(lambda: isa.dense_forward(Qd, Kd, Vd, out=O), args.dense_steps,
+                                              stream, flush)))
+        log("isa_dense_forward: %.3f ms/call (median of %d flushed calls)" % (dense_ms, args.dense_steps))
 
     # roofline of the dominant kernel (full attention)
     flops = full_route_flops(views, w, gamma)
@@ -357,6 +486,10 @@ def main():
     if not args.no_backward and w.dtype == "bf16":
         backward = time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream)
 
+    others_wl = None
+    if not args.no_others:
+        others_wl = time_other_workloads(args, stream, flush)
+
     cpu = None
     if not args.no_cpu:
         log("cpu oracle on %s heads ..." % (args.cpu_heads or "all"))
@@ -371,6 +504,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "timing": dict(summary(cold), warm_median_ms=round(float(np.median(warm)), 4),
+                       protocol="HIP events around each step on the launch stream; a 1 GiB write before each "
+                                "step (outside the events) flushes L2 and the Infinity Cache; value and "
+                                "ms_per_step use the median"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -389,6 +526,7 @@ def main():
         "backward": backward,
         "context_rows": context,
         "fp8_variant": fp8,
+        "other_workloads": others_wl,
     }
     print(json.dumps(out), flush=True)
 

@@ -47,6 +47,33 @@ def make_inputs(B, H, d, Ns, Nc, seed, dtype="bf16", clips=((1.0, 0.5),), sharp=
     return Q, K, V
 
 
+def make_inputs_device(B, H, d, Ns, Nc, seed, device, dtype="bf16", clips=((1.0, 0.5),), sharp=0.20):
+    """The recipe above drawn on the GPU with torch's generator (seeded), for
+    timing runs that do not need the host copy: torch tensors Q [B,H,Ns,d],
+    K and V [B,H,Ns+Nc,d] in bf16 (round to nearest even) or float32.  The
+    values differ from make_inputs' numpy draw; shapes, distributions and
+    structure are the same."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    Q = torch.randn((B, H, Ns, d), generator=g, device=device, dtype=torch.float32)
+    K = torch.randn((B, H, Ns + Nc, d), generator=g, device=device, dtype=torch.float32)
+    V = torch.randn((B, H, Ns + Nc, d), generator=g, device=device, dtype=torch.float32)
+    lo = 0
+    for i, (frac, scale) in enumerate(clips):
+        hi = Nc if i == len(clips) - 1 else lo + int(round(frac * Nc))
+        K[:, :, Ns + lo:Ns + hi] *= scale
+        lo = hi
+    nsh = int(np.floor(sharp * Ns))
+    for x in range(B):
+        for h in range(H):
+            perm = torch.randperm(Ns, generator=g, device=device)[:nsh]
+            t = torch.randint(0, Ns, (nsh,), generator=g, device=device)
+            Q[x, h, perm] += 4.0 * K[x, h, t]
+    if dtype == "bf16":
+        Q, K, V = (t.to(torch.bfloat16) for t in (Q, K, V))
+    return Q, K, V
+
+
 def workload_inputs(w, heads=None):
     """Inputs of a Workload (configs.py).  heads=None draws all w.H heads."""
     H = w.H if heads is None else heads

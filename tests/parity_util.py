@@ -8,6 +8,9 @@ against the oracle run with the GPU's own sets, so an ambiguous flip cannot
 fail the float check.
 """
 
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
@@ -55,3 +58,21 @@ def assert_output(got, ref, dtype):
     else:
         assert maxabs <= F32_MAXABS and rel <= BF16_RELL2, (maxabs, rel)
     return maxabs, rel
+
+
+def host_workers():
+    """Worker threads for oracle work: the host cores visible to this
+    process, at most 16 (the host share of one GPU)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def run_parallel(fn, jobs, workers=None):
+    """[fn(j) for j in jobs] on a thread pool with one BLAS thread per
+    worker (NumPy releases the GIL inside its array kernels)."""
+    from threadpoolctl import threadpool_limits
+    workers = workers or host_workers()
+    with threadpool_limits(limits=1):
+        if workers == 1 or len(jobs) <= 1:
+            return [fn(j) for j in jobs]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, jobs))
