@@ -28,11 +28,20 @@
  *              over the kept blocks (exp(q.k_t) ~ exp(q.kbar_j) inside j).
  *   merge      every source row of O is written by its block's route.
  *
- * Tensors (device memory, caller-owned, contiguous, d fastest):
+ * Tensors (device memory, caller-owned, d unit-stride):
  *   Q [B,H,Ns,d], K and V [B,H,Ns+Nc,d] (rows [0,Ns) source, [Ns,Ns+Nc)
- *   context), O [B,H,Ns,d]; all of element type desc->dtype.
- *   Pointers must be 16-byte aligned.  Context-token query rows are not
- *   computed.
+ *   context), O [B,H,Ns,d]; all of element type desc->dtype.  Each tensor is
+ *   addressed through its own element strides of the batch, head and row
+ *   dimensions (isa_desc.q, .k, .v, .o): row r of head h of batch x of Q
+ *   starts at element x*q.b + h*q.h + r*q.n (likewise K, V, O).  A layout
+ *   [B,N,H,d] (tokens before heads, as a fused QKV projection leaves it)
+ *   has strides {N*H*d, d, H*d}; all three 0 means contiguous [B,H,rows,d].
+ *   Pointers and every stride that is used (dimension larger than 1) must
+ *   be 16-byte aligned in bytes; O's strides (for isa_backward also Q's, K's
+ *   and V's, which address dQ, dK, dV) must not make two of its elements
+ *   overlap; one head of a tensor must span less than 2^31 bytes
+ *   and a row step less than 2^24 bytes.
+ *   Context-token query rows are not computed.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Every call only enqueues work on that stream: no host
@@ -63,27 +72,44 @@ extern "C" {
 typedef enum isa_status {
   ISA_OK = 0,
   ISA_ERR_INVALID_ARGUMENT = 1, /* null pointer, rho/gamma not in [0,1] or NaN,
-                                   Ns < 1, Nc < 0, B or H < 1, b < 1, misaligned */
-  ISA_ERR_UNSUPPORTED = 2,      /* d not 64/128, b > 256, unknown dtype,
-                                   sizes beyond int32 row indexing */
+                                   Ns < 1, Nc < 0, B or H < 1, b < 1, misaligned
+                                   pointer or stride, negative stride, an output
+                                   layout whose elements overlap, reserved != 0 */
+  ISA_ERR_UNSUPPORTED = 2,      /* d not 64/128, b > 256, unknown dtype, B*H >
+                                   65535, Ns + Nc >= 2^24, a head of a tensor
+                                   spanning 2^31 bytes or more, a row step of
+                                   2^24 bytes or more */
   ISA_ERR_WORKSPACE = 3,        /* workspace too small or not 256-byte aligned */
   ISA_ERR_DEVICE = 4            /* a kernel launch failed; see isa_last_error() */
 } isa_status;
 
 typedef enum isa_dtype { ISA_BF16 = 0, ISA_F32 = 1 } isa_dtype;
 
+/* Element strides of the batch, head and row dimensions of one tensor
+ * (the d dimension is unit-stride).  {0, 0, 0} = contiguous [B,H,rows,d]. */
+typedef struct isa_strides {
+  int64_t b;
+  int64_t h;
+  int64_t n;
+} isa_strides;
+
 /* Problem description.  rho and gamma are doubles so that the kept counts
  * ceil(f*n - 1e-9) are evaluated exactly as documented. */
 typedef struct isa_desc {
   int32_t B;      /* batch, >= 1 */
-  int32_t H;      /* heads, >= 1 */
+  int32_t H;      /* heads, >= 1; B*H <= 65535 */
   int32_t Ns;     /* source (query) rows, >= 1 */
-  int32_t Nc;     /* context rows, >= 0 */
+  int32_t Nc;     /* context rows, >= 0; Ns + Nc < 2^24 */
   int32_t d;      /* head width, 64 or 128 */
   int32_t b;      /* block size in tokens, 1..256 */
   double rho;     /* fraction of context blocks kept, in [0,1] */
   double gamma;   /* fraction of query blocks sent to full attention, in [0,1] */
   int32_t dtype;  /* isa_dtype of Q, K, V and O */
+  int32_t reserved; /* must be 0 */
+  isa_strides q;  /* Q (also dQ of isa_backward and Qc of isa_context_forward) */
+  isa_strides k;  /* K (also dK) */
+  isa_strides v;  /* V (also dV) */
+  isa_strides o;  /* O (also dO of isa_backward and Oc of isa_context_forward) */
 } isa_desc;
 
 /* Derived counts (host values). */

@@ -14,19 +14,13 @@ isa_status device_status(hipError_t e) {
   return ISA_ERR_DEVICE;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
 isa_status check_io(const void* Q, const void* K, const void* V, const void* O, bool need_o) {
-  if (!Q || !K || !V || (need_o && !O)) return ISA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || (need_o && !aligned16(O)))
-    return ISA_ERR_INVALID_ARGUMENT;
-  return ISA_OK;
+  const void* p[4] = {Q, K, V, O};
+  return isa::check_tensors(p, need_o ? 4 : 3);
 }
 
 isa_status check_ws(const isa::Layout& L, const void* ws, size_t bytes) {
-  if (!ws) return ISA_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)ws % isa::kWsAlign) != 0 || bytes < L.total) return ISA_ERR_WORKSPACE;
-  return ISA_OK;
+  return isa::check_workspace(ws, bytes, L.total);
 }
 
 #define ISA_RUN(call)                             \
@@ -121,9 +115,7 @@ isa_status fp8_prepare(const isa_desc* desc, const void* Q, const void* K, const
   if ((st = isa::make_fp8_layout(*L, F)) != ISA_OK) return st;
   if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
   if ((st = check_ws(*L, ws, ws_bytes)) != ISA_OK) return st;
-  if (!fws) return ISA_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)fws % isa::kWsAlign) != 0 || fws_bytes < F->total) return ISA_ERR_WORKSPACE;
-  return ISA_OK;
+  return isa::check_workspace(fws, fws_bytes, F->total);
 }
 
 }  // namespace
@@ -170,6 +162,7 @@ extern "C" isa_status isa_context_forward(const isa_desc* desc, const void* Qc, 
   isa_status st = isa::make_layout(desc, &L);
   if (st != ISA_OK) return st;
   if (L.es != 2) return ISA_ERR_UNSUPPORTED;
+  if ((st = isa::context_maps(desc, &L)) != ISA_OK) return st;
   if ((st = check_io(Qc, K, V, Oc, true)) != ISA_OK) return st;
   if (L.Nc == 0) return ISA_OK;
   const isa::Bufs B{Qc, K, V, Oc, nullptr};
@@ -215,12 +208,14 @@ isa_status bwd_prepare(const isa_desc* desc, const void* Q, const void* K, const
   isa_status st = isa::make_layout(desc, L);
   if (st != ISA_OK) return st;
   if ((st = isa::make_bwd_layout(*L, W)) != ISA_OK) return st;
+  // dQ, dK, dV are written through the maps of Q, K, V
+  if (!isa::map_disjoint(L->q, desc->B, L->Ns, L->d) || !isa::map_disjoint(L->k, desc->B, L->Nk, L->d) ||
+      !isa::map_disjoint(L->v, desc->B, L->Nk, L->d))
+    return ISA_ERR_INVALID_ARGUMENT;
   if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
   if ((st = check_io(dO, dQ, dK, dV, true)) != ISA_OK) return st;
   if ((st = check_ws(*L, ws, ws_bytes)) != ISA_OK) return st;
-  if (!bws) return ISA_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)bws % isa::kWsAlign) != 0 || bws_bytes < W->total) return ISA_ERR_WORKSPACE;
-  return ISA_OK;
+  return isa::check_workspace(bws, bws_bytes, W->total);
 }
 
 }  // namespace

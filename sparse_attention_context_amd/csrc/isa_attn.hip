@@ -37,6 +37,7 @@ struct AttnArgs {
   void* O;
   const void* K;
   const void* V;
+  RowMap rmq, rmo, rmk, rmv;  // element strides of Q, O, K, V
   const int* ctx_rows;   // gather: [BH][ctx_tok]
   const int* kept;       // gather: [BH][kc]
   long long ctx_tok;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void isa_attn_kernel(AttnArgs a) {
 
   Op qB[D / 16];
   {
-    const T* qp = (const T*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D + 8 * h;
+    const T* qp = (const T*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       if (qrow >= 0) qB[s] = *(const Op*)(qp + 16 * s);
@@ -115,13 +116,16 @@ __global__ __launch_bounds__(256) void isa_attn_kernel(AttnArgs a) {
   const char* Kg;
   const char* Vg;
   const char* Klo = nullptr;
+  long long krs = KRB, vrs = KRB;   // bytes between key rows, value rows
   if constexpr (POOLED) {
     Kg = (const char*)a.pkhi + (long long)bh * a.mk_pad * KRB;
     Vg = (const char*)a.pv + (long long)bh * a.mk_pad * KRB;
     if constexpr (SPLIT) Klo = (const char*)a.pklo + (long long)bh * a.mk_pad * KRB;
   } else {
-    Kg = (const char*)a.K + (long long)bh * a.Nk * KRB;
-    Vg = (const char*)a.V + (long long)bh * a.Nk * KRB;
+    Kg = (const char*)a.K + rm_head(a.rmk, bh) * ES;
+    Vg = (const char*)a.V + rm_head(a.rmv, bh) * ES;
+    krs = a.rmk.sn * ES;
+    vrs = a.rmv.sn * ES;
   }
   const int* crow = KM == KM_GATHER ? a.ctx_rows + (long long)bh * a.ctx_tok : nullptr;
 
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(256) void isa_attn_kernel(AttnArgs a) {
       const int kr = q / KCPR, c = q % KCPR;
       const int row = key_row(t0 + kr);
       if (row >= 0) {
-        kreg[i] = *(const uint4*)(Kg + (long long)row * KRB + c * 16);
-        if constexpr (SPLIT) kreg_lo[i] = *(const uint4*)(Klo + (long long)row * KRB + c * 16);
+        kreg[i] = *(const uint4*)(Kg + (long long)row * krs + c * 16);
+        if constexpr (SPLIT) kreg_lo[i] = *(const uint4*)(Klo + (long long)row * krs + c * 16);
       } else {
         kreg[i] = uint4{0, 0, 0, 0};
         if constexpr (SPLIT) kreg_lo[i] = uint4{0, 0, 0, 0};
@@ -158,7 +162,7 @@ if constexpr (WO) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = key_row(t0 + 4 * vkg + i);
-        const char* src = Vg + (long long)(row < 0 ? 0 : row) * KRB + vdc * DPT * ES;
+        const char* src = Vg + (long long)(row < 0 ? 0 : row) * vrs + vdc * DPT * ES;
         if constexpr (VW == 2) {
           uint2 v = uint2{0, 0};
           if (row >= 0) v = *(const uint2*)src;
@@ -352,7 +356,7 @@ if constexpr (WO) {
   const float inv = 1.0f / l_tot;
   if (qrow >= 0) {
     if constexpr (WO) {
-      T* op = (T*)a.O + ((long long)bh * a.Ns + qrow) * D;
+      T* op = (T*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -375,6 +379,7 @@ if constexpr (WO) {
 static AttnArgs attn_args(const Layout& L, const Bufs& B) {
   AttnArgs a = {};
   a.Q = B.Q; a.O = B.O; a.K = B.K; a.V = B.V;
+  a.rmq = L.q; a.rmo = L.o; a.rmk = L.k; a.rmv = L.v;
   a.Ns = L.Ns; a.Nk = L.Nk;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)L.d));
   if (B.ws) {

@@ -72,8 +72,10 @@ enum { FR_IDENTITY = 0, FR_TABLE = 1 };
 struct FlashArgs {
   const void* Q;
   void* O;
-  const void* K;        // token modes: [BH][Nk][D]
+  const void* K;        // token modes: [B,H,Nk,D] through mk
   const void* V;
+  RowMap rmq, rmo, rmk, rmv;   // element strides of Q, O, K, V
+  int o_span;           // bytes of one head of O: ((rows - 1) * mo.sn + D) * 2 < 2^31
   const int* ctx_rows;  // gather: [BH][ctx_tok] absolute rows, -1 past a short last block
   const int* kept;      // gather: [BH][kc]
   const int* key_rows;  // gather, d = 128: [BH][n_keytab] row of every full-route key (0 for padding)
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   else qrow = vrow < a.Ns ? (int)vrow : -1;
   Op qB[D / 16];
   {
-    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D + 8 * h;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
   }
@@ -162,13 +164,16 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   const char* Kg;
   const char* Kg_lo = nullptr;
   const char* Vg;
+  long long krs = KRB, vrs = KRB;   // bytes between key rows, value rows
   if constexpr (POOLED) {
     Kg = (const char*)a.pkhi + (long long)bh * a.mk_pad * KRB;
     Kg_lo = (const char*)a.pklo + (long long)bh * a.mk_pad * KRB;
     Vg = (const char*)a.pv + (long long)bh * a.mk_pad * KRB;
   } else {
-    Kg = (const char*)a.K + (long long)bh * a.Nk * KRB;
-    Vg = (const char*)a.V + (long long)bh * a.Nk * KRB;
+    Kg = (const char*)a.K + rm_head(a.rmk, bh) * ES;
+    Vg = (const char*)a.V + rm_head(a.rmv, bh) * ES;
+    krs = a.rmk.sn * ES;
+    vrs = a.rmv.sn * ES;
   }
   const int* crow = GATHER ? a.ctx_rows + (long long)bh * a.ctx_tok : nullptr;
   const int ctx_last = (int)a.ctx_tok - 1;
@@ -201,14 +206,14 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
       const int c = (tid + NTHR * i) % KCPR;
-      g.k[0][i] = *(const u32x4*)(Kg + (long long)rows.r[i] * KRB + c * 16);
-      if constexpr (POOLED) g.k[NKT - 1][i] = *(const u32x4*)(Kg_lo + (long long)rows.r[i] * KRB + c * 16);
+      g.k[0][i] = *(const u32x4*)(Kg + (long long)rows.r[i] * krs + c * 16);
+      if constexpr (POOLED) g.k[NKT - 1][i] = *(const u32x4*)(Kg_lo + (long long)rows.r[i] * krs + c * 16);
     }
     if constexpr (WO) {
 #pragma unroll
       for (int i = 0; i < NKC; ++i) {
         const int c = (tid + NTHR * i) % KCPR;
-        g.v[i] = *(const u32x4*)(Vg + (long long)rows.r[i] * KRB + c * 16);
+        g.v[i] = *(const u32x4*)(Vg + (long long)rows.r[i] * vrs + c * 16);
       }
     }
     g.bias = 0.f;
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
     if (qrow >= 0) {
       const float inv = 1.0f / l_tot;
       if constexpr (WO) {
-        bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
+        bf16_t* op = (bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   else qrow = vrow < a.Ns ? (int)vrow : -1;
   Op qB[D / 16];
   {
-    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D + 8 * h;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
   }
@@ -488,8 +493,9 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   const int t_begin = split * a.tiles_per_split;
   const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
 
-  const char* Kg = (const char*)a.K + (long long)bh * a.Nk * RB;
-  const char* Vg = (const char*)a.V + (long long)bh * a.Nk * RB;
+  const char* Kg = (const char*)a.K + rm_head(a.rmk, bh) * 2;
+  const char* Vg = (const char*)a.V + rm_head(a.rmv, bh) * 2;
+  const unsigned krs = (unsigned)a.rmk.sn * 2u, vrs = (unsigned)a.rmv.sn * 2u;   // row steps in bytes (< 2^24)
   const int* tab = GATHER ? a.key_rows + (long long)bh * a.n_keytab : nullptr;
 
   // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
@@ -524,31 +530,34 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   };
   const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
   const unsigned lds_v = lds_k + NST * TB;
-  // Lane part of the i-th load: row lrow0 + 4i (its offset within a tile)
-  // and the 16-byte chunk that the swizzle puts at this lane.
-  unsigned lchunk[2], lrowoff[2];
+  // Lane part of the i-th load: row lrow0 + 4i (its offset within a tile,
+  // in K and in V rows) and the 16-byte chunk that the swizzle puts at this
+  // lane.
+  unsigned lchunk[2], lrowk[2], lrowv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
-    lrowoff[i] = (unsigned)(lrow0 + 4 * i) * RB + lchunk[i];
+    lrowk[i] = __umul24((unsigned)(lrow0 + 4 * i), krs) + lchunk[i];
+    lrowv[i] = __umul24((unsigned)(lrow0 + 4 * i), vrs) + lchunk[i];
   }
-  // Global offsets of the wave's two loads of a tile: gathered rows come
-  // from the key-row table (whose padding reads row 0), dense tiles of
-  // valid rows only are a contiguous row range (a uniform branch).
-  auto src_offs = [&](Rows rows, int tile, unsigned* o) {
+  // Global offsets of the wave's two loads of a tile (rows rs bytes apart;
+  // lro: the lane parts for that tensor): gathered rows come from the
+  // key-row table (whose padding reads row 0), dense tiles of valid rows
+  // only are a contiguous row range (a uniform branch).
+  auto src_offs = [&](Rows rows, int tile, unsigned* o, unsigned rs, const unsigned* lro) {
     const int t0 = tile * BN;
     if constexpr (GATHER) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) o[i] = (unsigned)rows.r[i] * RB + lchunk[i];
+      for (int i = 0; i < 2; ++i) o[i] = __umul24((unsigned)rows.r[i], rs) + lchunk[i];
     } else {
       if (t0 + BN <= n_valid) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) o[i] = (unsigned)t0 * RB + lrowoff[i];
+        for (int i = 0; i < 2; ++i) o[i] = (unsigned)t0 * rs + lro[i];
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int t = t0 + lrow0 + 4 * i;
-          o[i] = (unsigned)(t < n_valid ? t : 0) * RB + lchunk[i];
+          o[i] = __umul24((unsigned)(t < n_valid ? t : 0), rs) + lchunk[i];
         }
       }
     }
@@ -556,15 +565,16 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   // LDS base of this wave's first load into a ring stage (the second is 4
   // rows further)
   const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
-  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, int tile) {
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, int tile, unsigned rs,
+                        const unsigned* lro) {
     unsigned o[2];
-    src_offs(rows, tile, o);
+    src_offs(rows, tile, o, rs, lro);
     const unsigned d0 = ring + wrow + (unsigned)stage * TB;
     dma16x2(d0, d0 + 4 * RB, base, o[0], o[1]);
   };
   auto issue = [&](int sk, Rows rk, int tk, int sv, Rows rv, int tv) {
-    issue_tile(lds_k, sk, Kg, rk, tk);
-    issue_tile(lds_v, sv, Vg, rv, tv);
+    issue_tile(lds_k, sk, Kg, rk, tk, krs, lrowk);
+    issue_tile(lds_v, sv, Vg, rv, tv, vrs, lrowv);
   };
 
   // operand offsets: K row 32*ti + l32, logical chunk 2s + h; V^T transpose
@@ -777,7 +787,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   const float l_tot = l_run + wave_shfl_xor(l_run, 32);
   if (a.nsplit == 1) {
     if (qrow >= 0) {
-      store_row((bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D, 1.0f / l_tot);
+      store_row((bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn, 1.0f / l_tot);
       if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref * sc + __builtin_log2f(l_tot);
     }
   } else {
@@ -863,7 +873,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   Op qB[D / 16];
   auto load_q = [&](int r, int bh) {
     const int qrow = sq[w][r][lane];
-    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D + 8 * h;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
   };
@@ -889,23 +899,28 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
   const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+  // K and V share one row map here (the launch checks it): head hd's rows
+  // start rm_head(mk, hd) elements into each, rs bytes apart
+  const unsigned rs = (unsigned)a.rmk.sn * 2u;
+  auto head_off = [&](int hd) { return rm_head(a.rmk, hd) * 2; };
   auto issue_tile = [&](unsigned ring, int stage, const void* base, int bh, Rows rows) {
-    const char* G0 = (const char*)base + (long long)bh * a.Nk * RB;
+    const char* G0 = (const char*)base + head_off(bh);
     const unsigned d0 = ring + wrow + (unsigned)stage * TB;
-    dma16x2(d0, d0 + 4 * RB, G0, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+    dma16x2(d0, d0 + 4 * RB, G0, __umul24((unsigned)rows.r[0], rs) + lchunk[0],
+            __umul24((unsigned)rows.r[1], rs) + lchunk[1]);
   };
 
-  // the loads of step s (stage Z = s mod 4): K tile s + 3 (head kbh, rows
-  // rk), V tile s + 2 (head vbh, rows rv), key-table entries of position
-  // pos (cursor c)
+  // the loads of step s (stage Z = s mod 4): K tile s + 3 (head offset ko,
+  // in bytes, rows rk), V tile s + 2 (head offset vo, rows rv), key-table
+  // entries of position pos (cursor c)
   Rows rk, rv;
-  auto issue_step = [&](int Z, int kbh, int vbh, int pos, const Cursor& c) {
+  auto issue_step = [&](int Z, long long ko, long long vo, int pos, const Cursor& c) {
     const int kt = 4 * (lane & 1) + ((lane >> 1) & 3);
     const int* tab = a.key_rows + (long long)c.it.bh * a.n_keytab;
     const int idx = (c.it.t_begin + c.k) * BN + 32 * grp + 8 * wg + kt;
     dma_kvt(lds_k + wrow + (unsigned)((Z + 3) & 3) * TB, lds_v + wrow + (unsigned)((Z + 2) & 3) * TB,
-            (const char*)a.K + (long long)kbh * a.Nk * RB, (const char*)a.V + (long long)vbh * a.Nk * RB,
-            (unsigned)rk.r[0], (unsigned)rk.r[1], (unsigned)rv.r[0], (unsigned)rv.r[1], lchunk[0], lchunk[1],
+            (const char*)a.K + ko, (const char*)a.V + vo, rs, (unsigned)rk.r[0], (unsigned)rk.r[1],
+            (unsigned)rv.r[0], (unsigned)rv.r[1], lchunk[0], lchunk[1],
             stab_w + (unsigned)(pos & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)idx * 4u);
   };
 
@@ -1037,9 +1052,9 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     const float l_tot = l_run + wave_shfl_xor(l_run, 32);
     const int qrow = sq[w][r][lane];
     if (a.nsplit == 1) {
-      const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + (long long)it.bh * a.Ns * D, (short)0,
-                                                        a.Ns * D * 2, 0x00020000);
-      store_rows(rO, qrow >= 0 ? (unsigned)qrow * RB : kOut, 1.0f / l_tot);
+      const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + rm_head(a.rmo, it.bh), (short)0, a.o_span,
+                                                        0x00020000);
+      store_rows(rO, qrow >= 0 ? (unsigned)qrow * ((unsigned)a.rmo.sn * 2u) : kOut, 1.0f / l_tot);
       const auto rL = __builtin_amdgcn_make_buffer_rsrc(a.lse ? a.lse + (long long)it.bh * a.Ns : a.lse, (short)0,
                                                         a.lse ? a.Ns * 4 : 0, 0x00020000);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref * sc + __builtin_log2f(l_tot)), rL,
@@ -1110,7 +1125,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   // offsets from the compute cursor and the other cursors are not moved
   // (they are set again after the inner run).  nv: valid keys of the item's
   // head, kept in a register for the item.
-  auto step = [&](int s, auto first_c, auto last_c, auto inner_c, int nv) {
+  auto step = [&](int s, auto first_c, auto last_c, auto inner_c, int nv, long long ho) {
     constexpr bool FIRST = decltype(first_c)::value, LAST = decltype(last_c)::value;
     constexpr bool INNER = decltype(inner_c)::value;
     const int Z = s & 3;
@@ -1127,7 +1142,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       fin_r = cc.r;
     }
     if constexpr (INNER) {
-      issue_step(Z, cc.it.bh, cc.it.bh, s + 6, Cursor{cc.r, cc.k + 6, cc.it});
+      issue_step(Z, ho, ho, s + 6, Cursor{cc.r, cc.k + 6, cc.it});
       const Rows rn = rows_of(s + 4);
       P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
       rv = rk;
@@ -1135,7 +1150,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       ++cc.k;
       __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
     } else {
-      issue_step(Z, ck.it.bh, cv.it.bh, cp(s + 6), ct);
+      issue_step(Z, head_off(ck.it.bh), head_off(cv.it.bh), cp(s + 6), ct);
       const Rows rn = rows_of(cp(s + 4));
       if (s < total) P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
       rv = rk;
@@ -1160,19 +1175,20 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   for (int r = 0; r < nr; ++r) {
     const int ntr = cc.it.nt;   // >= kPpsMinTiles
     const int nv = snv[r];
-    step(s++, T_{}, F_{}, F_{}, nv);
+    const long long ho = head_off(cc.it.bh);   // the item's K and V rows (inner steps)
+    step(s++, T_{}, F_{}, F_{}, nv, ho);
     // K, V and table positions stay in the item while k + 6 < ntr
-    for (int k = 1; k + 6 < ntr; ++k) step(s++, F_{}, F_{}, T_{}, nv);
+    for (int k = 1; k + 6 < ntr; ++k) step(s++, F_{}, F_{}, T_{}, nv, ho);
     ck = cc; advance(ck); advance(ck); advance(ck);
     cv = cc; advance(cv); advance(cv);
     ct = cc;
 #pragma unroll 1
     for (int j = 0; j < 6; ++j) advance(ct);
 #pragma unroll 1
-    for (int k = ntr - 6; k < ntr - 1; ++k) step(s++, F_{}, F_{}, F_{}, nv);
-    step(s++, F_{}, T_{}, F_{}, nv);
+    for (int k = ntr - 6; k < ntr - 1; ++k) step(s++, F_{}, F_{}, F_{}, nv, ho);
+    step(s++, F_{}, T_{}, F_{}, nv, ho);
   }
-  step(s, F_{}, F_{}, F_{}, 0);   // s == total: the last P.V (no softmax)
+  step(s, F_{}, F_{}, F_{}, 0, 0);   // s == total: the last P.V (no softmax)
   finish(fin_r, fin);
   __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
   if (grp == 0) phase_barrier();   // balances group 1's extra barrier
@@ -1225,7 +1241,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   };
   auto load_q = [&](int ri, Op* q) {
     const int qr = query_row(ri);
-    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)tile_bh(ri) * a.Ns + (qr < 0 ? 0 : qr)) * D + 8 * h;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, tile_bh(ri)) + (long long)(qr < 0 ? 0 : qr) * a.rmq.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) q[s] = *(const Op*)(qp + 16 * s);
   };
@@ -1374,9 +1390,9 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     const int qr = query_row(ri);
     const long long bh = tile_bh(ri);
     const float inv = 1.0f / l_tot;
-    constexpr unsigned kOut = 0x80000000u;   // beyond every buffer below (Ns * D * 2 < 2^31)
-    const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + bh * a.Ns * D, (short)0, a.Ns * D * 2, 0x00020000);
-    const unsigned oo = qr >= 0 ? (unsigned)qr * D * 2 : kOut;
+    constexpr unsigned kOut = 0x80000000u;   // beyond every buffer below (each under 2^31 bytes)
+    const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + rm_head(a.rmo, bh), (short)0, a.o_span, 0x00020000);
+    const unsigned oo = qr >= 0 ? (unsigned)qr * ((unsigned)a.rmo.sn * 2u) : kOut;
     // 16-byte chunk c = d / 8 = 4t + g of the row: lanes l and l + 32 hold
     // its halves.  For the chunk pair (2k, 2k + 1) one permlane32 swap per
     // word gives lane l all of chunk 2k and lane l + 32 all of chunk 2k + 1,
@@ -1544,7 +1560,7 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   }
   const float inv = 1.0f / l;
   if (a.lse && e == 0) a.lse[bh * a.Ns + qrow] = mstar * a.scale_log2 + __builtin_log2f(l);
-  bf16_t* op = (bf16_t*)a.O + (bh * a.Ns + qrow) * D + e;
+  bf16_t* op = (bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn + e;
   *(u32x4*)op = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
 }
@@ -1554,6 +1570,8 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
 static FlashArgs flash_args(const Layout& L, const Bufs& B) {
   FlashArgs a = {};
   a.Q = B.Q; a.O = B.O; a.K = B.K; a.V = B.V;
+  a.rmq = L.q; a.rmo = L.o; a.rmk = L.k; a.rmv = L.v;
+  a.o_span = (int)span_bytes(L.o, L.Ns, L.d, 2);
   a.Ns = L.Ns; a.Nk = L.Nk;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)L.d));
   a.nsplit = 1;
@@ -1595,8 +1613,8 @@ static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, lo
       const long long grid = nwg < kCUs ? nwg : kCUs;
       const long long prows = (long long)a.row_tiles * kFlashRows * a.nsplit;
       if (kUsePps && a.tiles_per_split >= kPpsMinTiles && last >= kPpsMinTiles &&
-          (nwg + grid - 1) / grid <= kPpsMaxItems && (long long)a.Ns * D * 2 < (1LL << 31) &&
-          prows * D * 2 < (1LL << 31)) {
+          (nwg + grid - 1) / grid <= kPpsMaxItems && prows * D * 2 < (1LL << 31) && a.rmk.sb == a.rmv.sb &&
+          a.rmk.sh == a.rmv.sh && a.rmk.sn == a.rmv.sn) {
         hipLaunchKernelGGL(isa_flash_pps_kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
         return hipGetLastError();
       }
@@ -1616,8 +1634,10 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
     case FlashWhat::kDense:
       return flash_launch<D, FK_DENSE, FR_IDENTITY, true, false>(a, L.Ns, L.Nk, L.BH, s);
     case FlashWhat::kContext:
-      // context query rows: Q and O hold Nc rows per head
+      // context query rows: Q and O hold Nc rows per head (L.q and L.o
+      // describe them)
       a.Ns = L.Nc;
+      a.o_span = (int)span_bytes(L.o, L.Nc, L.d, 2);
       return flash_launch<D, FK_DENSE, FR_IDENTITY, true, false>(a, L.Nc, L.Nk, L.BH, s);
     case FlashWhat::kFull:
       a.q_list = (const int*)(B.ws + L.off_fullq);
@@ -1640,7 +1660,7 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
     }
     case FlashWhat::kSharpTaylor:
       if constexpr (D == 128 && kFlashWaves == 8) {
-        if (L.mk_pad >= 2 * 64 && (long long)L.Ns * D * 2 < (1LL << 31)) {
+        if (L.mk_pad >= 2 * 64) {
           // persistent: one workgroup per compute unit, row tiles dealt round-robin
           a.n_rows = L.Ns;
           a.row_tiles = (int)((L.Ns + kFlashRows - 1) / kFlashRows);

@@ -65,6 +65,7 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
+  RowMap rmq, rmk, rmv, rmo;   // element strides: Q and dQ, K and dK, V and dV, O and dO
   const float* lse;      // [BH][Ns] from the forward
   float* delta;          // [BH][Ns]
   const int* ctx_rows;   // [BH][ctx_tok]
@@ -108,15 +109,17 @@ template <int D>
 __global__ __launch_bounds__(256) void isa_bwd_delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8, RPB = 256 / LPR;
   const int e = (threadIdx.x % LPR) * 8;
-  long long row;
+  long long row;       // bh * Ns + source row (the workspace's row order)
+  long long bh;
   bool ok;
   long long rv = -1;   // route entry (bh * n_rowtab + v) of the route workgroups
   if ((long long)blockIdx.x < a.delta_wgs) {
     row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
     ok = row < a.BH * a.Ns;
+    bh = ok ? row / a.Ns : 0;
   } else {
     rv = ((long long)blockIdx.x - a.delta_wgs) * RPB + threadIdx.x / LPR;
-    const long long bh = rv / a.n_rowtab;
+    bh = rv / a.n_rowtab;
     const int r = bh < a.BH ? route_row(a.q_list + bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, rv - bh * a.n_rowtab) : -1;
     ok = r >= 0;
     row = bh * a.Ns + (r < 0 ? 0 : r);
@@ -124,9 +127,10 @@ __global__ __launch_bounds__(256) void isa_bwd_delta_kernel(BwdArgs a) {
   }
   float s = 0.f;
   if (ok) {
-    // (non-temporal: a streaming read of O and dO)
-    const u32x4 o = __builtin_nontemporal_load((const u32x4*)((const bf16_t*)a.O + row * D + e));
-    const u32x4 g = __builtin_nontemporal_load((const u32x4*)((const bf16_t*)a.dO + row * D + e));
+    // (non-temporal: a streaming read of O and dO, which share O's strides)
+    const long long off = rm_head(a.rmo, bh) + (row - bh * a.Ns) * a.rmo.sn + e;
+    const u32x4 o = __builtin_nontemporal_load((const u32x4*)((const bf16_t*)a.O + off));
+    const u32x4 g = __builtin_nontemporal_load((const u32x4*)((const bf16_t*)a.dO + off));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       s += __uint_as_float(o[i] << 16) * __uint_as_float(g[i] << 16) +
@@ -181,8 +185,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_kernel(BwdArgs a) {
   float lse_r = INFINITY, del_r = 0.f;  // rows off the route: p = 0
   {
     const long long r = (long long)bh * a.Ns + (qrow < 0 ? 0 : qrow);
-    const bf16_t* qp = (const bf16_t*)a.Q + r * D + 8 * h;
-    const bf16_t* gp = (const bf16_t*)a.dO + r * D + 8 * h;
+    const long long qr = qrow < 0 ? 0 : qrow;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + qr * a.rmq.sn + 8 * h;
+    const bf16_t* gp = (const bf16_t*)a.dO + rm_head(a.rmo, bh) + qr * a.rmo.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       qB[s] = *(const Op*)(qp + 16 * s);
@@ -210,13 +215,16 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_kernel(BwdArgs a) {
   const char* Kg;
   const char* Kg_lo = nullptr;
   const char* Vg;
+  long long krs = KRB, vrs = KRB;   // bytes between key rows, value rows
   if constexpr (POOLED) {
     Kg = (const char*)a.pkhi + (long long)bh * a.mk_pad * KRB;
     Kg_lo = (const char*)a.pklo + (long long)bh * a.mk_pad * KRB;
     Vg = (const char*)a.pv + (long long)bh * a.mk_pad * KRB;
   } else {
-    Kg = (const char*)a.K + (long long)bh * a.Nk * KRB;
-    Vg = (const char*)a.V + (long long)bh * a.Nk * KRB;
+    Kg = (const char*)a.K + rm_head(a.rmk, bh) * ES;
+    Vg = (const char*)a.V + rm_head(a.rmv, bh) * ES;
+    krs = a.rmk.sn * ES;
+    vrs = a.rmv.sn * ES;
   }
   const int* crow = POOLED ? nullptr : a.ctx_rows + (long long)bh * a.ctx_tok;
   const int ctx_last = (int)a.ctx_tok - 1;
@@ -240,9 +248,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_kernel(BwdArgs a) {
       const int q = tid + NTHR * i;
       const int row = key_row(tile * BN + q / KCPR);
       const int c = q % KCPR;
-      g.k[0][i] = *(const u32x4*)(Kg + (long long)row * KRB + c * 16);
-      if constexpr (POOLED) g.k[1][i] = *(const u32x4*)(Kg_lo + (long long)row * KRB + c * 16);
-      g.v[i] = *(const u32x4*)(Vg + (long long)row * KRB + c * 16);
+      g.k[0][i] = *(const u32x4*)(Kg + (long long)row * krs + c * 16);
+      if constexpr (POOLED) g.k[1][i] = *(const u32x4*)(Kg_lo + (long long)row * krs + c * 16);
+      g.v[i] = *(const u32x4*)(Vg + (long long)row * vrs + c * 16);
     }
     g.bias = 0.f;
     if constexpr (POOLED) {
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_kernel(BwdArgs a) {
 
   if (qrow < 0 && a.nsplit == 1) return;
   if (a.nsplit == 1) {
-    bf16_t* op = (bf16_t*)a.dQ + ((long long)bh * a.Ns + qrow) * D;
+    bf16_t* op = (bf16_t*)a.dQ + rm_head(a.rmq, bh) + (long long)qrow * a.rmq.sn;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -366,7 +374,8 @@ __global__ __launch_bounds__(256) void isa_bwd_dq_merge_kernel(BwdArgs a) {
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < a.nsplit; ++k) s += *(const f32x4*)(a.part_dq + (gid * a.nsplit + k) * D + e);
   s *= a.inv_sqrt_d;
-  *(u32x2*)((bf16_t*)a.dQ + (bh * a.Ns + qrow) * D + e) = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  *(u32x2*)((bf16_t*)a.dQ + rm_head(a.rmq, bh) + (long long)qrow * a.rmq.sn + e) =
+      u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
 }
 
 // ---------------------------------------------------------------------------
@@ -436,8 +445,8 @@ __global__ __launch_bounds__(512) void isa_bwd_dkdv_kernel(BwdArgs a) {
     }
     kvalid = krow >= 0;
     krow = kvalid ? krow : 0;
-    Kg = (const char*)a.K + ((long long)bh * a.Nk + krow) * KRB;
-    Vg = (const char*)a.V + ((long long)bh * a.Nk + krow) * KRB;
+    Kg = (const char*)a.K + (rm_head(a.rmk, bh) + (long long)krow * a.rmk.sn) * ES;
+    Vg = (const char*)a.V + (rm_head(a.rmv, bh) + (long long)krow * a.rmv.sn) * ES;
   }
   Op kB[D / 16], kBl[POOLED ? D / 16 : 1], vB[DK ? D / 16 : 1];
 #pragma unroll
@@ -454,6 +463,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dkdv_kernel(BwdArgs a) {
   const long long s_begin = split * per;
   const int ns = (int)max(0LL, min(per, nsteps - s_begin));
   const int* qlist = a.q_list + (long long)bh * a.q_k;
+  const long long qhead = rm_head(a.rmq, bh), ghead = rm_head(a.rmo, bh);
 
   struct Staged { u32x4 q[NRC]; u32x4 g[NRC]; float l, d; };
   auto load = [&](long long step) -> Staged {
@@ -462,9 +472,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < NRC; ++i) {
       const int q = tid + NTHR * i;
       const int r = route_row(qlist, a.q_k, a.b, a.nb_s, a.Ns, step * BR + q / KCPR);
-      const long long off = ((long long)bh * a.Ns + (r < 0 ? 0 : r)) * D + (q % KCPR) * 8;
-      st.q[i] = *(const u32x4*)((const bf16_t*)a.Q + off);
-      st.g[i] = *(const u32x4*)((const bf16_t*)a.dO + off);
+      const long long rr = r < 0 ? 0 : r;
+      st.q[i] = *(const u32x4*)((const bf16_t*)a.Q + qhead + rr * a.rmq.sn + (q % KCPR) * 8);
+      st.g[i] = *(const u32x4*)((const bf16_t*)a.dO + ghead + rr * a.rmo.sn + (q % KCPR) * 8);
     }
     st.l = INFINITY;  // rows off the route: p = 0
     st.d = 0.f;
@@ -585,7 +595,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dkdv_kernel(BwdArgs a) {
     }
     const float inv_n = 1.0f / (float)n;
     const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D + (DK ? 0 : D);
-    bf16_t* out = (bf16_t*)(DK ? a.dK : a.dV) + ((long long)bh * a.Nk + krow) * D;
+    bf16_t* out = (bf16_t*)(DK ? a.dK : a.dV) + rm_head(DK ? a.rmk : a.rmv, bh) + (long long)krow * (DK ? a.rmk : a.rmv).sn;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -648,14 +658,15 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
   krow = kvalid ? krow : 0;
   Op kB[D / 16];
   {
-    const char* Kg = (const char*)a.K + ((long long)bh * a.Nk + krow) * RB;
+    const char* Kg = (const char*)a.K + (rm_head(a.rmk, bh) + (long long)krow * a.rmk.sn) * ES;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) kB[s] = *(const Op*)(Kg + (16 * s + 8 * h) * ES);
   }
 
   const int nt = a.n_rowtab / BN;   // row tiles of the route
-  const char* Qg = (const char*)a.Q + (long long)bh * a.Ns * RB;
-  const char* Gg = (const char*)a.dO + (long long)bh * a.Ns * RB;
+  const char* Qg = (const char*)a.Q + rm_head(a.rmq, bh) * 2;
+  const char* Gg = (const char*)a.dO + rm_head(a.rmo, bh) * 2;
+  const unsigned qrs = (unsigned)a.rmq.sn * 2u, grs = (unsigned)a.rmo.sn * 2u;   // row steps in bytes
   const int* tab = a.rrow + (long long)bh * a.n_rowtab;
   const float* lseg = a.rlse + (long long)bh * a.n_rowtab;
 
@@ -681,9 +692,10 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
   const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
-  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows) {
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, unsigned rs) {
     const unsigned d0 = ring + wrow + (unsigned)stage * TB;
-    dma16x2(d0, d0 + 4 * RB, base, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+    dma16x2(d0, d0 + 4 * RB, base, __umul24((unsigned)rows.r[0], rs) + lchunk[0],
+            __umul24((unsigned)rows.r[1], rs) + lchunk[1]);
   };
   auto issue_lse = [&](int slot, int tile) {
     if (w == 0) dma4(lds_l + (unsigned)slot * BN * 4, lseg + tile * BN, (unsigned)lane * 4u);
@@ -776,11 +788,11 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
       const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1));
       rv = rows_of(cl(2));
       rk = rows_of(cl(3));
-      issue_tile(lds_q, 0, Qg, r0);
-      issue_tile(lds_g, 0, Gg, r0);
-      issue_tile(lds_q, 1, Qg, r1);
-      issue_tile(lds_g, 1, Gg, r1);
-      issue_tile(lds_q, 2, Qg, rv);   // (dO(2) is loaded by the first step)
+      issue_tile(lds_q, 0, Qg, r0, qrs);
+      issue_tile(lds_g, 0, Gg, r0, grs);
+      issue_tile(lds_q, 1, Qg, r1, qrs);
+      issue_tile(lds_g, 1, Gg, r1, grs);
+      issue_tile(lds_q, 2, Qg, rv, qrs);   // (dO(2) is loaded by the first step)
       issue_lse(0, cl(0));
       issue_lse(1, cl(1));
       issue_lse(2, cl(2));
@@ -804,8 +816,8 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
       __builtin_amdgcn_s_setprio(0);
       phase_barrier();
       // Y_j
-      issue_tile(lds_q, (Z + 3) & 3, Qg, rk);
-      issue_tile(lds_g, (Z + 2) & 3, Gg, rv);
+      issue_tile(lds_q, (Z + 3) & 3, Qg, rk, qrs);
+      issue_tile(lds_g, (Z + 2) & 3, Gg, rv, grs);
       issue_lse((Z + 3) & 3, cl(j + 3));
       const Rows rn = rows_of(cl(j + 4));
       fetch_rows(cl(j + 6), cl(j + 6));
@@ -836,7 +848,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
   }
   const float inv_n = 1.0f / (float)n;
   const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D + D;
-  bf16_t* out = (bf16_t*)a.dV + ((long long)bh * a.Nk + krow) * D;
+  bf16_t* out = (bf16_t*)a.dV + rm_head(a.rmv, bh) + (long long)krow * a.rmv.sn;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -890,8 +902,8 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
   krow = kvalid ? krow : 0;
   Op kB[D / 16], vB[D / 16];
   {
-    const char* Kg = (const char*)a.K + ((long long)bh * a.Nk + krow) * RB;
-    const char* Vg = (const char*)a.V + ((long long)bh * a.Nk + krow) * RB;
+    const char* Kg = (const char*)a.K + (rm_head(a.rmk, bh) + (long long)krow * a.rmk.sn) * ES;
+    const char* Vg = (const char*)a.V + (rm_head(a.rmv, bh) + (long long)krow * a.rmv.sn) * ES;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       kB[s] = *(const Op*)(Kg + (16 * s + 8 * h) * ES);
@@ -900,8 +912,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
   }
 
   const int nt = a.n_rowtab / BN;
-  const char* Qg = (const char*)a.Q + (long long)bh * a.Ns * RB;
-  const char* Gg = (const char*)a.dO + (long long)bh * a.Ns * RB;
+  const char* Qg = (const char*)a.Q + rm_head(a.rmq, bh) * 2;
+  const char* Gg = (const char*)a.dO + rm_head(a.rmo, bh) * 2;
+  const unsigned qrs = (unsigned)a.rmq.sn * 2u, grs = (unsigned)a.rmo.sn * 2u;   // row steps in bytes
   const int* tab = a.rrow + (long long)bh * a.n_rowtab;
   const float* lseg = a.rlse + (long long)bh * a.n_rowtab;
   const float* delg = a.rdel + (long long)bh * a.n_rowtab;
@@ -925,9 +938,10 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
   const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
-  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows) {
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, unsigned rs) {
     const unsigned d0 = ring + wrow + (unsigned)stage * TB;
-    dma16x2(d0, d0 + 4 * RB, base, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+    dma16x2(d0, d0 + 4 * RB, base, __umul24((unsigned)rows.r[0], rs) + lchunk[0],
+            __umul24((unsigned)rows.r[1], rs) + lchunk[1]);
   };
   auto issue_ld = [&](int slot, int tile) {   // lse by wave 0, D by wave 1
     if (w == 0) dma4(lds_ld + (unsigned)slot * BN * 4, lseg + tile * BN, (unsigned)lane * 4u);
@@ -1029,12 +1043,12 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
       const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1)), r2 = rows_of(cl(2));
       rk = rows_of(cl(3));
-      issue_tile(lds_q, 0, Qg, r0);
-      issue_tile(lds_g, 0, Gg, r0);
-      issue_tile(lds_q, 1, Qg, r1);
-      issue_tile(lds_g, 1, Gg, r1);
-      issue_tile(lds_q, 2, Qg, r2);
-      issue_tile(lds_g, 2, Gg, r2);
+      issue_tile(lds_q, 0, Qg, r0, qrs);
+      issue_tile(lds_g, 0, Gg, r0, grs);
+      issue_tile(lds_q, 1, Qg, r1, qrs);
+      issue_tile(lds_g, 1, Gg, r1, grs);
+      issue_tile(lds_q, 2, Qg, r2, qrs);
+      issue_tile(lds_g, 2, Gg, r2, grs);
       issue_ld(0, cl(0));
       issue_ld(1, cl(1));
       issue_ld(2, cl(2));
@@ -1060,8 +1074,8 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
       phase_barrier();
       // Y_j
       const int q3 = q_cur + 3 < NQ ? q_cur + 3 : q_cur + 3 - NQ;   // (j + 3) % 5
-      issue_tile(lds_q, q3, Qg, rk);
-      issue_tile(lds_g, (Z + 3) & 3, Gg, rk);
+      issue_tile(lds_q, q3, Qg, rk, qrs);
+      issue_tile(lds_g, (Z + 3) & 3, Gg, rk, grs);
       issue_ld((Z + 3) & 3, cl(j + 3));
       const Rows rn = rows_of(cl(j + 4));
       fetch_rows(cl(j + 6), cl(j + 6));
@@ -1092,7 +1106,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
   }
   const float inv_n = 1.0f / (float)n;
   const float* pb = a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D;
-  bf16_t* out = (bf16_t*)a.dK + ((long long)bh * a.Nk + krow) * D;
+  bf16_t* out = (bf16_t*)a.dK + rm_head(a.rmk, bh) + (long long)krow * a.rmk.sn;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1144,8 +1158,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
   float lse_r = INFINITY, del_r = 0.f;  // rows off the route: p = 0
   {
     const long long r = (long long)bh * a.Ns + (qrow < 0 ? 0 : qrow);
-    const bf16_t* qp = (const bf16_t*)a.Q + r * D + 8 * h;
-    const bf16_t* gp = (const bf16_t*)a.dO + r * D + 8 * h;
+    const long long qr = qrow < 0 ? 0 : qrow;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + qr * a.rmq.sn + 8 * h;
+    const bf16_t* gp = (const bf16_t*)a.dO + rm_head(a.rmo, bh) + qr * a.rmo.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       qB[s] = *(const Op*)(qp + 16 * s);
@@ -1164,8 +1179,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
   const int t_begin = split * a.tiles_per_split;
   const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
 
-  const char* Kg = (const char*)a.K + (long long)bh * a.Nk * RB;
-  const char* Vg = (const char*)a.V + (long long)bh * a.Nk * RB;
+  const char* Kg = (const char*)a.K + rm_head(a.rmk, bh) * 2;
+  const char* Vg = (const char*)a.V + rm_head(a.rmv, bh) * 2;
+  const unsigned krs = (unsigned)a.rmk.sn * 2u, vrs = (unsigned)a.rmv.sn * 2u;   // row steps in bytes
   const int* tab = a.key_rows + (long long)bh * a.n_keytab;
 
   const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
@@ -1186,9 +1202,10 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
   const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
-  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows) {
+  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, unsigned rs) {
     const unsigned d0 = ring + wrow + (unsigned)stage * TB;
-    dma16x2(d0, d0 + 4 * RB, base, (unsigned)rows.r[0] * RB + lchunk[0], (unsigned)rows.r[1] * RB + lchunk[1]);
+    dma16x2(d0, d0 + 4 * RB, base, __umul24((unsigned)rows.r[0], rs) + lchunk[0],
+            __umul24((unsigned)rows.r[1], rs) + lchunk[1]);
   };
 
   int koff[8], voff[NT][2];
@@ -1285,12 +1302,12 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
       const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1)), r2 = rows_of(cl(2));
       rk = rows_of(cl(3));
-      issue_tile(lds_k, 0, Kg, r0);
-      issue_tile(lds_v, 0, Vg, r0);
-      issue_tile(lds_k, 1, Kg, r1);
-      issue_tile(lds_v, 1, Vg, r1);
-      issue_tile(lds_k, 2, Kg, r2);
-      issue_tile(lds_v, 2, Vg, r2);
+      issue_tile(lds_k, 0, Kg, r0, krs);
+      issue_tile(lds_v, 0, Vg, r0, vrs);
+      issue_tile(lds_k, 1, Kg, r1, krs);
+      issue_tile(lds_v, 1, Vg, r1, vrs);
+      issue_tile(lds_k, 2, Kg, r2, krs);
+      issue_tile(lds_v, 2, Vg, r2, vrs);
       fetch_rows(cl(4), tl(4));
       fetch_rows(cl(5), tl(5));
       // K stage 4 is first loaded in step 1; step 0 reads it as zeros
@@ -1313,8 +1330,8 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
       phase_barrier();
       // Y_j
       const int k3 = k_cur + 3 < NK ? k_cur + 3 : k_cur + 3 - NK;   // (j + 3) % 5
-      issue_tile(lds_k, k3, Kg, rk);
-      issue_tile(lds_v, (Z + 3) & 3, Vg, rk);
+      issue_tile(lds_k, k3, Kg, rk, krs);
+      issue_tile(lds_v, (Z + 3) & 3, Vg, rk, vrs);
       const Rows rn = rows_of(cl(j + 4));
       fetch_rows(cl(j + 6), tl(j + 6));
       if (j < nt) dS = dsoft(j, S, dP);
@@ -1332,7 +1349,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
   // ---- epilogue (as isa_bwd_dq_kernel)
   if (qrow < 0 && a.nsplit == 1) return;
   if (a.nsplit == 1) {
-    bf16_t* op = (bf16_t*)a.dQ + ((long long)bh * a.Ns + qrow) * D;
+    bf16_t* op = (bf16_t*)a.dQ + rm_head(a.rmq, bh) + (long long)qrow * a.rmq.sn;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1382,10 +1399,11 @@ __global__ __launch_bounds__(256) void isa_bwd_zero_pruned_kernel(BwdArgs a) {
   const int r0 = a.Ns + c * a.b;
   const int nr = c == a.nb_c - 1 ? a.tail_c : a.b;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const long long kh = rm_head(a.rmk, bh), vh = rm_head(a.rmv, bh);
   for (int q = threadIdx.x; q < nr * CPR; q += 256) {
-    const long long off = (bh * a.Nk + r0 + q / CPR) * D + (q % CPR) * 8;
-    *(u32x4*)((bf16_t*)a.dK + off) = u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)((bf16_t*)a.dV + off) = u32x4{0u, 0u, 0u, 0u};
+    const long long r = r0 + q / CPR, e = (q % CPR) * 8;
+    *(u32x4*)((bf16_t*)a.dK + kh + r * a.rmk.sn + e) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)((bf16_t*)a.dV + vh + r * a.rmv.sn + e) = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -1395,6 +1413,7 @@ static BwdArgs bwd_args(const Layout& L, const BwdLayout& W, const BwdBufs& B) {
   BwdArgs a = {};
   a.Q = B.Q; a.K = B.K; a.V = B.V; a.O = B.O; a.dO = B.dO;
   a.dQ = B.dQ; a.dK = B.dK; a.dV = B.dV;
+  a.rmq = L.q; a.rmk = L.k; a.rmv = L.v; a.rmo = L.o;
   a.lse = (const float*)(B.ws + L.off_lse);
   a.delta = (float*)(B.bws + W.off_delta);
   a.ctx_rows = (const int*)(B.ws + L.off_ctxrows);

@@ -71,6 +71,7 @@ struct Fp8Args {
   void* O;
   const void* K;
   const void* V;
+  RowMap rmq, rmo, rmk, rmv;   // element strides of Q, O, K, V
   const int* ctx_rows;   // [BH][ctx_tok]
   const int* kept;       // [BH][kc]
   long long ctx_tok;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void isa_fp8_pack_kernel(Fp8Args a) {
     const int row = key_row(t);
     float x[32];
     if (row >= 0) {
-      const bf16_t* kp = (const bf16_t*)a.K + (bh * a.Nk + row) * D + kb * 32;
+      const bf16_t* kp = (const bf16_t*)a.K + rm_head(a.rmk, bh) + (long long)row * a.rmk.sn + kb * 32;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x4 w = *(const u32x4*)(kp + 8 * c);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void isa_fp8_pack_kernel(Fp8Args a) {
     const int i = q / (D / 8), c = q % (D / 8);
     const int row = key_row(tile * BN + i);
     u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (row >= 0) w = *(const u32x4*)((const bf16_t*)a.V + (bh * a.Nk + row) * D + c * 8);
+    if (row >= 0) w = *(const u32x4*)((const bf16_t*)a.V + rm_head(a.rmv, bh) + (long long)row * a.rmv.sn + c * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       vt[i][c * 8 + 2 * j] = __uint_as_float(w[j] << 16);
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_kernel(Fp8Args a) {
   v8i qB[NU];
   int qS[NU];
   {
-    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       float x[32];
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_kernel(Fp8Args a) {
   if (a.nsplit == 1) {
     if (qrow < 0) return;
     const float inv = 1.0f / l_tot;
-    bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
+    bf16_t* op = (bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_pp_kernel(Fp8Args a) {
   v8i qB[NU];
   int qS[NU];
   {
-    const bf16_t* qp = (const bf16_t*)a.Q + ((long long)bh * a.Ns + (qrow < 0 ? 0 : qrow)) * D;
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       float x[32];
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_pp_kernel(Fp8Args a) {
   if (a.nsplit == 1) {
     if (qrow < 0) return;
     const float inv = 1.0f / l_tot;
-    bf16_t* op = (bf16_t*)a.O + ((long long)bh * a.Ns + qrow) * D;
+    bf16_t* op = (bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -715,6 +716,7 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_pp_kernel(Fp8Args a) {
 static Fp8Args fp8_args(const Layout& L, const Fp8Layout& F, const Bufs& B, char* fws) {
   Fp8Args a = {};
   a.Q = B.Q; a.O = B.O; a.K = B.K; a.V = B.V;
+  a.rmq = L.q; a.rmo = L.o; a.rmk = L.k; a.rmv = L.v;
   a.ctx_rows = (const int*)(B.ws + L.off_ctxrows);
   a.kept = (const int*)(B.ws + L.off_kept);
   a.ctx_tok = L.ctx_tok;

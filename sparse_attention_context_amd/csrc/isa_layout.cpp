@@ -38,6 +38,83 @@ int choose_splits(int64_t units, int ntiles) {
 
 static size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Row map of one tensor [B,H,rows,d] from its isa_strides (all zero:
+// contiguous).  Checks the signs, the 16-byte alignment of every used
+// stride and the 32-bit spans the kernels address a head with.
+static isa_status make_map(const isa_strides& s, int B, int H, int rows, int d, int es, RowMap* m) {
+  int64_t sb, sh, sn;
+  if (s.b == 0 && s.h == 0 && s.n == 0) {
+    sn = d;
+    sh = (int64_t)rows * d;
+    sb = (int64_t)H * sh;
+  } else {
+    if (s.b < 0 || s.h < 0 || s.n < 0) return ISA_ERR_INVALID_ARGUMENT;
+    sb = s.b;
+    sh = s.h;
+    sn = s.n;
+  }
+  // magnitudes first, so that the products below cannot overflow
+  if (sn >= kMaxRowStride || sb >= (int64_t(1) << 50) || sh >= (int64_t(1) << 50)) return ISA_ERR_UNSUPPORTED;
+  if ((B > 1 && (sb * es) % 16) || (H > 1 && (sh * es) % 16) || (rows > 1 && (sn * es) % 16))
+    return ISA_ERR_INVALID_ARGUMENT;
+  if (sn * es >= kMaxRowStride) return ISA_ERR_UNSUPPORTED;
+  m->sb = sb;
+  m->sh = sh;
+  m->sn = (int32_t)sn;
+  m->H = H;
+  m->hmul = H > 1 ? (uint32_t)(((uint64_t(1) << 32) + (uint64_t)H - 1) / (uint64_t)H) : 0u;
+  m->pad = 0;
+  if (span_bytes(*m, rows, d, es) >= kMaxSpan) return ISA_ERR_UNSUPPORTED;
+  return ISA_OK;
+}
+
+bool map_disjoint(const RowMap& m, int B, int rows, int d) {
+  // dimensions of more than one element, by stride: each stride must step
+  // past the whole extent of the dimensions below it
+  int64_t st[4] = {1, m.sn, m.sh, m.sb};
+  int64_t n[4] = {d, rows, m.H, B};
+  int k = 0;
+  int64_t ss[4], nn[4];
+  for (int i = 0; i < 4; ++i)
+    if (n[i] > 1) {
+      ss[k] = st[i];
+      nn[k] = n[i];
+      ++k;
+    }
+  for (int i = 1; i < k; ++i)
+    for (int j = i; j > 0 && ss[j] < ss[j - 1]; --j) {
+      int64_t t = ss[j]; ss[j] = ss[j - 1]; ss[j - 1] = t;
+      t = nn[j]; nn[j] = nn[j - 1]; nn[j - 1] = t;
+    }
+  if (k > 0 && ss[0] < 1) return false;
+  for (int i = 1; i < k; ++i)
+    if (ss[i] < ss[i - 1] * nn[i - 1]) return false;
+  return true;
+}
+
+isa_status context_maps(const isa_desc* desc, Layout* L) {
+  if (!desc || !L) return ISA_ERR_INVALID_ARGUMENT;
+  isa_status st;
+  if ((st = make_map(desc->q, desc->B, desc->H, L->Nc, L->d, L->es, &L->q)) != ISA_OK) return st;
+  if ((st = make_map(desc->o, desc->B, desc->H, L->Nc, L->d, L->es, &L->o)) != ISA_OK) return st;
+  if (!map_disjoint(L->o, desc->B, L->Nc, L->d)) return ISA_ERR_INVALID_ARGUMENT;
+  return ISA_OK;
+}
+
+isa_status check_tensors(const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return ISA_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)ptrs[i] & 15u) != 0) return ISA_ERR_INVALID_ARGUMENT;
+  }
+  return ISA_OK;
+}
+
+isa_status check_workspace(const void* ws, size_t bytes, size_t need) {
+  if (!ws) return ISA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)ws % kWsAlign) != 0 || bytes < need) return ISA_ERR_WORKSPACE;
+  return ISA_OK;
+}
+
 isa_status make_layout(const isa_desc* desc, Layout* L) {
   if (!desc || !L) return ISA_ERR_INVALID_ARGUMENT;
   const isa_desc& D = *desc;
@@ -47,10 +124,20 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   if (D.d != 64 && D.d != 128) return ISA_ERR_UNSUPPORTED;
   if (D.b > 256) return ISA_ERR_UNSUPPORTED;
   if (D.dtype != ISA_BF16 && D.dtype != ISA_F32) return ISA_ERR_UNSUPPORTED;
+  if (D.reserved != 0) return ISA_ERR_INVALID_ARGUMENT;
   const int64_t nk = (int64_t)D.Ns + D.Nc;
-  if (nk > (int64_t(1) << 30)) return ISA_ERR_UNSUPPORTED;
+  if (nk > kMaxRows) return ISA_ERR_UNSUPPORTED;
   const int64_t bh = (int64_t)D.B * D.H;
-  if (bh > (int64_t(1) << 24)) return ISA_ERR_UNSUPPORTED;
+  if (bh > kMaxBH) return ISA_ERR_UNSUPPORTED;
+  {
+    const int es = D.dtype == ISA_BF16 ? 2 : 4;
+    isa_status st;
+    if ((st = make_map(D.q, D.B, D.H, D.Ns, D.d, es, &L->q)) != ISA_OK) return st;
+    if ((st = make_map(D.k, D.B, D.H, (int)nk, D.d, es, &L->k)) != ISA_OK) return st;
+    if ((st = make_map(D.v, D.B, D.H, (int)nk, D.d, es, &L->v)) != ISA_OK) return st;
+    if ((st = make_map(D.o, D.B, D.H, D.Ns, D.d, es, &L->o)) != ISA_OK) return st;
+    if (!map_disjoint(L->o, D.B, D.Ns, D.d)) return ISA_ERR_INVALID_ARGUMENT;
+  }
 
   L->BH = bh;
   L->Ns = D.Ns;

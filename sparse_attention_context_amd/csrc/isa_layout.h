@@ -24,9 +24,34 @@ constexpr int kFlashRows = 32 * kFlashWaves;    // query rows per full-attention
 constexpr int kCUs = 256;          // compute units of the target GPU (split-K balance)
 constexpr int kMaxSplits = 8;
 constexpr size_t kWsAlign = 256;
+constexpr int kMaxBH = 65535;            // B*H: grid-y of the per-head launches
+constexpr int64_t kMaxSpan = int64_t(1) << 31;   // bytes of one head of a tensor (32-bit offsets)
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // bytes between rows (24-bit multiplies)
+constexpr int kMaxRows = (1 << 24) - 1;  // Ns + Nc
+
+// Row addressing of one caller tensor [B,H,rows,d]: element strides of the
+// batch, head and row dimensions (d is unit-stride) and the head count; row
+// r of slice bh = x*H + h starts at element x*sb + h*sh + r*sn.  hmul =
+// ceil(2^32 / H) (0 for H = 1) gives x = (bh * hmul) >> 32 exactly for
+// bh < 2^16: with hmul*H = 2^32 + e, 0 <= e < H, the product overshoots
+// bh/H by bh*e/(H 2^32) < 1/H, less than the gap to the next integer.
+struct RowMap {
+  int64_t sb, sh;
+  int32_t sn;          // < 2^23 elements (row step under 2^24 bytes)
+  int32_t H;
+  uint32_t hmul;
+  int32_t pad;
+};
+
+// Bytes from the first to the last byte of one head of a tensor of `rows`
+// rows of d elements of es bytes addressed by m.
+inline int64_t span_bytes(const RowMap& m, int rows, int d, int es) {
+  return ((int64_t)(rows > 0 ? rows - 1 : 0) * m.sn + d) * es;
+}
 
 struct Layout {
   int64_t BH;          // B*H slices
+  RowMap q, k, v, o;   // Q (and dQ, Qc), K (and dK), V (and dV), O (and dO, Oc)
   int Ns, Nc, Nk, d, b, es;   // es = element size of Q/K/V/O
   int nb_s, nb_c, M;   // source blocks, context blocks, all blocks
   int kc, kq, mk;      // kept context blocks, full-route query blocks, kept blocks
@@ -50,6 +75,20 @@ struct Layout {
 
 // Validates *desc and fills *L.  Returns ISA_OK or the error of isa.h.
 isa_status make_layout(const isa_desc* desc, Layout* L);
+
+// True when no two elements of the [B,rows,d] x m.H tensor addressed by m
+// share an address (the strides of an output).
+bool map_disjoint(const RowMap& m, int B, int rows, int d);
+
+// isa_context_forward: Q and O maps of the context query rows [B,H,Nc,d]
+// (the q and o strides of *desc, with Nc rows; contiguous defaults).
+isa_status context_maps(const isa_desc* desc, Layout* L);
+
+// Validates `n` tensor pointers: non-null and 16-byte aligned.
+isa_status check_tensors(const void* const* ptrs, int n);
+
+// Validates a workspace pointer and size against `need` bytes.
+isa_status check_workspace(const void* ws, size_t bytes, size_t need);
 
 // Backward pass (bf16): keys per dK/dV workgroup (8 waves x 32) and query
 // rows staged per step.

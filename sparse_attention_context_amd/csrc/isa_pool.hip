@@ -22,6 +22,7 @@ struct PoolArgs {
   const void* Q;
   const void* K;
   const void* V;
+  RowMap rmq, rmk, rmv;  // element strides of Q, K, V
   float* qbar;
   float* kbar;
   float* vbar;
@@ -35,19 +36,26 @@ struct PoolArgs {
   long long total_tasks;
 };
 
-// Mean of `rows` rows of d elements from `base` (16-byte chunk column c =
-// lane % CPR of each row): every lane of column c ends with the sums.  NT:
-// non-temporal loads (the streaming pass reads every input row once; the
-// hint keeps its 0.4 GB from cycling through the caches).
+// Mean of `rows` rows of d elements from `base`, rows `rs` bytes apart
+// (16-byte chunk column c = lane % CPR of each row): every lane of column c
+// ends with the sums.  NT: non-temporal loads (the streaming pass reads
+// every input row once; the hint keeps its 0.4 GB from cycling through the
+// caches).
 template <typename T, int D, bool NT>
-__device__ __forceinline__ void pool_rows(const char* base, int rows, float* acc) {
+__device__ __forceinline__ void pool_rows(const char* base, int rows, unsigned rs, float* acc) {
   constexpr int ES = sizeof(T);
   constexpr int CPR = D * ES / 16;     // 16-byte chunks per row
   constexpr int RG = 64 / CPR;         // rows in flight per wave
   constexpr int EPC = 16 / ES;         // elements per chunk
   const int lane = threadIdx.x & 63;
   const int c = lane % CPR, rg = lane / CPR;
-  base += c * 16;
+  // 32-bit offsets from the wave's (scalar) block base: rows < 2^24 and
+  // rs < 2^24, and a head spans less than 2^31 bytes.  The non-temporal
+  // loads go through a buffer descriptor of the block's rows (cache policy
+  // NT; anything past the last row reads as zero).
+  const unsigned coff = (unsigned)c * 16u;
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)((unsigned)(rows - 1) * rs + D * ES),
+                                                      0x00020000);
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
   // BATCH rows per lane are loaded before any is added (bytes in flight);
@@ -58,9 +66,13 @@ __device__ __forceinline__ void pool_rows(const char* base, int rows, float* acc
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       const int r = r0b + i * RG;
-      const u32x4* src = (const u32x4*)(base + (long long)r * D * ES);
-      if constexpr (NT) v[i] = r < rows ? __builtin_nontemporal_load(src) : u32x4{0u, 0u, 0u, 0u};
-      else v[i] = r < rows ? *src : u32x4{0u, 0u, 0u, 0u};
+      const unsigned off = __umul24((unsigned)r, rs) + coff;
+      if constexpr (NT) {
+        v[i] = r < rows ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 2))
+                        : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        v[i] = r < rows ? *(const u32x4*)(base + off) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
@@ -104,25 +116,28 @@ __global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
   constexpr int CPR = D * ES / 16;
   constexpr int EPC = 16 / ES;
   const int lane = threadIdx.x & 63;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // (the wave index through readfirstlane: the task is wave-uniform, so its
+  // row addresses are a scalar base plus per-lane offsets)
+  const long long task = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (task >= a.total_tasks) return;
   const long long bh = task / a.tasks_per_head;
   const int t = (int)(task - bh * a.tasks_per_head);
   const void* src;
+  const RowMap* m;
   float* dst;
   int blk;
-  long long nrows_head;
   if (t < a.nb_s) {
-    src = a.Q; dst = a.qbar + (bh * a.nb_s + t) * D; blk = t; nrows_head = a.Ns;
+    src = a.Q; m = &a.rmq; dst = a.qbar + (bh * a.nb_s + t) * D; blk = t;
   } else if (t < a.nb_s + a.M) {
-    blk = t - a.nb_s; src = a.K; dst = a.kbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
+    blk = t - a.nb_s; src = a.K; m = &a.rmk; dst = a.kbar + (bh * a.M + blk) * D;
   } else {
-    blk = t - a.nb_s - a.M; src = a.V; dst = a.vbar + (bh * a.M + blk) * D; nrows_head = a.Nk;
+    blk = t - a.nb_s - a.M; src = a.V; m = &a.rmv; dst = a.vbar + (bh * a.M + blk) * D;
   }
   int r0, rows;
   block_rows(a, blk, &r0, &rows);
   float acc[EPC];
-  pool_rows<T, D, true>((const char*)src + ((bh * nrows_head + r0) * D) * ES, rows, acc);
+  pool_rows<T, D, true>((const char*)src + (rm_head(*m, bh) + (long long)r0 * m->sn) * ES, rows,
+                        (unsigned)m->sn * ES, acc);
   if (lane < CPR) {
     const float n = (float)rows;
 #pragma unroll
@@ -145,7 +160,7 @@ __global__ __launch_bounds__(256) void isa_pool_pack_kernel(PoolArgs a) {
   constexpr int CPR = D * ES / 16;
   constexpr int EPC = 16 / ES;
   const int lane = threadIdx.x & 63;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long task = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (task >= a.total_tasks) return;
   const long long bh = task / a.mk_pad;
   const int p = (int)(task - bh * a.mk_pad);
@@ -164,7 +179,8 @@ __global__ __launch_bounds__(256) void isa_pool_pack_kernel(PoolArgs a) {
     const float* vb = a.vbar + (bh * a.M + j) * D;
     if (j >= a.nb_s) {
       float acc[EPC];
-      pool_rows<T, D, false>((const char*)a.V + ((bh * a.Nk + r0) * D) * ES, rows, acc);
+      pool_rows<T, D, false>((const char*)a.V + (rm_head(a.rmv, bh) + (long long)r0 * a.rmv.sn) * ES, rows,
+                             (unsigned)a.rmv.sn * ES, acc);
       const float n = (float)rows;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) v[e] = acc[e] / n;
@@ -217,6 +233,7 @@ __global__ __launch_bounds__(256) void isa_pool_pack_kernel(PoolArgs a) {
 static PoolArgs pool_args(const Layout& L, const Bufs& B) {
   PoolArgs a;
   a.Q = B.Q; a.K = B.K; a.V = B.V;
+  a.rmq = L.q; a.rmk = L.k; a.rmv = L.v;
   a.qbar = (float*)(B.ws + L.off_qbar);
   a.kbar = (float*)(B.ws + L.off_kbar);
   a.vbar = (float*)(B.ws + L.off_vbar);

@@ -38,10 +38,16 @@ BWD_STAGES = ["delta", "dk_pooled", "dv_pooled", "dkv_reduce", "dk_full", "dv_fu
 BWD_STAGE = {name: i for i, name in enumerate(BWD_STAGES)}
 
 
+class Strides(ctypes.Structure):
+    """isa_strides: element strides of the batch, head and row dimensions."""
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
 class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Ns", ctypes.c_int32), ("Nc", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("b", ctypes.c_int32), ("rho", ctypes.c_double),
-                ("gamma", ctypes.c_double), ("dtype", ctypes.c_int32)]
+                ("gamma", ctypes.c_double), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q", Strides), ("k", Strides), ("v", Strides), ("o", Strides)]
 
 
 class Counts(ctypes.Structure):
@@ -106,15 +112,27 @@ def _check(fn, code):
         raise IsaError(fn, code, detail)
 
 
-def make_desc(B, H, Ns, Nc, d, b, rho, gamma, dtype):
+def _strides(t):
+    """(b, h, n) element strides of a [B,H,rows,d] tensor view; None: contiguous."""
+    if t is None:
+        return None
+    return tuple(int(x) for x in t.stride()[:3])
+
+
+def make_desc(B, H, Ns, Nc, d, b, rho, gamma, dtype, q=None, k=None, v=None, o=None):
+    """isa_desc; q, k, v, o: (b, h, n) element strides of each tensor, None for
+    contiguous [B,H,rows,d]."""
     dt = {torch.bfloat16: ISA_BF16, torch.float32: ISA_F32, "bf16": ISA_BF16, "f32": ISA_F32}.get(dtype, dtype)
-    return Desc(int(B), int(H), int(Ns), int(Nc), int(d), int(b), float(rho), float(gamma), int(dt))
+    st = [Strides(*x) if x is not None else Strides(0, 0, 0) for x in (q, k, v, o)]
+    return Desc(int(B), int(H), int(Ns), int(Nc), int(d), int(b), float(rho), float(gamma), int(dt), 0, *st)
 
 
-def desc_for(Q, K, b, rho, gamma):
-    """Descriptor of Q [B,H,Ns,d], K [B,H,Ns+Nc,d] (torch tensors)."""
+def desc_for(Q, K, b, rho, gamma, V=None, O=None):
+    """Descriptor of Q [B,H,Ns,d], K (and V) [B,H,Ns+Nc,d] and O [B,H,Ns,d]
+    (torch tensors or views; their strides go into the descriptor)."""
     B, H, Ns, d = Q.shape
-    return make_desc(B, H, Ns, K.shape[2] - Ns, d, b, rho, gamma, Q.dtype)
+    return make_desc(B, H, Ns, K.shape[2] - Ns, d, b, rho, gamma, Q.dtype, _strides(Q), _strides(K),
+                     _strides(V if V is not None else K), _strides(O))
 
 
 def counts(desc):
@@ -139,23 +157,68 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _tensor(name, t, shape, like):
+    """t must be a 4-D device tensor (or view) of `shape`, the dtype and
+    device of `like`, with a unit-stride last dimension."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != like.dtype or t.device != like.device or not t.is_cuda:
+        raise ValueError("%s must be a %s tensor on %s" % (name, like.dtype, like.device))
+    if t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1):
+        raise ValueError("%s must be [B,H,rows,d] with d unit-stride" % name)
+
+
 def _inputs(Q, K, V):
-    for t in (Q, K, V):
-        if not (t.is_cuda and t.is_contiguous()):
-            raise ValueError("Q, K, V must be contiguous device tensors")
-    if not (Q.dtype == K.dtype == V.dtype):
-        raise ValueError("Q, K, V must share one dtype")
+    """Validates Q [B,H,Ns,d], K and V [B,H,Ns+Nc,d] (device tensors or
+    strided views of one dtype); returns (B, H, Ns, Nk, d)."""
+    if not isinstance(Q, torch.Tensor) or Q.dim() != 4 or not Q.is_cuda:
+        raise ValueError("Q must be a [B,H,Ns,d] device tensor")
+    if not isinstance(K, torch.Tensor) or K.dim() != 4:
+        raise ValueError("K must be a [B,H,Ns+Nc,d] device tensor")
+    B, H, Ns, d = Q.shape
+    Nk = K.shape[2]
+    if Nk < Ns:
+        raise ValueError("K has %d rows, fewer than Q's %d source rows" % (Nk, Ns))
+    _tensor("Q", Q, (B, H, Ns, d), Q)
+    _tensor("K", K, (B, H, Nk, d), Q)
+    _tensor("V", V, (B, H, Nk, d), Q)
+    return B, H, Ns, Nk, d
+
+
+def _output(name, t, shape, like):
+    """A caller's output tensor (validated), or a new contiguous one."""
+    if t is None:
+        return torch.empty(shape, dtype=like.dtype, device=like.device)
+    _tensor(name, t, shape, like)
+    return t
+
+
+def _workspace(name, ws, like, need):
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.device != like.device:
+        raise ValueError("%s must be a uint8 tensor on %s" % (name, like.device))
+    if not ws.is_contiguous() or ws.numel() < need:
+        raise ValueError("%s must be contiguous with at least %d bytes" % (name, need))
+    return ws
 
 
 def new_workspace(desc, device):
     return torch.empty(workspace_size(desc), dtype=torch.uint8, device=device)
 
 
+def _ws_for(desc, Q, workspace):
+    need = workspace_size(desc)
+    if workspace is None:
+        return new_workspace(desc, Q.device)
+    return _workspace("workspace", workspace, Q, need)
+
+
 def plan(Q, K, V, b, rho, gamma, workspace=None, stream=None):
     """isa_plan: returns the workspace holding the plan."""
     _inputs(Q, K, V)
-    desc = desc_for(Q, K, b, rho, gamma)
-    ws = new_workspace(desc, Q.device) if workspace is None else workspace
+    desc = desc_for(Q, K, b, rho, gamma, V=V)
+    ws = _ws_for(desc, Q, workspace)
     _check("isa_plan", lib().isa_plan(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(ws),
                                       ws.numel(), _stream(stream)))
     return ws
@@ -164,19 +227,22 @@ def plan(Q, K, V, b, rho, gamma, workspace=None, stream=None):
 def forward(Q, K, V, workspace, b, rho, gamma, out=None, stream=None):
     """isa_forward on a planned workspace: returns O."""
     _inputs(Q, K, V)
-    desc = desc_for(Q, K, b, rho, gamma)
-    O = torch.empty_like(Q) if out is None else out
+    O = _output("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=O)
+    ws = _workspace("workspace", workspace, Q, workspace_size(desc))
     _check("isa_forward", lib().isa_forward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
-                                            _ptr(workspace), workspace.numel(), _stream(stream)))
+                                            _ptr(ws), ws.numel(), _stream(stream)))
     return O
 
 
 def attention(Q, K, V, b, rho, gamma, out=None, workspace=None, stream=None):
-    """isa_attention (plan + forward in one call): returns (O, workspace)."""
+    """isa_attention (plan + forward in one call): returns (O, workspace).
+    Q, K, V (and out) may be strided views, e.g. X.transpose(1, 2) of a
+    [B,N,H,d] tensor."""
     _inputs(Q, K, V)
-    desc = desc_for(Q, K, b, rho, gamma)
-    ws = new_workspace(desc, Q.device) if workspace is None else workspace
-    O = torch.empty_like(Q) if out is None else out
+    O = _output("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=O)
+    ws = _ws_for(desc, Q, workspace)
     _check("isa_attention", lib().isa_attention(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
                                                 _ptr(ws), ws.numel(), _stream(stream)))
     return O, ws
@@ -185,8 +251,8 @@ def attention(Q, K, V, b, rho, gamma, out=None, workspace=None, stream=None):
 def dense_forward(Q, K, V, out=None, stream=None):
     """isa_dense_forward: dense attention of every source row over every key."""
     _inputs(Q, K, V)
-    desc = desc_for(Q, K, 1, 1.0, 1.0)
-    O = torch.empty_like(Q) if out is None else out
+    O = _output("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, 1, 1.0, 1.0, V=V, O=O)
     _check("isa_dense_forward", lib().isa_dense_forward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
                                                         _ptr(O), _stream(stream)))
     return O
@@ -195,14 +261,18 @@ def dense_forward(Q, K, V, out=None, stream=None):
 def context_forward(Qc, K, V, out=None, stream=None):
     """isa_context_forward: dense attention of the context query rows Qc
     [B,H,Nc,d] over all keys K, V [B,H,Ns+Nc,d]; returns Oc."""
-    B, H, Nc, d = Qc.shape
-    if K.shape[:2] != (B, H) or K.shape[3] != d or K.shape[2] < Nc or V.shape != K.shape:
+    if not isinstance(Qc, torch.Tensor) or Qc.dim() != 4 or not isinstance(K, torch.Tensor) or K.dim() != 4:
         raise ValueError("Qc [B,H,Nc,d] needs K and V [B,H,Ns+Nc,d]")
-    for t in (Qc, K, V):
-        if t.dtype != Qc.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("Qc, K, V must be contiguous device tensors of one dtype")
-    desc = make_desc(B, H, K.shape[2] - Nc, Nc, d, 1, 1.0, 1.0, Qc.dtype)
-    O = torch.empty_like(Qc) if out is None else out
+    B, H, Nc, d = Qc.shape
+    Nk = K.shape[2]
+    if Nk < Nc:
+        raise ValueError("K has %d rows, fewer than Qc's %d context rows" % (Nk, Nc))
+    _tensor("Qc", Qc, (B, H, Nc, d), Qc)
+    _tensor("K", K, (B, H, Nk, d), Qc)
+    _tensor("V", V, (B, H, Nk, d), Qc)
+    O = _output("out", out, Qc.shape, Qc)
+    desc = make_desc(B, H, Nk - Nc, Nc, d, 1, 1.0, 1.0, Qc.dtype, _strides(Qc), _strides(K), _strides(V),
+                     _strides(O))
     _check("isa_context_forward", lib().isa_context_forward(ctypes.byref(desc), _ptr(Qc), _ptr(K), _ptr(V), _ptr(O),
                                                             _stream(stream)))
     return O
@@ -210,30 +280,34 @@ def context_forward(Qc, K, V, out=None, stream=None):
 
 def run_stage(stage, Q, K, V, workspace, b, rho, gamma, out=None, stream=None):
     """isa_run_stage: one kernel of the layer (stage name or isa_stage value)."""
-    desc = desc_for(Q, K, b, rho, gamma)
+    _inputs(Q, K, V)
+    if out is not None:
+        _tensor("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=out)
+    ws = _workspace("workspace", workspace, Q, workspace_size(desc))
     code = STAGE[stage] if isinstance(stage, str) else int(stage)
     _check("isa_run_stage", lib().isa_run_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
-                                                _ptr(workspace), workspace.numel(), _stream(stream)))
+                                                _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
 def plan_views(Q, K, workspace, b, rho, gamma):
     """Tensor views of a planned workspace: dict of device tensors + counts."""
     desc = desc_for(Q, K, b, rho, gamma)
+    ws = _workspace("workspace", workspace, Q, workspace_size(desc))
     v = PlanView()
-    _check("isa_plan_views", lib().isa_plan_views(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
-                                                  ctypes.byref(v)))
+    _check("isa_plan_views", lib().isa_plan_views(ctypes.byref(desc), _ptr(ws), ws.numel(), ctypes.byref(v)))
     c = v.counts
     B, H, _, d = Q.shape
-    base = workspace.data_ptr()
+    base = ws.data_ptr()
 
     def view(ptr, dtype, shape):
         n = 1
-        for s in shape:
-            n *= s
+        for x in shape:
+            n *= x
         esz = torch.empty(0, dtype=dtype).element_size()
         off = ptr - base
-        return workspace[off:off + n * esz].view(dtype).view(*shape)
+        return ws[off:off + n * esz].view(dtype).view(*shape)
 
     return {
         "qbar": view(v.qbar, torch.float32, (B, H, c.nb_s, d)),
@@ -259,37 +333,50 @@ def new_backward_workspace(desc, device):
     return torch.empty(backward_workspace_size(desc), dtype=torch.uint8, device=device)
 
 
+def _grad(name, t, like):
+    """A gradient tensor laid out like `like` (its strides: the descriptor
+    has one set of strides per pair): the caller's, checked, or a new one."""
+    if t is None:
+        return torch.empty_strided(like.shape, like.stride(), dtype=like.dtype, device=like.device)
+    _tensor(name, t, like.shape, like)
+    if t.stride() != like.stride():
+        raise ValueError("%s must have the strides of its tensor (%s)" % (name, like.stride()))
+    return t
+
+
 def _bwd_args(Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma):
     _inputs(Q, K, V)
-    for t in (O, dO):
-        if t.shape != Q.shape or t.dtype != Q.dtype or not t.is_contiguous():
-            raise ValueError("O and dO must be contiguous and shaped and typed like Q")
-    desc = desc_for(Q, K, b, rho, gamma)
-    bws = new_backward_workspace(desc, Q.device) if bwd_workspace is None else bwd_workspace
-    dQ = torch.empty_like(Q) if dQ is None else dQ
-    dK = torch.empty_like(K) if dK is None else dK
-    dV = torch.empty_like(V) if dV is None else dV
-    return desc, bws, dQ, dK, dV
+    _tensor("O", O, Q.shape, Q)
+    _tensor("dO", dO, Q.shape, Q)
+    if dO.stride() != O.stride():
+        raise ValueError("dO must have the strides of O (%s)" % (O.stride(),))
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=O)
+    ws = _workspace("workspace", workspace, Q, workspace_size(desc))
+    bneed = backward_workspace_size(desc)
+    bws = new_backward_workspace(desc, Q.device) if bwd_workspace is None else \
+        _workspace("bwd_workspace", bwd_workspace, Q, bneed)
+    return desc, ws, bws, _grad("dQ", dQ, Q), _grad("dK", dK, K), _grad("dV", dV, V)
 
 
 def backward(Q, K, V, O, dO, workspace, b, rho, gamma, bwd_workspace=None, dQ=None, dK=None, dV=None, stream=None):
     """isa_backward: (dQ, dK, dV, bwd_workspace) of the layer planned in `workspace`
-    (from attention() or plan() + forward() on the same inputs), O its output."""
-    desc, bws, dQ, dK, dV = _bwd_args(Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma)
+    (from attention() or plan() + forward() on the same inputs), O its output.
+    dQ, dK, dV have the strides of Q, K, V and dO those of O."""
+    desc, ws, bws, dQ, dK, dV = _bwd_args(Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma)
     _check("isa_backward", lib().isa_backward(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
-                                              _ptr(workspace), workspace.numel(), _ptr(bws), bws.numel(),
+                                              _ptr(ws), ws.numel(), _ptr(bws), bws.numel(),
                                               _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)))
     return dQ, dK, dV, bws
 
 
 def run_backward_stage(stage, Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma, stream=None):
     """isa_run_backward_stage: one kernel of the backward pass (name or isa_bwd_stage value)."""
-    desc = desc_for(Q, K, b, rho, gamma)
+    desc, ws, bws, dQ, dK, dV = _bwd_args(Q, K, V, O, dO, workspace, bwd_workspace, dQ, dK, dV, b, rho, gamma)
     code = BWD_STAGE[stage] if isinstance(stage, str) else int(stage)
     _check("isa_run_backward_stage",
            lib().isa_run_backward_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
-                                        _ptr(workspace), workspace.numel(), _ptr(bwd_workspace),
-                                        bwd_workspace.numel(), _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)))
+                                        _ptr(ws), ws.numel(), _ptr(bws), bws.numel(), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                        _stream(stream)))
 
 
 FP8_STAGES = ["pack", "full", "full_merge"]
@@ -304,11 +391,12 @@ def fp8_workspace_size(desc):
 def attention_fp8(Q, K, V, b, rho, gamma, out=None, workspace=None, fp8_workspace=None, stream=None):
     """isa_attention_fp8: the layer with the full route in e4m3; returns (O, workspace, fp8_workspace)."""
     _inputs(Q, K, V)
-    desc = desc_for(Q, K, b, rho, gamma)
-    ws = new_workspace(desc, Q.device) if workspace is None else workspace
-    fws = (torch.empty(fp8_workspace_size(desc), dtype=torch.uint8, device=Q.device)
-           if fp8_workspace is None else fp8_workspace)
-    O = torch.empty_like(Q) if out is None else out
+    O = _output("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=O)
+    ws = _ws_for(desc, Q, workspace)
+    fneed = fp8_workspace_size(desc)
+    fws = torch.empty(fneed, dtype=torch.uint8, device=Q.device) if fp8_workspace is None else \
+        _workspace("fp8_workspace", fp8_workspace, Q, fneed)
     _check("isa_attention_fp8", lib().isa_attention_fp8(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
                                                         _ptr(ws), ws.numel(), _ptr(fws), fws.numel(), _stream(stream)))
     return O, ws, fws
@@ -316,8 +404,13 @@ def attention_fp8(Q, K, V, b, rho, gamma, out=None, workspace=None, fp8_workspac
 
 def run_fp8_stage(stage, Q, K, V, workspace, fp8_workspace, b, rho, gamma, out=None, stream=None):
     """isa_run_fp8_stage: one kernel of the FP8 full route (name or isa_fp8_stage value)."""
-    desc = desc_for(Q, K, b, rho, gamma)
+    _inputs(Q, K, V)
+    if out is not None:
+        _tensor("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=out)
+    ws = _workspace("workspace", workspace, Q, workspace_size(desc))
+    fws = _workspace("fp8_workspace", fp8_workspace, Q, fp8_workspace_size(desc))
     code = FP8_STAGES.index(stage) if isinstance(stage, str) else int(stage)
-    _check("isa_run_fp8_stage", lib().isa_run_fp8_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
-                                                        _ptr(workspace), workspace.numel(), _ptr(fp8_workspace),
-                                                        fp8_workspace.numel(), _stream(stream)))
+    _check("isa_run_fp8_stage", lib().isa_run_fp8_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V),
+                                                        _ptr(out), _ptr(ws), ws.numel(), _ptr(fws), fws.numel(),
+                                                        _stream(stream)))

@@ -6,6 +6,8 @@ import ctypes
 import math
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -153,3 +155,85 @@ def test_backward_workspace_sizes_of_the_workloads():
             continue
         d = isa.make_desc(w.B, w.H, w.Ns, w.Nc, w.d, w.b, w.rho, w.gamma, w.dtype)
         assert 0 < isa.backward_workspace_size(d) < 2e9
+
+
+# ---------------------------------------------------------------------------
+# strided tensors (isa_desc.q/.k/.v/.o) and the limits of the kernels'
+# addressing, all decided on the host before any launch
+
+def _sdesc(**kw):
+    base = dict(B=1, H=4, Ns=300, Nc=200, d=128, b=16, rho=0.5, gamma=0.25, dtype="bf16")
+    st = {k: kw.pop(k) for k in ("q", "k", "v", "o") if k in kw}
+    base.update(kw)
+    return isa.make_desc(**base, **st)
+
+
+def test_token_major_strides_are_accepted():
+    # [B,N,H,d] views: tokens before heads
+    H, d, Ns, Nk = 4, 128, 300, 500
+    d1 = _sdesc(q=(Ns * H * d, d, H * d), k=(Nk * H * d, d, H * d), v=(Nk * H * d, d, H * d),
+                o=(Ns * H * d, d, H * d))
+    assert isa.workspace_size(d1) == isa.workspace_size(_sdesc())
+    # one fused QKV buffer [B,N,3,H,d]: rows 3*H*d apart
+    d2 = _sdesc(Nc=0, q=(Ns * 3 * H * d, d, 3 * H * d), k=(Ns * 3 * H * d, d, 3 * H * d),
+                v=(Ns * 3 * H * d, d, 3 * H * d))
+    assert isa.workspace_size(d2) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=(0, 0, -128)), 1),                    # negative stride
+    (dict(k=(500 * 4 * 136, 500 * 136, 130)), 1),  # 260-byte rows: not 16-byte aligned
+    (dict(q=(300 * 4 * 128, 12, 128)), 1),         # head stride of 24 bytes
+    (dict(o=(300 * 4 * 128, 300 * 128, 64)), 1),   # O rows overlap
+    (dict(o=(128, 0, 512)), 1),                    # all heads of O on one range
+    (dict(k=(500 * 4 * (1 << 23), 500 * (1 << 23), 1 << 23)), 2),   # row step of 2^24 bytes
+    (dict(k=(0, 500 * 5000000, 5000000)), 2),      # a head of K spans over 2^31 bytes
+    (dict(B=256, H=256), 2),                       # B*H = 65536
+    (dict(Ns=(1 << 24) - 10, Nc=10, d=64), 2),     # Ns + Nc = 2^24
+])
+def test_bad_strides_and_limits_rejected(kw, code):
+    with pytest.raises(isa.IsaError) as e:
+        isa.workspace_size(_sdesc(**kw))
+    assert e.value.code == code
+
+
+def test_overlapping_inputs_are_valid_but_not_as_gradients():
+    """Q rows that overlap are a valid read-only input, but isa_backward
+    writes dQ through Q's strides and must refuse them."""
+    d = _sdesc(q=(300 * 4 * 128, 300 * 128, 64))
+    need = isa.workspace_size(d)
+    bneed = isa.backward_workspace_size(d)
+    host = ctypes.create_string_buffer(need + bneed + 1024)
+    base = (ctypes.addressof(host) + 255) // 256 * 256
+    ws = ctypes.c_void_p(base)
+    bws = ctypes.c_void_p(base + (need + 255) // 256 * 256)
+    p = ctypes.c_void_p(base)   # never dereferenced: the call fails validation
+    nul = ctypes.c_void_p(0)
+    L = isa.lib()
+    assert L.isa_backward(ctypes.byref(d), p, p, p, p, p, ws, need, bws, bneed, p, p, p, nul) == 1
+
+
+def test_reserved_field_must_be_zero():
+    d = _sdesc()
+    d.reserved = 3
+    with pytest.raises(isa.IsaError) as e:
+        isa.workspace_size(d)
+    assert e.value.code == 1
+
+
+def test_planner_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """tests/host/abi_check.cpp with the planner and the validation code
+    (isa_layout.cpp), built by g++ with ASan + UBSan: every workspace slice of
+    a grid of descriptors, the output-overlap test against brute force, the
+    multiply that replaces the head division, random descriptors."""
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "abi_check")
+    src = [os.path.join(ROOT, "sparse_attention_context_amd", "csrc", "isa_layout.cpp"),
+           os.path.join(ROOT, "tests", "host", "abi_check.cpp")]
+    subprocess.run(["g++", "-std=c++17", "-g", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-I" + os.path.join(ROOT, "include")] + src + ["-o", exe], check=True)
+    r = subprocess.run([exe], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"), capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "abi_check ok" in r.stdout
