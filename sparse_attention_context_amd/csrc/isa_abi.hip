@@ -158,8 +158,14 @@ extern "C" isa_status isa_run_fp8_stage(const isa_desc* desc, int stage, const v
 
 extern "C" isa_status isa_context_forward(const isa_desc* desc, const void* Qc, const void* K, const void* V,
                                           void* Oc, void* stream) {
+  if (!desc) return ISA_ERR_INVALID_ARGUMENT;
+  // Q and O hold the Nc context rows here: their strides are checked against
+  // that row count by context_maps, not as source rows by make_layout
+  isa_desc D = *desc;
+  D.q = isa_strides{0, 0, 0};
+  D.o = isa_strides{0, 0, 0};
   isa::Layout L;
-  isa_status st = isa::make_layout(desc, &L);
+  isa_status st = isa::make_layout(&D, &L);
   if (st != ISA_OK) return st;
   if (L.es != 2) return ISA_ERR_UNSUPPORTED;
   if ((st = isa::context_maps(desc, &L)) != ISA_OK) return st;

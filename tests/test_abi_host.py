@@ -237,3 +237,24 @@ def test_planner_under_address_and_undefined_behaviour_sanitizers(tmp_path):
                        timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "abi_check ok" in r.stdout
+
+
+def test_context_rows_strides_are_checked_against_their_row_count():
+    """isa_context_forward's Qc and Oc hold Nc rows: their strides are
+    validated for Nc rows (an output whose heads would overlap as Ns rows is
+    fine), and overlapping Oc rows are refused before any launch."""
+    B, H, Ns, Nc, d = 1, 4, 300, 200, 128
+    L = isa.lib()
+    host = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p((ctypes.addressof(host) + 255) // 256 * 256)   # never dereferenced
+    nul = ctypes.c_void_p(0)
+    bad = isa.make_desc(B, H, Ns, Nc, d, 1, 1.0, 1.0, "bf16", o=(H * Nc * d, Nc * d, 64))
+    assert L.isa_context_forward(ctypes.byref(bad), p, p, p, p, nul) == 1
+    bad_q = isa.make_desc(B, H, Ns, Nc, d, 1, 1.0, 1.0, "bf16", q=(H * Nc * d, Nc * d, 65))
+    assert L.isa_context_forward(ctypes.byref(bad_q), p, p, p, p, nul) == 1
+    import torch
+    if not torch.cuda.is_available():
+        # valid for Nc rows: passes validation and fails only at the launch
+        # (no device here)
+        ok = isa.make_desc(B, H, Ns, Nc, d, 1, 1.0, 1.0, "bf16", q=(H * Nc * d, Nc * d, d), o=(H * Nc * d, Nc * d, d))
+        assert L.isa_context_forward(ctypes.byref(ok), p, p, p, p, nul) == 4
