@@ -179,15 +179,8 @@ def time_fp8(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(isa.FP8_STAGES) + 1)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        for i, name in enumerate(isa.FP8_STAGES):
-            evs[k][i].record(stream)
-            isa.run_fp8_stage(name, Qd, Kd, Vd, ws8, fws, w.b, w.rho, gamma, out=O8)
-        evs[k][-1].record(stream)
-    torch.cuda.synchronize()
-    st = {name: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) / args.steps
-          for i, name in enumerate(isa.FP8_STAGES)}
+    st = time_stage_pass(lambda name: isa.run_fp8_stage(name, Qd, Kd, Vd, ws8, fws, w.b, w.rho, gamma, out=O8),
+                         isa.FP8_STAGES, args.steps, stream)
     flops = full_route_flops(views, w, gamma)
     tf = flops / (st["full"] * 1e-3) / 1e12 if st.get("full") else None
     log("isa_attention_fp8: %.3f ms/call; full-route stages: %s" % (ms, ", ".join("%s %.3f" % kv for kv in st.items())))
@@ -223,16 +216,8 @@ def time_backward(args, w, gamma, Qd, Kd, Vd, O, ws, views, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.backward_steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(isa.BWD_STAGES) + 1)]
-           for _ in range(args.backward_steps)]
-    for k in range(args.backward_steps):
-        for i, name in enumerate(isa.BWD_STAGES):
-            evs[k][i].record(stream)
-            isa.run_backward_stage(name, Qd, Kd, Vd, O, dO, ws, bws, dQ, dK, dV, w.b, w.rho, gamma)
-        evs[k][-1].record(stream)
-    torch.cuda.synchronize()
-    st = {name: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.backward_steps)) / args.backward_steps
-          for i, name in enumerate(isa.BWD_STAGES)}
+    st = time_stage_pass(lambda name: isa.run_backward_stage(name, Qd, Kd, Vd, O, dO, ws, bws, dQ, dK, dV, w.b, w.rho,
+                                                             gamma), isa.BWD_STAGES, args.backward_steps, stream)
     log("isa_backward: %.3f ms/call; stages: %s" % (ms, ", ".join("%s %.3f" % kv for kv in st.items())))
     pairs = full_route_flops(views, w, gamma) // (4 * w.d)
     # per (query, key) pair of the full route: dK kernel S, dP, dK (6 d); dV kernel S, dV (4 d); dQ kernel S, dP, dQ (6 d)
@@ -271,6 +256,26 @@ def time_steps(fn, steps, stream, flush):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
+def time_stage_pass(run, names, steps, stream):
+    """Per-stage milliseconds: HIP events between the stages of one stream,
+    one untimed pass first, then `steps` passes; the median over the passes
+    (a pass whose host launches fell behind the GPU shows up as an outlier,
+    which the median ignores)."""
+    import torch
+    for name in names:
+        run(name)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for s in range(steps):
+        for i, name in enumerate(names):
+            evs[s][i].record(stream)
+            run(name)
+        evs[s][-1].record(stream)
+    torch.cuda.synchronize()
+    return {name: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]))
+            for i, name in enumerate(names)}
+
+
 def summary(ms_list):
     a = np.asarray(ms_list, dtype=np.float64)
     return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
@@ -292,10 +297,9 @@ def time_other_workloads(args, stream, flush):
             continue
         Qd, Kd, Vd = make_inputs_device(w.B, w.H, w.d, w.Ns, w.Nc, w.seed, dev, w.dtype, w.clips, w.sharp)
         O = torch.empty_like(Qd)
-        dense = None
-        if w.dtype == "bf16":
-            isa.dense_forward(Qd, Kd, Vd, out=O)
-            dense = float(np.median(time_steps(lambda: isa.dense_forward(Qd, Kd, Vd, out=O), 3, stream, flush)))
+        # the dense kernel takes f32 too
+        isa.dense_forward(Qd, Kd, Vd, out=O)
+        dense = float(np.median(time_steps(lambda: isa.dense_forward(Qd, Kd, Vd, out=O), 3, stream, flush)))
         for g in (w.gammas or (w.gamma,)):
             desc = isa.desc_for(Qd, Kd, w.b, w.rho, g)
             ws = isa.new_workspace(desc, dev)
@@ -313,16 +317,8 @@ def time_other_workloads(args, stream, flush):
                 names = list(isa.ATTENTION_STAGES)
                 if views["counts"]["kq"] == views["counts"]["nb_s"]:
                     names[names.index("sharp_taylor")] = "sharp"
-                per = []
-                for _ in range(3):
-                    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-                    for i, name in enumerate(names):
-                        evs[i].record(stream)
-                        isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, g, out=O)
-                    evs[-1].record(stream)
-                    torch.cuda.synchronize()
-                    per.append(evs[names.index("full")].elapsed_time(evs[names.index("full") + 1]))
-                full_ms = float(np.median(per))
+                full_ms = time_stage_pass(lambda name: isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, g, out=O),
+                                          names, 3, stream)["full"]
             c = summary(cold)
             rec = {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Ns": w.Ns, "Nc": w.Nc, "b": w.b, "rho": w.rho,
                    "gamma": g, "dtype": w.dtype, "kc": views["counts"]["kc"], "kq": views["counts"]["kq"],
@@ -407,16 +403,18 @@ def main():
         names = list(isa.ATTENTION_STAGES)
         if counts["kq"] == counts["nb_s"]:
             names[names.index("sharp_taylor")] = "sharp"
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-        for s in range(args.steps):
-            for i, name in enumerate(names):
-                evs[s][i].record(stream)
-                isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, gamma, out=O)
-            evs[s][-1].record(stream)
-        torch.cuda.synchronize()
-        for i, name in enumerate(names):
-            stage_ms[name] = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
-        log("stages: " + ", ".join("%s %.3f" % kv for kv in stage_ms.items()))
+        stage_ms = time_stage_pass(lambda name: isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, gamma, out=O),
+                                   names, args.steps, stream)
+        log("stages (median of %d passes): %s" % (args.steps, ", ".join("%s %.3f" % kv for kv in stage_ms.items())))
+    # host time to enqueue one call (the binding's argument checks and the
+    # library's launches), against which the GPU time per call is measured
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        step()
+    host_us = (time.perf_counter() - t0) / 10 * 1e6
+    torch.cuda.synchronize()
+    log("host time to enqueue one isa_attention call: %.1f us" % host_us)
 
     dense_ms = None
     if not args.no_dense and w.dtype == "bf16":
@@ -504,7 +502,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "timing": dict(summary(cold), warm_median_ms=round(float(np.median(warm)), 4),
+        "timing": dict(summary(cold), warm_median_ms=round(float(np.median(warm)), 4), host_enqueue_us=round(host_us, 1),
                        protocol="HIP events around each step on the launch stream; a 1 GiB write before each "
                                 "step (outside the events) flushes L2 and the Infinity Cache; value and "
                                 "ms_per_step use the median"),

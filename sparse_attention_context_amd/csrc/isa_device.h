@@ -8,6 +8,13 @@
 
 namespace isa {
 
+// A wave-uniform 64-bit value (read from LDS, say) moved to scalar registers.
+__device__ __forceinline__ long long uniform64(long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // First element of slice bh = x*H + h of a caller tensor addressed by m
 // (bh < 2^16; x by the multiply of RowMap.hmul, no division).
 __device__ __forceinline__ long long rm_head(const RowMap& m, long long bh) {

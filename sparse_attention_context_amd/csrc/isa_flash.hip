@@ -825,6 +825,11 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   __shared__ __attribute__((aligned(16))) int stab[8][4][64];         // per-wave key-table ring
   __shared__ int sq[8][kPpsMaxItems][64];                             // query row of each lane and item
   __shared__ int snv[kPpsMaxItems];                                   // valid keys of each item's head
+  // per item: byte offsets of its head in Q, O and K (= V, whose row map is
+  // K's here), and the Q and O row steps.  Read from LDS where an item starts
+  // or ends, so that the strides hold no registers across the tile loop.
+  __shared__ long long shead[3][kPpsMaxItems];
+  __shared__ unsigned sstep[2];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
@@ -852,7 +857,14 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     if (tid == 0) {
       const bool tail_kept = a.kc > 0 && a.kept[(long long)it.bh * a.kc + a.kc - 1] == a.nb_c - 1;
       snv[r] = n_keys - (tail_kept ? a.b - a.tail_c : 0);
+      shead[0][r] = rm_head(a.rmq, it.bh) * 2;
+      shead[1][r] = rm_head(a.rmo, it.bh) * 2;
+      shead[2][r] = rm_head(a.rmk, it.bh) * 2;
     }
+  }
+  if (tid == 0) {
+    sstep[0] = (unsigned)a.rmq.sn * 2u;
+    sstep[1] = (unsigned)a.rmo.sn * 2u;
   }
   __syncthreads();
 
@@ -871,9 +883,10 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   };
 
   Op qB[D / 16];
-  auto load_q = [&](int r, int bh) {
+  auto load_q = [&](int r) {
     const int qrow = sq[w][r][lane];
-    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
+    const bf16_t* qp =
+        (const bf16_t*)((const char*)a.Q + shead[0][r] + (long long)(qrow < 0 ? 0 : qrow) * sstep[0]) + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
   };
@@ -902,9 +915,9 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   // K and V share one row map here (the launch checks it): head hd's rows
   // start rm_head(mk, hd) elements into each, rs bytes apart
   const unsigned rs = (unsigned)a.rmk.sn * 2u;
-  auto head_off = [&](int hd) { return rm_head(a.rmk, hd) * 2; };
-  auto issue_tile = [&](unsigned ring, int stage, const void* base, int bh, Rows rows) {
-    const char* G0 = (const char*)base + head_off(bh);
+  auto head_off = [&](int r) { return uniform64(shead[2][r]); };   // of item r
+  auto issue_tile = [&](unsigned ring, int stage, const void* base, int r, Rows rows) {
+    const char* G0 = (const char*)base + head_off(r);
     const unsigned d0 = ring + wrow + (unsigned)stage * TB;
     dma16x2(d0, d0 + 4 * RB, G0, __umul24((unsigned)rows.r[0], rs) + lchunk[0],
             __umul24((unsigned)rows.r[1], rs) + lchunk[1]);
@@ -1052,9 +1065,9 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     const float l_tot = l_run + wave_shfl_xor(l_run, 32);
     const int qrow = sq[w][r][lane];
     if (a.nsplit == 1) {
-      const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + rm_head(a.rmo, it.bh), (short)0, a.o_span,
+      const auto rO = __builtin_amdgcn_make_buffer_rsrc((char*)a.O + uniform64(shead[1][r]), (short)0, a.o_span,
                                                         0x00020000);
-      store_rows(rO, qrow >= 0 ? (unsigned)qrow * ((unsigned)a.rmo.sn * 2u) : kOut, 1.0f / l_tot);
+      store_rows(rO, qrow >= 0 ? (unsigned)qrow * sstep[1] : kOut, 1.0f / l_tot);
       const auto rL = __builtin_amdgcn_make_buffer_rsrc(a.lse ? a.lse + (long long)it.bh * a.Ns : a.lse, (short)0,
                                                         a.lse ? a.Ns * 4 : 0, 0x00020000);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref * sc + __builtin_log2f(l_tot)), rL,
@@ -1086,7 +1099,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   int total = 0;
   for (int r = 0; r < nr; ++r) total += item_of(r).nt;
   const Item it0 = item_of(0);
-  load_q(0, it0.bh);
+  load_q(0);
   auto cp = [&](int s) { return min(s, total - 1); };   // slot positions past the end clamp
   // cursors: compute (step s), K (s + 3), V (s + 2), table (s + 6)
   Cursor cc = cursor0(), ck = cursor0(), cv = cursor0(), ct = cursor0();
@@ -1100,11 +1113,11 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     const Rows r0 = rows_of(0), r1 = rows_of(1);
     rv = rows_of(2);
     rk = rows_of(3);
-    issue_tile(lds_k, 0, a.K, ck.it.bh, r0); advance(ck);
-    issue_tile(lds_v, 0, a.V, cv.it.bh, r0); advance(cv);
-    issue_tile(lds_k, 1, a.K, ck.it.bh, r1); advance(ck);
-    issue_tile(lds_v, 1, a.V, cv.it.bh, r1); advance(cv);
-    issue_tile(lds_k, 2, a.K, ck.it.bh, rv); advance(ck);   // (V(2) is loaded by the first step)
+    issue_tile(lds_k, 0, a.K, ck.r, r0); advance(ck);
+    issue_tile(lds_v, 0, a.V, cv.r, r0); advance(cv);
+    issue_tile(lds_k, 1, a.K, ck.r, r1); advance(ck);
+    issue_tile(lds_v, 1, a.V, cv.r, r1); advance(cv);
+    issue_tile(lds_k, 2, a.K, ck.r, rv); advance(ck);   // (V(2) is loaded by the first step)
     fetch_rows(4, ct); advance(ct);
     fetch_rows(5, ct); advance(ct);
     u32x4* vz = (u32x4*)(smem + NST * TB + 3 * TB);
@@ -1150,13 +1163,13 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       ++cc.k;
       __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
     } else {
-      issue_step(Z, head_off(ck.it.bh), head_off(cv.it.bh), cp(s + 6), ct);
+      issue_step(Z, head_off(ck.r), head_off(cv.r), cp(s + 6), ct);
       const Rows rn = rows_of(cp(s + 4));
       if (s < total) P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
       rv = rk;
       rk = rn;
       const bool next_item = LAST && cc.r + 1 < nr;
-      if (next_item) load_q(cc.r + 1, item_of(cc.r + 1).bh);
+      if (next_item) load_q(cc.r + 1);
       advance(cc);
       advance(ck);
       advance(cv);
@@ -1175,7 +1188,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   for (int r = 0; r < nr; ++r) {
     const int ntr = cc.it.nt;   // >= kPpsMinTiles
     const int nv = snv[r];
-    const long long ho = head_off(cc.it.bh);   // the item's K and V rows (inner steps)
+    const long long ho = head_off(r);   // the item's K and V rows (inner steps)
     step(s++, T_{}, F_{}, F_{}, nv, ho);
     // K, V and table positions stay in the item while k + 6 < ntr
     for (int k = 1; k + 6 < ntr; ++k) step(s++, F_{}, F_{}, T_{}, nv, ho);
@@ -1224,10 +1237,18 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   // Khi ring, Klo ring, V ring
   __shared__ __attribute__((aligned(1024))) char smem[3 * NST * TB];
   __shared__ __attribute__((aligned(256))) float sbias[NST][BN];
+  // the Q and O row maps, read from LDS where a row tile starts or ends, so
+  // that they hold no registers across the tile loop
+  __shared__ RowMap smap[2];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
+  if (tid == 0) {
+    smap[0] = a.rmq;
+    smap[1] = a.rmo;
+  }
+  __syncthreads();
   const int G = gridDim.x;
   const int n_tiles = a.n_wg;                  // row tiles over all heads
   const int nr = n_tiles > (int)blockIdx.x ? (n_tiles - 1 - (int)blockIdx.x) / G + 1 : 0;
@@ -1241,7 +1262,8 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   };
   auto load_q = [&](int ri, Op* q) {
     const int qr = query_row(ri);
-    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, tile_bh(ri)) + (long long)(qr < 0 ? 0 : qr) * a.rmq.sn + 8 * h;
+    const RowMap m = smap[0];
+    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(m, tile_bh(ri)) + (long long)(qr < 0 ? 0 : qr) * m.sn + 8 * h;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) q[s] = *(const Op*)(qp + 16 * s);
   };
@@ -1391,8 +1413,10 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     const long long bh = tile_bh(ri);
     const float inv = 1.0f / l_tot;
     constexpr unsigned kOut = 0x80000000u;   // beyond every buffer below (each under 2^31 bytes)
-    const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + rm_head(a.rmo, bh), (short)0, a.o_span, 0x00020000);
-    const unsigned oo = qr >= 0 ? (unsigned)qr * ((unsigned)a.rmo.sn * 2u) : kOut;
+    const RowMap m = smap[1];
+    const auto rO = __builtin_amdgcn_make_buffer_rsrc((bf16_t*)a.O + uniform64(rm_head(m, bh)), (short)0, a.o_span,
+                                                      0x00020000);
+    const unsigned oo = qr >= 0 ? (unsigned)qr * ((unsigned)m.sn * 2u) : kOut;
     // 16-byte chunk c = d / 8 = 4t + g of the row: lanes l and l + 32 hold
     // its halves.  For the chunk pair (2k, 2k + 1) one permlane32 swap per
     // word gives lane l all of chunk 2k and lane l + 32 all of chunk 2k + 1,
