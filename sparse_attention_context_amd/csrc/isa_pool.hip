@@ -121,22 +121,24 @@ __global__ __launch_bounds__(256) void isa_pool_kernel(PoolArgs a) {
   if (task >= a.total_tasks) return;
   const long long bh = task / a.tasks_per_head;
   const int t = (int)(task - bh * a.tasks_per_head);
+  // (the row map is selected by value: a pointer into the argument block
+  // would make the compiler copy the whole block to scratch memory)
   const void* src;
-  const RowMap* m;
+  RowMap m;
   float* dst;
   int blk;
   if (t < a.nb_s) {
-    src = a.Q; m = &a.rmq; dst = a.qbar + (bh * a.nb_s + t) * D; blk = t;
+    src = a.Q; m = a.rmq; dst = a.qbar + (bh * a.nb_s + t) * D; blk = t;
   } else if (t < a.nb_s + a.M) {
-    blk = t - a.nb_s; src = a.K; m = &a.rmk; dst = a.kbar + (bh * a.M + blk) * D;
+    blk = t - a.nb_s; src = a.K; m = a.rmk; dst = a.kbar + (bh * a.M + blk) * D;
   } else {
-    blk = t - a.nb_s - a.M; src = a.V; m = &a.rmv; dst = a.vbar + (bh * a.M + blk) * D;
+    blk = t - a.nb_s - a.M; src = a.V; m = a.rmv; dst = a.vbar + (bh * a.M + blk) * D;
   }
   int r0, rows;
   block_rows(a, blk, &r0, &rows);
   float acc[EPC];
-  pool_rows<T, D, true>((const char*)src + (rm_head(*m, bh) + (long long)r0 * m->sn) * ES, rows,
-                        (unsigned)m->sn * ES, acc);
+  pool_rows<T, D, true>((const char*)src + (rm_head(m, bh) + (long long)r0 * m.sn) * ES, rows,
+                        (unsigned)m.sn * ES, acc);
   if (lane < CPR) {
     const float n = (float)rows;
 #pragma unroll
