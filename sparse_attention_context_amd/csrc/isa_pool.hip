@@ -49,30 +49,37 @@ __device__ __forceinline__ void pool_rows(const char* base, int rows, unsigned r
   constexpr int EPC = 16 / ES;         // elements per chunk
   const int lane = threadIdx.x & 63;
   const int c = lane % CPR, rg = lane / CPR;
-  // 32-bit offsets from the wave's (scalar) block base: rows < 2^24 and
-  // rs < 2^24, and a head spans less than 2^31 bytes.  The loads go through
-  // a buffer descriptor of the block's rows (anything past it reads as
-  // zero), non-temporal (cache policy NT) for the streaming pass.
+  // Row offsets: rows < 2^24 and rs < 2^24, and a head spans less than 2^31
+  // bytes.  The streaming pass (NT) loads with non-temporal global loads,
+  // a row past the block not at all; the packing pass loads through a
+  // buffer descriptor of the block's rows (anything past it reads as zero),
+  // unconditionally.  (Measured on the video-DiT layer: each form is the
+  // faster one for its pass.)
   const unsigned coff = (unsigned)c * 16u;
-  // (every value of the descriptor is wave-uniform: readfirstlane says so)
+  // (every value of the descriptor is wave-uniform: readfirstlane says so;
+  // the streaming pass does not use it)
   const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform64((long long)base), (short)0,
       (int)__builtin_amdgcn_readfirstlane((unsigned)(rows - 1) * rs + D * ES), 0x00020000);
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
   // BATCH rows per lane are loaded before any is added (bytes in flight);
-  // each lane still adds its rows in increasing order.  Loads and adds are
-  // unconditional (so that no load waits inside a branch); a row past the
-  // block is zeroed by a select, so it adds nothing.
+  // each lane adds its rows in increasing order, a row past the block as
+  // zero.
   constexpr int BATCH = 16;
   for (int r0b = rg; r0b < rows; r0b += RG * BATCH) {
     u32x4 v[BATCH];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       const int r = r0b + i * RG;
-      const unsigned off = __umul24((unsigned)r, rs) + coff;
-      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, NT ? 2 : 0));
-      v[i] = r < rows ? x : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (NT) {
+        const u32x4* src = (const u32x4*)(base + (long long)r * rs + coff);
+        v[i] = r < rows ? __builtin_nontemporal_load(src) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const unsigned off = __umul24((unsigned)r, rs) + coff;
+        const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+        v[i] = r < rows ? x : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
