@@ -29,10 +29,11 @@ def _host_views(views):
     return {k: (v.cpu().numpy() if hasattr(v, "cpu") else v) for k, v in views.items()}
 
 
-def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True):
+def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol=BAND):
     """Checks pooled means, scores and index sets of one (batch, head) of a
-    GPU run (host views hv) against the oracle.  Returns the head's figures
-    and its GPU lists (kept, full)."""
+    GPU run (host views hv) against the oracle.  Scores must lie within
+    score_tol of the oracle's (at most the 1e-6 band of the set check).
+    Returns the head's figures and its GPU lists (kept, full)."""
     Ns = Qh.shape[0]
     Nc = Kh.shape[0] - Ns
     ref = orc.oracle_plan_head(Qh, Kh, Vh, b, rho, gamma)
@@ -46,17 +47,18 @@ def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True):
     if check_pool:
         qbar = hv["qbar"][x, h].astype(np.float64)
         kbar = hv["kbar"][x, h].astype(np.float64)
-        vbar = hv["vbar"][x, h].astype(np.float64)
         have = list(range(nb_s)) + [nb_s + int(c) for c in kept]
+        # (pooled values of pruned context blocks are never computed)
+        vbar = hv["vbar"][x, h][have].astype(np.float64)
         errs = [np.abs(qbar - ref["qbar"]).max(initial=0.0), np.abs(kbar - ref["kbar"]).max(initial=0.0),
-                np.abs(vbar[have] - ref["vbar"][have]).max(initial=0.0)]
+                np.abs(vbar - ref["vbar"][have]).max(initial=0.0)]
         stats["pool_err"] = float(max(errs))
         assert stats["pool_err"] <= 2e-6, errs
 
     sal = hv["sal"][x, h]
     if nb_c:
         stats["sal_err"] = float(np.max(np.abs(sal - ref["sal"])))
-        assert stats["sal_err"] < BAND, stats["sal_err"]
+        assert stats["sal_err"] < score_tol, stats["sal_err"]
     stats["amb_ctx"] = check_set(kept, ref["sal"], kc)
 
     # sharpness against the oracle on the GPU's kept set
@@ -65,7 +67,7 @@ def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True):
     sh = hv["sh"][x, h]
     # scores must sit closer to the oracle than the band the set check excludes
     stats["sh_err"] = float(np.max(np.abs(sh - sh_ref)))
-    assert stats["sh_err"] < BAND, stats["sh_err"]
+    assert stats["sh_err"] < score_tol, stats["sh_err"]
     stats["amb_q"] = check_set(full, sh_ref, kq)
     assert sorted(set(full.tolist()) | set(tayl.tolist())) == list(range(nb_s))
     assert tayl.tolist() == sorted(tayl.tolist())
@@ -209,6 +211,16 @@ def test_dense_forward_elementwise(dtype, d):
 
 _INPUTS = {}
 
+# Score tolerance at the workload shapes: a fifth of the 1e-6 band.  The
+# saliency sums run in fp64 from logits carried to ~2^-17 relative by the
+# hi/lo split (bf16) or fp32 products (f32), and a sharpness peak is
+# exp2(m - m_ref)/l with l an fp32 sum of a few hundred terms.  Measured
+# maxima over every head: 1.0e-8 (saliency) and 7.2e-9 (sharpness) on the
+# four bf16 workloads, 8.8e-8 and 3.7e-8 on the f32 tiny check.  The small
+# shapes with blocks of 1 or 2 tokens sum thousands of fp32 terms per row and
+# measured up to 4.5e-7, so they keep the band itself.
+WORKLOAD_SCORE_TOL = 2e-7
+
 
 def _workload_inputs(w):
     if w.name not in _INPUTS:
@@ -230,7 +242,7 @@ def _run_workload(w, gamma, record):
 
     def plan_job(xh):
         x, h = xh
-        return _plan_checks(Q[x, h], K[x, h], V[x, h], w.b, w.rho, gamma, hv, x, h)
+        return _plan_checks(Q[x, h], K[x, h], V[x, h], w.b, w.rho, gamma, hv, x, h, score_tol=WORKLOAD_SCORE_TOL)
 
     plans = dict(zip(heads, run_parallel(plan_job, heads)))
     _report("  plans checked on %d heads" % len(heads))
