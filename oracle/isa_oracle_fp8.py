@@ -106,21 +106,6 @@ def error_budget(q, Kt, Vt):
     return out
 
 
-def fp8_forward_head(Qh, Kh, Vh, b, kept_ctx, full_q):
-    """ISA output of one (batch, head) with the full route in FP8 and the
-    Taylor route as in isa_oracle; the full route's key list is the source
-    rows, then the tokens of the kept context blocks in kept order."""
-    Qh, Kh, Vh = (np.asarray(x, dtype=np.float64) for x in (Qh, Kh, Vh))
-    O = orc.oracle_forward_head(Qh, Kh, Vh, b, kept_ctx, np.zeros(0, dtype=np.int64))
-    Ns = Qh.shape[0]
-    src, ctx = orc.block_ranges(Ns, Kh.shape[0] - Ns, b)
-    tok = np.concatenate([np.arange(Ns)] + [np.arange(*ctx[int(c)]) for c in kept_ctx])
-    full_rows = [r for i in full_q for r in range(*src[int(i)])]
-    if full_rows:
-        O[full_rows] = fp8_full_attention_rows(Qh[full_rows], Kh[tok], Vh[tok])
-    return O
-
-
 def main():
     """Error budget of the FP8 full route on the benchmark's input
     distribution (seeded N(0,1) rows, 20 % of the queries sharpened)."""
