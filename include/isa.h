@@ -294,6 +294,26 @@ isa_status isa_run_fp8_stage(const isa_desc* desc, int stage, const void* Q, con
                              void* workspace, size_t workspace_bytes, void* fp8_workspace,
                              size_t fp8_workspace_bytes, void* stream);
 
+/* ---- Without allocation --------------------------------------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * isa_attention with its workspace in a fixed scratch array inside the
+ * library (isa_noalloc_scratch_bytes() = 128 MiB per device, held by each
+ * device the library runs on until the process ends) instead of caller
+ * memory.  Same arguments, output and errors as isa_attention without the
+ * workspace; ISA_ERR_WORKSPACE when isa_workspace_size(desc) exceeds the
+ * scratch.  The plan is not kept for the caller (isa_plan_views and
+ * isa_backward need isa_attention's workspace).  No allocation, no host
+ * synchronisation.  Every call on a device shares that device's scratch:
+ * calls that overlap on one device race, so the caller orders them (one
+ * stream, or stream order); each call writes every scratch word it reads. */
+isa_status isa_attention_noalloc(const isa_desc* desc, const void* Q, const void* K, const void* V, void* O,
+                                 void* stream);
+
+/* Bytes of the scratch array of isa_attention_noalloc. */
+size_t isa_noalloc_scratch_bytes(void);
+
 /* Device pointers to the plan held in a workspace (no device access). */
 isa_status isa_plan_views(const isa_desc* desc, void* workspace, size_t workspace_bytes,
                           isa_plan_view* out);

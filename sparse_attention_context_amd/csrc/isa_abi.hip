@@ -8,11 +8,17 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 
-isa_status device_status(hipError_t e) {
+}  // namespace
+
+isa_status isa::device_status(hipError_t e) {
   if (e == hipSuccess) return ISA_OK;
   snprintf(g_last_error, sizeof(g_last_error), "%s (%d)", hipGetErrorString(e), (int)e);
   return ISA_ERR_DEVICE;
 }
+
+namespace {
+
+using isa::device_status;
 
 isa_status check_io(const void* Q, const void* K, const void* V, const void* O, bool need_o) {
   const void* p[4] = {Q, K, V, O};
@@ -73,15 +79,9 @@ extern "C" isa_status isa_forward(const isa_desc* desc, const void* Q, const voi
   return ISA_OK;
 }
 
-extern "C" isa_status isa_attention(const isa_desc* desc, const void* Q, const void* K, const void* V,
-                                    void* O, void* workspace, size_t workspace_bytes, void* stream) {
-  isa::Layout L;
-  isa_status st = isa::make_layout(desc, &L);
-  if (st != ISA_OK) return st;
-  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
-  if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
-  const isa::Bufs B{Q, K, V, O, (char*)workspace};
-  hipStream_t s = (hipStream_t)stream;
+// The launches of isa_attention on validated arguments.
+isa_status isa::run_attention(const isa::Layout& L, const isa::Bufs& B, hipStream_t s) {
+  isa_status st;
   if ((st = select_context(L, B, s)) != ISA_OK) return st;
   // sharpness of every row; unless every block goes to full attention the
   // same pass also writes the Taylor output of every row
@@ -92,6 +92,16 @@ extern "C" isa_status isa_attention(const isa_desc* desc, const void* Q, const v
     ISA_RUN(isa::launch_full_merge(L, B, s));
   }
   return ISA_OK;
+}
+
+extern "C" isa_status isa_attention(const isa_desc* desc, const void* Q, const void* K, const void* V,
+                                    void* O, void* workspace, size_t workspace_bytes, void* stream) {
+  isa::Layout L;
+  isa_status st = isa::make_layout(desc, &L);
+  if (st != ISA_OK) return st;
+  if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
+  if ((st = check_ws(L, workspace, workspace_bytes)) != ISA_OK) return st;
+  return isa::run_attention(L, isa::Bufs{Q, K, V, O, (char*)workspace}, (hipStream_t)stream);
 }
 
 extern "C" isa_status isa_dense_forward(const isa_desc* desc, const void* Q, const void* K, const void* V,

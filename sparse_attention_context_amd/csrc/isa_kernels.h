@@ -17,6 +17,13 @@ struct Bufs {
   char* ws;
 };
 
+// ISA_OK, or ISA_ERR_DEVICE with the text of e kept for isa_last_error().
+isa_status device_status(hipError_t e);
+
+// The kernel sequence of isa_attention on validated arguments (B.ws: a
+// workspace of at least L.total bytes).
+isa_status run_attention(const Layout& L, const Bufs& B, hipStream_t s);
+
 // Block mean-pool of the source query blocks, every key block and the
 // source value blocks.
 hipError_t launch_pool(const Layout& L, const Bufs& B, hipStream_t s);

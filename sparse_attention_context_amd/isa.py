@@ -23,7 +23,8 @@ STATUS = {0: "ISA_OK", 1: "ISA_ERR_INVALID_ARGUMENT", 2: "ISA_ERR_UNSUPPORTED", 
 EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "isa_attention",
            "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_backward_workspace_size", "isa_backward",
            "isa_run_backward_stage", "isa_context_forward", "isa_fp8_workspace_size", "isa_attention_fp8",
-           "isa_run_fp8_stage", "isa_status_string", "isa_last_error"]
+           "isa_run_fp8_stage", "isa_attention_noalloc", "isa_status_string", "isa_last_error",
+           "isa_noalloc_scratch_bytes"]
 
 # isa_stage values (include/isa.h)
 STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
@@ -96,6 +97,10 @@ def lib():
         L.isa_backward.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp]
         L.isa_run_backward_stage.argtypes = [P(Desc), ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp, vp, vp,
                                              vp]
+        L.isa_attention_noalloc.argtypes = [P(Desc), vp, vp, vp, vp, vp]
+        L.isa_attention_noalloc.restype = ctypes.c_int
+        L.isa_noalloc_scratch_bytes.argtypes = []
+        L.isa_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.isa_status_string.argtypes = [ctypes.c_int]
         L.isa_status_string.restype = ctypes.c_char_p
         L.isa_last_error.argtypes = []
@@ -414,3 +419,20 @@ def run_fp8_stage(stage, Q, K, V, workspace, fp8_workspace, b, rho, gamma, out=N
     _check("isa_run_fp8_stage", lib().isa_run_fp8_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V),
                                                         _ptr(out), _ptr(ws), ws.numel(), _ptr(fws), fws.numel(),
                                                         _stream(stream)))
+
+
+def noalloc_scratch_bytes():
+    """Size of the scratch array isa_attention_noalloc works in."""
+    return lib().isa_noalloc_scratch_bytes()
+
+
+def attention_noalloc(Q, K, V, b, rho, gamma, out=None, stream=None):
+    """isa_attention_noalloc: the layer with the library's fixed scratch as its
+    workspace (no allocation by the library); returns O.  out=None allocates
+    O here, in Python; pass out= to allocate nothing at all."""
+    _inputs(Q, K, V)
+    O = _output("out", out, Q.shape, Q)
+    desc = desc_for(Q, K, b, rho, gamma, V=V, O=O)
+    _check("isa_attention_noalloc", lib().isa_attention_noalloc(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
+                                                                _ptr(O), _stream(stream)))
+    return O

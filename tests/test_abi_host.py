@@ -258,3 +258,19 @@ def test_context_rows_strides_are_checked_against_their_row_count():
         # (no device here)
         ok = isa.make_desc(B, H, Ns, Nc, d, 1, 1.0, 1.0, "bf16", q=(H * Nc * d, Nc * d, d), o=(H * Nc * d, Nc * d, d))
         assert L.isa_context_forward(ctypes.byref(ok), p, p, p, p, nul) == 4
+
+
+def test_noalloc_entry_point_refuses_layers_beyond_its_scratch():
+    """isa_attention_noalloc checks the layer's workspace against its fixed
+    scratch before any device call."""
+    L = isa.lib()
+    assert isa.noalloc_scratch_bytes() == 128 << 20
+    big = isa.make_desc(1, 24, 32760, 32760, 128, 64, 0.25, 0.3, "bf16")   # the long clip at gamma 0.3: 235 MiB
+    assert isa.workspace_size(big) > isa.noalloc_scratch_bytes()
+    host = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p((ctypes.addressof(host) + 255) // 256 * 256)   # never dereferenced
+    nul = ctypes.c_void_p(0)
+    assert L.isa_attention_noalloc(ctypes.byref(big), p, p, p, p, nul) == 3
+    assert L.isa_attention_noalloc(ctypes.byref(big), p, p, p, nul, nul) == 1
+    bad = isa.make_desc(1, 2, 300, 200, 64, 16, 2.0, 0.25, "bf16")
+    assert L.isa_attention_noalloc(ctypes.byref(bad), p, p, p, p, nul) == 1
