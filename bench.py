@@ -311,6 +311,9 @@ def time_other_workloads(args, stream, flush):
             step()
             cold = time_steps(step, args.other_steps, stream, flush)
             warm = time_steps(step, args.other_steps, stream, None)
+            layer = isa.CapturedAttention(Qd, Kd, Vd, w.b, w.rho, g, out=O, workspace=ws)
+            g_cold = time_steps(layer.replay, args.other_steps, stream, flush)
+            del layer
             views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, g)
             full_ms = None
             if views["counts"]["kq"] > 0:
@@ -323,6 +326,7 @@ def time_other_workloads(args, stream, flush):
             rec = {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Ns": w.Ns, "Nc": w.Nc, "b": w.b, "rho": w.rho,
                    "gamma": g, "dtype": w.dtype, "kc": views["counts"]["kc"], "kq": views["counts"]["kq"],
                    "ms": c, "warm_median_ms": round(float(np.median(warm)), 4),
+                   "graph_median_ms": round(float(np.median(g_cold)), 4),
                    "queries_per_s": round(w.B * w.Ns / (c["median_ms"] * 1e-3), 1),
                    "dense_ms": None if dense is None else round(dense, 4),
                    "dense_over_isa": None if dense is None else round(dense / c["median_ms"], 3)}
@@ -331,8 +335,8 @@ def time_other_workloads(args, stream, flush):
                 rec["full_route_ms"] = round(full_ms, 4)
                 rec["full_route_tflops"] = round(fl / (full_ms * 1e-3) / 1e12, 1)
             out.append(rec)
-            log("other workload %s gamma=%g: %.3f ms (p10 %.3f p90 %.3f, warm %.3f), dense %s"
-                % (w.name, g, c["median_ms"], c["p10_ms"], c["p90_ms"], rec["warm_median_ms"],
+            log("other workload %s gamma=%g: %.3f ms (p10 %.3f p90 %.3f, warm %.3f, graph %.3f), dense %s"
+                % (w.name, g, c["median_ms"], c["p10_ms"], c["p90_ms"], rec["warm_median_ms"], rec["graph_median_ms"],
                    "-" if dense is None else "%.3f ms" % dense))
             del ws
         del Qd, Kd, Vd, O
@@ -394,6 +398,12 @@ def main():
     ms = float(np.median(cold))
     log("isa_attention: %.3f ms/call (median of %d flushed steps; p10 %.3f, p90 %.3f; warm median %.3f)"
         % (ms, len(cold), np.percentile(cold, 10), np.percentile(cold, 90), np.median(warm)))
+    # the same call captured in a HIP graph: one host launch per step
+    layer = isa.CapturedAttention(Qd, Kd, Vd, w.b, w.rho, gamma, out=O, workspace=ws)
+    g_cold = time_steps(layer.replay, args.steps, stream, flush)
+    g_warm = time_steps(layer.replay, args.steps, stream, None)
+    log("isa_attention as a graph: %.3f ms/replay (median, flushed; p10 %.3f, p90 %.3f; warm median %.3f)"
+        % (np.median(g_cold), np.percentile(g_cold, 10), np.percentile(g_cold, 90), np.median(g_warm)))
     views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, gamma)
     counts = views["counts"]
 
@@ -503,6 +513,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "timing": dict(summary(cold), warm_median_ms=round(float(np.median(warm)), 4), host_enqueue_us=round(host_us, 1),
+                       graph=dict(summary(g_cold), warm_median_ms=round(float(np.median(g_warm)), 4)),
                        protocol="HIP events around each step on the launch stream; a 1 GiB write before each "
                                 "step (outside the events) flushes L2 and the Infinity Cache; value and "
                                 "ms_per_step use the median"),

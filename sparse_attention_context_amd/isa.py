@@ -436,3 +436,34 @@ def attention_noalloc(Q, K, V, b, rho, gamma, out=None, stream=None):
     _check("isa_attention_noalloc", lib().isa_attention_noalloc(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V),
                                                                 _ptr(O), _stream(stream)))
     return O
+
+
+class CapturedAttention:
+    """One isa_attention call captured in a HIP graph (torch.cuda.CUDAGraph)
+    on fixed tensors; replay() runs the captured kernel sequence again on the
+    current contents of Q, K, V, writing out and workspace.  The library's
+    calls only enqueue kernels (no allocation, synchronisation or memset), so
+    the whole layer captures as one graph; a replay costs one launch from the
+    host instead of one per kernel."""
+
+    def __init__(self, Q, K, V, b, rho, gamma, out=None, workspace=None):
+        _inputs(Q, K, V)
+        self.out = _output("out", out, Q.shape, Q)
+        desc = desc_for(Q, K, b, rho, gamma, V=V, O=self.out)
+        self.workspace = _ws_for(desc, Q, workspace)
+        args = (Q, K, V, b, rho, gamma)
+        # one eager call on a side stream first (the graph then captures
+        # launches of modules that are already loaded)
+        cur = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            attention(*args, out=self.out, workspace=self.workspace)
+        cur.wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            attention(*args, out=self.out, workspace=self.workspace)
+
+    def replay(self):
+        self.graph.replay()
+        return self.out
