@@ -17,7 +17,6 @@ MFMA), the other workload shapes, and the CPU oracle timed on the host cores.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -80,20 +79,20 @@ def full_route_flops(views, w, kq_gamma):
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COUNTERS = os.path.join(ROOT, "profiles", "isa_video_dit_counters.txt")
-FLASH_SRC = os.path.join(ROOT, "sparse_attention_context_amd", "csrc", "isa_flash.hip")
 
 
 def counted_traffic(kernel_label):
     """HBM bytes per launch of `kernel_label` from the committed rocprofv3
     counter summary (FETCH_SIZE and WRITE_SIZE scaled by what they read for a
-    1 GiB copy), or None when the summary is missing or was taken on a
-    different version of the flash kernel source."""
+    1 GiB copy), or None when the summary is missing or was taken on another
+    version of the kernel sources."""
+    from sparse_attention_context_amd.profile_summary import sources_digest
     try:
         text = open(COUNTERS).read().splitlines()
-        src_hash = hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()
     except OSError:
         return None
-    if not any(src_hash in ln for ln in text if "sha256" in ln):
+    digest = sources_digest()
+    if not any(digest in ln for ln in text if "sha256" in ln):
         return None
     for ln in text:
         if ln.startswith(kernel_label):
@@ -315,13 +314,12 @@ def time_other_workloads(args, stream, flush):
             g_cold = time_steps(layer.replay, args.other_steps, stream, flush)
             del layer
             views = isa.plan_views(Qd, Kd, ws, w.b, w.rho, g)
-            full_ms = None
-            if views["counts"]["kq"] > 0:
-                names = list(isa.ATTENTION_STAGES)
-                if views["counts"]["kq"] == views["counts"]["nb_s"]:
-                    names[names.index("sharp_taylor")] = "sharp"
-                full_ms = time_stage_pass(lambda name: isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, g, out=O),
-                                          names, 3, stream)["full"]
+            names = list(isa.ATTENTION_STAGES)
+            if views["counts"]["kq"] == views["counts"]["nb_s"]:
+                names[names.index("sharp_taylor")] = "sharp"
+            stages = time_stage_pass(lambda name: isa.run_stage(name, Qd, Kd, Vd, ws, w.b, w.rho, g, out=O),
+                                     names, 5, stream)
+            full_ms = stages["full"] if views["counts"]["kq"] > 0 else None
             c = summary(cold)
             rec = {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Ns": w.Ns, "Nc": w.Nc, "b": w.b, "rho": w.rho,
                    "gamma": g, "dtype": w.dtype, "kc": views["counts"]["kc"], "kq": views["counts"]["kq"],
@@ -329,7 +327,8 @@ def time_other_workloads(args, stream, flush):
                    "graph_median_ms": round(float(np.median(g_cold)), 4),
                    "queries_per_s": round(w.B * w.Ns / (c["median_ms"] * 1e-3), 1),
                    "dense_ms": None if dense is None else round(dense, 4),
-                   "dense_over_isa": None if dense is None else round(dense / c["median_ms"], 3)}
+                   "dense_over_isa": None if dense is None else round(dense / c["median_ms"], 3),
+                   "stage_ms": {k: round(v, 4) for k, v in stages.items()}}
             if full_ms:
                 fl = full_route_flops(views, w, g)
                 rec["full_route_ms"] = round(full_ms, 4)
@@ -457,14 +456,22 @@ def main():
         pool_bytes = w.B * w.H * ((w.Ns + (w.Ns + w.Nc) + w.Ns) * w.d * es + (nb_s + 2 * M) * w.d * 4)
         gbs = pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9
         others.append({"kernel": "isa_pool_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": pool_bytes})
+                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": pool_bytes,
+                       "avg_launch_ms": round(stage_ms["pool"], 4),
+                       "traffic": counted_traffic("isa_pool_kernel") if w.name == "video_dit_layer" else None})
     if stage_ms.get("sharp_taylor"):
         mk = nb_s + counts["kc"]
-        tf = 4 * w.d * w.Ns * mk * w.B * w.H / (stage_ms["sharp_taylor"] * 1e-3) / 1e12
+        pooled_flops = 6 * w.d * w.Ns * mk * w.B * w.H
+        tf = pooled_flops / (stage_ms["sharp_taylor"] * 1e-3) / 1e12
+        # its HBM floor: Q read, O and the per-row peak written once, the packed kept set read once per head
+        pooled_bytes = w.B * w.H * (2 * w.Ns * w.d * es + 4 * w.Ns + mk * (3 * w.d * 2 + 4))
         others.append({"kernel": "isa_flash_pp_pooled_kernel (sharpness + Taylor)", "bound": "mfma",
                        "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                       "note": "4 d FLOP per (query, kept block); the lo half of the split keys is not counted"})
+                       "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_launch": pooled_flops,
+                       "avg_launch_ms": round(stage_ms["sharp_taylor"], 4), "hbm_bytes_floor": pooled_bytes,
+                       "traffic": counted_traffic("isa_flash_pp_pooled_kernel") if w.name == "video_dit_layer" else None,
+                       "note": "6 d FLOP per (query, kept block): the hi and the lo key products (2 d each) and P.V "
+                               "(2 d); bf16 MFMA"})
 
     context = None
     if not args.no_context and w.dtype == "bf16" and w.Nc > 0:
