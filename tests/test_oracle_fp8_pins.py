@@ -72,3 +72,52 @@ def test_fp8_error_budget_on_the_benchmark_distribution():
     q[::5] += 4 * rng.standard_normal((13, 128))
     e2 = f8.error_budget(q, rng.standard_normal((1536, 128)), rng.standard_normal((1536, 128)))
     assert e2["q,k"] > 0.05, e2
+
+
+def test_fp8_rows_without_rounding_are_exact_attention():
+    """With no operand rounded the FP8 route is softmax attention itself: the
+    exp2-domain logits, the whole-number reference maximum and the unrounded
+    row sum cancel exactly (up to fp64 rounding)."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((37, 64)) * 2.0
+    Kt = rng.standard_normal((101, 64))
+    Vt = rng.standard_normal((101, 64))
+    got = f8.fp8_full_attention_rows(q, Kt, Vt, parts=())
+    np.testing.assert_allclose(got, orc.full_attention_rows(q, Kt, Vt), rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_rows_are_exact_on_representable_operands():
+    """Q, K and V built from e4m3 values whose every scale block holds an
+    entry of magnitude 256..448 (times the block's power of two) have exact
+    block scales, so rounding them changes nothing and the route equals exact
+    attention.  V's blocks run along the keys (32 consecutive keys of one
+    column, the short last block padded): its columns 0 and 32 are large and
+    the others 2^-20 smaller, so blocks taken along a key row instead would
+    carry the large scale and flush the small columns to zero."""
+    rng = np.random.default_rng(5)
+    table = _e4m3_table()
+    mid = table[(np.abs(table) >= 1.0) & (np.abs(table) <= 448.0)]
+    big = table[(np.abs(table) >= 256.0) & (np.abs(table) <= 448.0)]
+
+    def qk_rows(n, d):                       # one big entry per (row, 32 columns)
+        X = rng.choice(mid, size=(n, d))
+        for j in range(0, d, 32):
+            X[:, j] = rng.choice(big, size=n)
+        return X / 64.0                      # a power of two keeps every block exact
+
+    q = qk_rows(20, 64)
+    Kt = qk_rows(70, 64)
+    Vt = rng.choice(mid, size=(70, 64)) * 2.0 ** -20
+    for i in range(0, 70, 32):               # one big entry per (column, 32 keys)
+        Vt[i, :] = rng.choice(big, size=64) * 2.0 ** -20
+    Vt[:, 0] = rng.choice(big, size=70)
+    Vt[:, 32] = rng.choice(big, size=70)
+    assert np.array_equal(f8.quantize_rows(q), q) and np.array_equal(f8.quantize_rows(Kt), Kt)
+    got = f8.fp8_full_attention_rows(q, Kt, Vt, parts=("q", "k", "v"))
+    ref = orc.full_attention_rows(q, Kt, Vt)
+    # (per column: the columns differ in scale by 2^20, and a cancelling sum
+    # carries the fp64 rounding of its column's magnitude)
+    assert np.all(np.abs(got - ref) <= 1e-12 * np.abs(Vt).max(axis=0)[None, :])
+    # the same values with scale blocks along the key rows lose the small columns
+    wrong = f8.quantize_rows(Vt)
+    assert np.abs(wrong[:, 1:32]).max() == 0.0
