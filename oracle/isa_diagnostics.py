@@ -1,8 +1,8 @@
 """Routing diagnostic for ISA on the CPU oracle (test infrastructure only).
 
 "Lightning Unified Video Editing via In-Context Sparse Attention" (English
-abstract) states that query sharpness correlates with the error of the
-approximation, which is why sharp query blocks go to full attention.  This
+abstract) ties how sharp a query is to how badly the approximate route
+serves it, which is why sharp query blocks go to full attention.  This
 module measures that on synthetic inputs with the fp64 oracle alone:
   * the error of the 0-th order Taylor route per query block against the full
     route over the same kept key set (the block's error norm over the layer's

@@ -134,8 +134,8 @@ def top_indices(scores, k):
 
 
 def sharpness_scores(Qs, src_ranges, kbar_K, n_K):
-    """Query sharpness per source block (abstract: query sharpness correlates
-    with the approximation error; reading R6).
+    """Query sharpness per source block (the abstract links a query's
+    sharpness to the error of the approximate route; reading R6).
 
     Qs: [Ns, d] source queries.  kbar_K, n_K: the kept key blocks.
     sh_i = mean over q in block i of max_j P_j(q), P the n-weighted pooled

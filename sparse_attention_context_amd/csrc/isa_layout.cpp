@@ -1,9 +1,9 @@
 // Argument checks, counts and workspace layout (no HIP calls).
 //
-// Counts follow the reading of "prune redundant context" and "routes
-// high-error queries to full attention" (Lightning Unified Video Editing via
-// In-Context Sparse Attention, English abstract): a fraction f of n items
-// keeps ceil(f*n - 1e-9) of them, clipped to [0, n], evaluated in double.
+// Counts of the two selections (the context pruning and the query routing of
+// Lightning Unified Video Editing via In-Context Sparse Attention, English
+// abstract): keeping a fraction f of n items keeps ceil(f*n - 1e-9) of them,
+// clipped to [0, n], evaluated in double.
 #include "isa_layout.h"
 
 #include <math.h>

@@ -1,8 +1,9 @@
 // Context saliency (pre-selection score) on MFMA.
 //
-// The abstract of "Lightning Unified Video Editing via In-Context Sparse
-// Attention" observes that context tokens carry much lower saliency than
-// source tokens and prunes redundant context before attention.  Saliency of
+// Per the abstract of "Lightning Unified Video Editing via In-Context Sparse
+// Attention", the context tokens matter far less to the source queries than
+// the source tokens do, so the least salient context blocks are dropped
+// before attention.  Saliency of
 // context block c is read here as the probability mass that the pooled
 // source queries put on it under the n-weighted softmax over every pooled
 // key block:

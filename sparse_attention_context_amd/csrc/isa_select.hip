@@ -1,9 +1,9 @@
 // Top-k selection, compaction and packing of the kept key set.
 //
-// Both selections of ISA -- the context pre-selection that prunes redundant
-// context and the dynamic query grouping that sends high-error (sharp) query
-// blocks to full attention (Lightning Unified Video Editing via In-Context
-// Sparse Attention, English abstract) -- keep the k highest scores.  The
+// ISA selects twice (Lightning Unified Video Editing via In-Context Sparse
+// Attention, English abstract): which context blocks survive the pruning, and
+// which query blocks, the sharpest, take the exact route.  Both keep the k
+// highest scores.  The
 // order is total: score descending, then index ascending, so ties go to the
 // lower index.  Lists are emitted in ascending index order.
 //
