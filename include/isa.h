@@ -318,6 +318,30 @@ size_t isa_noalloc_scratch_bytes(void);
 isa_status isa_plan_views(const isa_desc* desc, void* workspace, size_t workspace_bytes,
                           isa_plan_view* out);
 
+/* One stage of a traced call: its name ("pool", "saliency", "select_ctx",
+ * "pool_kept_v", "sharp_taylor" or "sharp", "select_q", "full",
+ * "full_merge"; static strings owned by the library) and the milliseconds
+ * between the events recorded on the stream before it and before the next
+ * stage (after the last). */
+typedef struct isa_trace_entry {
+  const char* stage;
+  float ms;
+} isa_trace_entry;
+
+/* Per-stage timestamps of the last isa_attention call made while the
+ * environment variable ISA_TRACE was set (to a value other than "" or "0";
+ * read at every call; isa_attention_noalloc never traces, since the first
+ * traced call creates HIP events).  Such a call
+ * records a HIP event on its stream before each kernel and one after the
+ * last, into a set of events that every traced call reuses: only the last
+ * call is kept, calls from several threads at once interleave, and a call on
+ * a stream under graph capture records nothing.  Waits for the last event,
+ * then writes up to max_entries stages to out and their number to
+ * *n_entries.  ISA_ERR_INVALID_ARGUMENT when n_entries is NULL, out is NULL
+ * with max_entries > 0, or no traced call has completed its recording;
+ * ISA_ERR_DEVICE when an event query fails. */
+isa_status isa_trace_read(isa_trace_entry* out, int max_entries, int* n_entries);
+
 /* Static text for a status code. */
 const char* isa_status_string(isa_status status);
 

@@ -17,7 +17,7 @@ BUILD = os.path.join(os.path.dirname(HERE), "_build")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 HIP_SOURCES = ["isa_pool.hip", "isa_score.hip", "isa_select.hip", "isa_attn.hip", "isa_flash.hip", "isa_flash_bwd.hip",
-               "isa_flash_fp8.hip", "isa_abi.hip", "isa_noalloc.hip"]
+               "isa_flash_fp8.hip", "isa_abi.hip", "isa_noalloc.hip", "isa_trace.hip"]
 CXX_SOURCES = ["isa_layout.cpp"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE,

@@ -37,10 +37,14 @@ isa_status check_ws(const isa::Layout& L, const void* ws, size_t bytes) {
 
 // Pooling, saliency, context pre-selection and packing of the kept set
 // (with the pooling of the kept context blocks' V).
-isa_status select_context(const isa::Layout& L, const isa::Bufs& B, hipStream_t s) {
+isa_status select_context(const isa::Layout& L, const isa::Bufs& B, hipStream_t s, isa::Tracer* tr = nullptr) {
+  if (tr) tr->mark("pool");
   ISA_RUN(isa::launch_pool(L, B, s));
+  if (tr) tr->mark("saliency");
   ISA_RUN(isa::launch_saliency(L, B, s));
+  if (tr) tr->mark("select_ctx");
   ISA_RUN(isa::launch_select_ctx(L, B, s));
+  if (tr) tr->mark("pool_kept_v");
   ISA_RUN(isa::launch_pool_pack(L, B, s));
   return ISA_OK;
 }
@@ -80,15 +84,20 @@ extern "C" isa_status isa_forward(const isa_desc* desc, const void* Q, const voi
 }
 
 // The launches of isa_attention on validated arguments.
-isa_status isa::run_attention(const isa::Layout& L, const isa::Bufs& B, hipStream_t s) {
+isa_status isa::run_attention(const isa::Layout& L, const isa::Bufs& B, hipStream_t s, bool trace) {
+  isa::Tracer tr(trace ? s : nullptr, trace);
   isa_status st;
-  if ((st = select_context(L, B, s)) != ISA_OK) return st;
+  if ((st = select_context(L, B, s, &tr)) != ISA_OK) return st;
   // sharpness of every row; unless every block goes to full attention the
   // same pass also writes the Taylor output of every row
+  tr.mark(L.kq == L.nb_s ? "sharp" : "sharp_taylor");
   ISA_RUN(isa::launch_pooled_attention(L, B, L.kq == L.nb_s ? 1 : 0, s));
+  tr.mark("select_q");
   ISA_RUN(isa::launch_select_q(L, B, s));
   if (L.kq > 0) {
+    tr.mark("full");
     ISA_RUN(isa::launch_full_attention(L, B, false, s));
+    tr.mark("full_merge");
     ISA_RUN(isa::launch_full_merge(L, B, s));
   }
   return ISA_OK;

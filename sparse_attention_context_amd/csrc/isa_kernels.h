@@ -21,8 +21,24 @@ struct Bufs {
 isa_status device_status(hipError_t e);
 
 // The kernel sequence of isa_attention on validated arguments (B.ws: a
-// workspace of at least L.total bytes).
-isa_status run_attention(const Layout& L, const Bufs& B, hipStream_t s);
+// workspace of at least L.total bytes); trace: record the stage timestamps
+// when ISA_TRACE is set.
+isa_status run_attention(const Layout& L, const Bufs& B, hipStream_t s, bool trace = true);
+
+// Stage timestamps of a layer call when the ISA_TRACE environment variable
+// is set (isa_trace.hip): mark(stage) records an event on the stream before
+// the stage's launch, the destructor one after the last; isa_trace_read
+// reports them.  Does nothing without ISA_TRACE or under stream capture.
+class Tracer {
+ public:
+  Tracer(hipStream_t s, bool allowed = true);
+  ~Tracer();
+  void mark(const char* stage);
+
+ private:
+  hipStream_t s_;
+  bool on_ = false;
+};
 
 // Block mean-pool of the source query blocks, every key block and the
 // source value blocks.

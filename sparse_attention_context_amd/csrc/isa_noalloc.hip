@@ -63,5 +63,5 @@ extern "C" isa_status isa_attention_noalloc(const isa_desc* desc, const void* Q,
   if (L.total > kScratchBytes) return ISA_ERR_WORKSPACE;   // the layer needs more than the fixed scratch
   void* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != ISA_OK) return st;
-  return isa::run_attention(L, isa::Bufs{Q, K, V, O, (char*)ws}, (hipStream_t)stream);
+  return isa::run_attention(L, isa::Bufs{Q, K, V, O, (char*)ws}, (hipStream_t)stream, false);
 }

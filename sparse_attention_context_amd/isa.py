@@ -24,7 +24,7 @@ EXPORTS = ["isa_get_counts", "isa_workspace_size", "isa_plan", "isa_forward", "i
            "isa_dense_forward", "isa_run_stage", "isa_plan_views", "isa_backward_workspace_size", "isa_backward",
            "isa_run_backward_stage", "isa_context_forward", "isa_fp8_workspace_size", "isa_attention_fp8",
            "isa_run_fp8_stage", "isa_attention_noalloc", "isa_status_string", "isa_last_error",
-           "isa_noalloc_scratch_bytes"]
+           "isa_noalloc_scratch_bytes", "isa_trace_read"]
 
 # isa_stage values (include/isa.h)
 STAGES = ["pool", "saliency", "select_ctx", "pool_kept_v", "pack", "sharp_taylor", "sharp", "select_q",
@@ -63,6 +63,10 @@ class PlanView(ctypes.Structure):
                 ("full_q", ctypes.c_void_p), ("taylor_q", ctypes.c_void_p), ("counts", Counts)]
 
 
+class TraceEntry(ctypes.Structure):
+    _fields_ = [("stage", ctypes.c_char_p), ("ms", ctypes.c_float)]
+
+
 class IsaError(RuntimeError):
     def __init__(self, fn, code, detail=""):
         self.code = code
@@ -99,6 +103,8 @@ def lib():
                                              vp]
         L.isa_attention_noalloc.argtypes = [P(Desc), vp, vp, vp, vp, vp]
         L.isa_attention_noalloc.restype = ctypes.c_int
+        L.isa_trace_read.argtypes = [ctypes.POINTER(TraceEntry), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.isa_trace_read.restype = ctypes.c_int
         L.isa_noalloc_scratch_bytes.argtypes = []
         L.isa_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.isa_status_string.argtypes = [ctypes.c_int]
@@ -419,6 +425,16 @@ def run_fp8_stage(stage, Q, K, V, workspace, fp8_workspace, b, rho, gamma, out=N
     _check("isa_run_fp8_stage", lib().isa_run_fp8_stage(ctypes.byref(desc), code, _ptr(Q), _ptr(K), _ptr(V),
                                                         _ptr(out), _ptr(ws), ws.numel(), _ptr(fws), fws.numel(),
                                                         _stream(stream)))
+
+
+def trace_read(max_entries=16):
+    """isa_trace_read: [(stage, ms), ...] of the last isa_attention call made
+    while the ISA_TRACE environment variable was set (the library reads it at
+    every call)."""
+    out = (TraceEntry * max_entries)()
+    n = ctypes.c_int(0)
+    _check("isa_trace_read", lib().isa_trace_read(out, max_entries, ctypes.byref(n)))
+    return [(out[i].stage.decode(), float(out[i].ms)) for i in range(n.value)]
 
 
 def noalloc_scratch_bytes():

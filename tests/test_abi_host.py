@@ -274,3 +274,16 @@ def test_noalloc_entry_point_refuses_layers_beyond_its_scratch():
     assert L.isa_attention_noalloc(ctypes.byref(big), p, p, p, nul, nul) == 1
     bad = isa.make_desc(1, 2, 300, 200, 64, 16, 2.0, 0.25, "bf16")
     assert L.isa_attention_noalloc(ctypes.byref(bad), p, p, p, p, nul) == 1
+
+
+def test_trace_read_without_a_traced_call_is_an_error():
+    """isa_trace_read checks its arguments and refuses when no traced call
+    has been recorded (this process makes no GPU call)."""
+    import ctypes
+    L = isa.lib()
+    n = ctypes.c_int(7)
+    assert L.isa_trace_read(None, 0, None) == 1
+    assert L.isa_trace_read(None, 4, ctypes.byref(n)) == 1
+    assert L.isa_trace_read(None, -1, ctypes.byref(n)) == 1
+    out = (isa.TraceEntry * 4)()
+    assert L.isa_trace_read(out, 4, ctypes.byref(n)) == 1 and n.value == 0
