@@ -29,10 +29,45 @@ def _host_views(views):
     return {k: (v.cpu().numpy() if hasattr(v, "cpu") else v) for k, v in views.items()}
 
 
-def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol=BAND):
+def _sharpness_bound(Qh, kbar_gpu, kbar_ref, n, src):
+    """Bound on the part of |sh_gpu - sh_ref| that the pooled pass's key
+    representation causes.
+
+    The kernels carry a pooled key as bf16 hi + bf16 lo of its fp32 mean, so
+    every logit q . kbar_j / sqrt(d) is off by e_ij = q_i . r_j / sqrt(d),
+    r_j = kbar_j - hi_j - lo_j (about 2^-18 of kbar_j per element), which is
+    computed here exactly from the GPU's own fp32 means.  Logits moved by at
+    most E_i = max_j |e_ij| change a row's peak probability p_i by at most a
+    factor exp(+-2 E_i); a block's sharpness is the mean over its rows.  The
+    2e-7 added is an allowance, not a bound, for the fp32 exponentials and
+    the fp32 sum of the row's softmax terms; with a few thousand blocks that
+    sum has measured up to 4.5e-7, which the 1e-6 band that the caller keeps
+    as the floor covers.  The representation term is small for the benchmark
+    shapes (p_i ~ 1e-2) and reaches 1e-5 for sharp queries over blocks of a
+    few tokens, where p_i comes close to 1."""
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+    k32 = np.asarray(kbar_gpu, dtype=np.float32)
+    hi = bf16(k32)
+    lo = bf16(k32 - hi)
+    r = np.asarray(kbar_ref, np.float64) - hi.astype(np.float64) - lo.astype(np.float64)
+    q = np.asarray(Qh, np.float64)
+    d = q.shape[1]
+    E = np.abs(q @ r.T).max(axis=1) / np.sqrt(d)
+    z = q @ np.asarray(kbar_ref, np.float64).T / np.sqrt(d) + np.log(n)[None, :]
+    z -= z.max(axis=1, keepdims=True)
+    p = 1.0 / np.exp(z).sum(axis=1)          # each row's peak probability
+    row = p * np.expm1(2.0 * E)
+    return max(float(row[a:e].mean()) for a, e in src) + 2e-7
+
+
+def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol=BAND, sh_bound=False):
     """Checks pooled means, scores and index sets of one (batch, head) of a
     GPU run (host views hv) against the oracle.  Scores must lie within
     score_tol of the oracle's (at most the 1e-6 band of the set check).
+    sh_bound: the sharpness tolerance, and the band of the query-set check,
+    may widen to the bound of _sharpness_bound for inputs whose pooled-key
+    rounding moves the scores by more than the band.
     Returns the head's figures and its GPU lists (kept, full)."""
     Ns = Qh.shape[0]
     Nc = Kh.shape[0] - Ns
@@ -67,8 +102,13 @@ def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol
     sh = hv["sh"][x, h]
     # scores must sit closer to the oracle than the band the set check excludes
     stats["sh_err"] = float(np.max(np.abs(sh - sh_ref)))
-    assert stats["sh_err"] < score_tol, stats["sh_err"]
-    stats["amb_q"] = check_set(full, sh_ref, kq)
+    sh_tol, q_band = score_tol, BAND
+    if sh_bound:
+        bound = _sharpness_bound(Qh, hv["kbar"][x, h][keyset], ref["kbar"][keyset], ref["n"][keyset], src)
+        stats["sh_bound"] = bound
+        sh_tol, q_band = max(score_tol, bound), max(BAND, bound)
+    assert stats["sh_err"] < sh_tol, (stats["sh_err"], sh_tol)
+    stats["amb_q"] = check_set(full, sh_ref, kq, band=q_band)
     assert sorted(set(full.tolist()) | set(tayl.tolist())) == list(range(nb_s))
     assert tayl.tolist() == sorted(tayl.tolist())
     return stats, kept, full
