@@ -87,6 +87,7 @@ struct FlashArgs {
   const void* pv;
   const float* pbias;   // pooled: [BH][mk_pad] log2 n_j, -inf for padding
   int mk_pad;
+  int mk, tail_s;       // pooled: kept blocks per head (source + kept context); rows of the last source block
   const int* q_list;    // route block list: [BH][q_k] (table rows)
   int q_k, nb_s;        // blocks in the list per head; source blocks
   long long n_rows;     // virtual query rows per head
@@ -100,6 +101,24 @@ struct FlashArgs {
   int n_wg;
   float scale_log2;     // log2(e)/sqrt(d)
 };
+
+// Pooled mode: key tile kt of the packed kept set (keys 64 kt .. 64 kt + 63)
+// is uniform when every one of its blocks holds b rows, so that its bias is
+// log2 b in every column -- no padding, not the short last source block,
+// not a short last context block that is kept (ctx_tail: the head keeps
+// it).  Such a tile's logits S*sc + log2 b need no per-element bias: the
+// maximum is taken over S and each exponent is one fma, S*sc + (log2 b -
+// m_ref).  Both pooled kernels apply the same rule, so they stay bit-identical.
+__device__ __forceinline__ bool pooled_uniform_tile(const FlashArgs& a, int kt, bool ctx_tail) {
+  const int k0 = kt * 64, k1 = k0 + 64;
+  if (k1 > a.mk) return false;
+  if (a.tail_s != a.b && a.nb_s - 1 >= k0 && a.nb_s - 1 < k1) return false;
+  if (ctx_tail && a.mk - 1 >= k0 && a.mk - 1 < k1) return false;
+  return true;
+}
+__device__ __forceinline__ bool pooled_ctx_tail(const FlashArgs& a, long long bh) {
+  return a.kc > 0 && a.tail_c != a.b && a.kept[bh * a.kc + a.kc - 1] == a.nb_c - 1;
+}
 
 template <int D, int KM, int RM, int NW, bool WO, bool WP>
 __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
@@ -147,12 +166,14 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 
   // ---- key range of this workgroup
   int n_keys, n_valid;
+  bool ctx_tail = false;   // pooled: the head keeps a short last context block
   if constexpr (GATHER) {
     n_keys = a.Ns + (int)a.ctx_tok;
     const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
     n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
   } else if constexpr (POOLED) {
     n_keys = n_valid = a.mk_pad;  // padding rows carry bias -inf
+    ctx_tail = pooled_ctx_tail(a, bh);
   } else {
     n_keys = n_valid = a.Nk;
   }
@@ -269,16 +290,20 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
   f32x16 acc[WO ? NT : 1];
 #pragma unroll
   for (int t = 0; t < (WO ? NT : 1); ++t) acc[t] = f32x16{};
-  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+  // pk: the row's largest term of the running sum l_run, rescaled with it,
+  // so that the peak probability pk / l rounds like the sum it divides
+  float m_ref = -INFINITY, pk = 0.f, l_run = 0.f;
   const float sc = a.scale_log2;
   // exp2-domain headroom before the reference max moves; token modes keep
   // logits raw (x = S), pooled mode works on x = S*sc + log2 n_j directly
   const float thresh = POOLED ? 8.0f : 8.0f / sc;
 
+  const float lb = POOLED ? log2f((float)a.b) : 0.f;   // the bias of a block of b rows
   auto softmax_pv = [&](int j, STile St) {
     f32x16* S = St.t;
     const int t0 = (t_begin + j) * BN;
-    if constexpr (POOLED) {
+    const bool uni = POOLED && pooled_uniform_tile(a, t_begin + j, ctx_tail);
+    if (POOLED && !uni) {
       const float* bs = sbias[j % NSTAGE];
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti)
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[ti][4 * g + e] = fmaf(S[ti][4 * g + e], sc, bb[e]);
         }
-    } else if (t0 + BN > n_valid) {
+    } else if (!POOLED && t0 + BN > n_valid) {
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -301,7 +326,8 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if constexpr (WP) m_true = fmaxf(m_true, mx);
+    const float smax = mx;              // uniform tiles: the largest S
+    if (uni) mx = fmaf(mx, sc, lb);     // the largest S*sc + log2 b (the fma is monotone in S)
     // each row moves its own reference (rows of a wave never influence one
     // another, so a row's result does not depend on how rows are grouped);
     // the branch is taken when any row of the wave needs it
@@ -310,6 +336,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
       const float m_new = move ? mx : m_ref;
       const float alpha = __builtin_amdgcn_exp2f(POOLED ? (m_ref - m_new) : (m_ref - m_new) * sc);
       l_run *= alpha;
+      if constexpr (WP) pk *= alpha;
       if constexpr (WO) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] *= alpha;
@@ -317,8 +344,22 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
       m_ref = m_new;
     }
     const float msub = POOLED ? m_ref : m_ref * sc;
+    const float lm = lb - m_ref;   // uniform pooled tiles: exponent S*sc + (log2 b - m_ref)
+    // the tile's largest term, with the expression of its terms below
+    if constexpr (WP) pk = fmaxf(pk, __builtin_amdgcn_exp2f(uni ? fmaf(smax, sc, lm) : mx - msub));
     Op pB[4];
     float psum = 0.f;  // tile-local sum first: fewer roundings at the running sum's scale
+    if (uni) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, lm));
+          psum += p;
+          pB[s][jj] = (__bf16)p;
+        }
+      }
+    } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -328,6 +369,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
         psum += p;
         pB[s][jj] = (__bf16)p;
       }
+    }
     }
     l_run += psum;
     if constexpr (WO) {
@@ -398,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
           }
       }
       if constexpr (WP) {
-        if (h == 0) a.peak[(long long)bh * a.Ns + qrow] = __builtin_amdgcn_exp2f(m_true - m_ref) * inv;
+        if (h == 0) a.peak[(long long)bh * a.Ns + qrow] = pk * inv;
       }
       if constexpr (WO) {
         // p = exp2(x - lse) with x = S*sc (tokens) or S*sc + log2 n_j (pooled)
@@ -1323,7 +1365,8 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   f32x16 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
-  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+  // pk: the row's largest term of l_run, rescaled with it (as in isa_flash_kernel)
+  float m_ref = -INFINITY, pk = 0.f, l_run = 0.f;
   const float sc = a.scale_log2;
   Op qB[D / 16], qN[D / 16];
 
@@ -1359,17 +1402,22 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     pp_issue_order<ISA_PP_LOOKAHEAD, 16, 32>();
     return S;
   };
-  auto softmax = [&](int stage, STile St) -> PTile {
+  // uni: the key tile is uniform (pooled_uniform_tile), its bias log2 b in
+  // every column
+  const float lb = log2f((float)a.b);
+  auto softmax = [&](int stage, STile St, bool uni) -> PTile {
     f32x16* S = St.t;
-    const float* bs = sbias[stage];
+    if (!uni) {
+      const float* bs = sbias[stage];
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+      for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 bb = *(const f32x4*)(bs + 32 * ti + 8 * g + 4 * h);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 bb = *(const f32x4*)(bs + 32 * ti + 8 * g + 4 * h);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[ti][4 * g + e] = fmaf(S[ti][4 * g + e], sc, bb[e]);
-      }
+          for (int e = 0; e < 4; ++e) S[ti][4 * g + e] = fmaf(S[ti][4 * g + e], sc, bb[e]);
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
@@ -1377,25 +1425,42 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    m_true = fmaxf(m_true, mx);
+    const float smax = mx;            // uniform tiles: the largest S
+    if (uni) mx = fmaf(mx, sc, lb);   // the largest S*sc + log2 b (the fma is monotone in S)
     const bool move = mx > m_ref + 8.0f;
     if (__ballot(move)) {
       const float m_new = move ? mx : m_ref;
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       l_run *= alpha;
+      pk *= alpha;
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] *= alpha;
       m_ref = m_new;
     }
     PTile P;
     float psum = 0.f;
+    const float lm = lb - m_ref;
+    // the tile's largest term, with the expression of its terms below
+    pk = fmaxf(pk, __builtin_amdgcn_exp2f(uni ? fmaf(smax, sc, lm) : mx - m_ref));
+    if (uni) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float p = __builtin_amdgcn_exp2f(S[s >> 1][8 * (s & 1) + jj] - m_ref);
-        psum += p;
-        P.p[s][jj] = (__bf16)p;
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, lm));
+          psum += p;
+          P.p[s][jj] = (__bf16)p;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = __builtin_amdgcn_exp2f(S[s >> 1][8 * (s & 1) + jj] - m_ref);
+          psum += p;
+          P.p[s][jj] = (__bf16)p;
+        }
       }
     }
     l_run += psum;
@@ -1441,7 +1506,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     }
     const unsigned po = (qr >= 0 && h == 0) ? (unsigned)qr * 4 : kOut;
     const auto rP = __builtin_amdgcn_make_buffer_rsrc(a.peak + bh * a.Ns, (short)0, a.Ns * 4, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_amdgcn_exp2f(m_true - m_ref) * inv), rP, po, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pk * inv), rP, po, 0, 0);
     if (a.lse) {
       const auto rL = __builtin_amdgcn_make_buffer_rsrc(a.lse + bh * a.Ns, (short)0, a.Ns * 4, 0x00020000);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref + __builtin_log2f(l_tot)), rL, po, 0, 0);
@@ -1449,7 +1514,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
     m_ref = -INFINITY;
-    m_true = -INFINITY;
+    pk = 0.f;
     l_run = 0.f;
   };
   auto phase_barrier = [&]() {
@@ -1477,9 +1542,13 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
     STile S = {};
     PTile P = {};
     Cursor ck = cursor_at(2), cv = cursor_at(1);   // K of step j+2, V of step j+1
+    // the head of the current row tile keeps a short last context block
+    bool ctx_tail = pooled_ctx_tail(a, tile_bh(0));
     auto step = [&](auto ph, int j) {
       constexpr int Z = decltype(ph)::value;   // j % 3
       const int kt = j % ntk, ri = j / ntk;
+      if (kt == 0 && j > 0 && ri < nr) ctx_tail = pooled_ctx_tail(a, tile_bh(ri));
+      const bool uni = pooled_uniform_tile(a, kt, ctx_tail);
       // X_j at raised wave priority (step `total` computes an S that is not used)
       if (kt == 0 && j > 0) {
 #pragma unroll
@@ -1499,7 +1568,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
         const bool more_k = j + 2 < total, more_v = j + 1 < total;
         if (more_k) load_k((Z + 2) % 3, ck);
         if (more_v) load_tile(a.pv, lds_v, (Z + 1) % 3, cv);
-        if (j < total) P = softmax(Z, S);
+        if (j < total) P = softmax(Z, S, uni);
         // the loads of Y_{j-1} have landed before the barrier that closes Y_j
         // (this step's 8 query loads or 9-10 output stores, if any, were
         // issued before its tiles)
@@ -1523,7 +1592,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
           __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
         }
       } else {
-        if (j < total) P = softmax(Z, S);
+        if (j < total) P = softmax(Z, S, uni);
       }
       // (outside the group branch, so that the cursors stay scalar)
       advance(ck);
@@ -1616,6 +1685,8 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
   a.n_keytab = L.n_keytab;
   a.kc = L.kc; a.nb_c = L.nb_c; a.b = L.b; a.tail_c = L.tail_c;
   a.mk_pad = L.mk_pad;
+  a.mk = L.mk;
+  a.tail_s = L.tail_s;
   a.nb_s = L.nb_s;
   return a;
 }
