@@ -10,7 +10,8 @@ if ROOT not in sys.path:
 
 # Per-case parity figures (max-abs, rel-L2, score errors, ambiguous counts)
 # collected by the GPU parity tests; printed in the terminal summary, so they
-# survive output capture, and written to gpurun_out/parity_records.json.
+# survive output capture, and written as JSON to the file that the
+# ISA_PARITY_RECORDS environment variable names, when it is set.
 _RECORDS = []
 
 
@@ -29,10 +30,12 @@ def pytest_terminal_summary(terminalreporter):
     terminalreporter.section("parity records")
     for rec in _RECORDS:
         terminalreporter.write_line(json.dumps(rec, sort_keys=True))
-    out = os.path.join(ROOT, "gpurun_out")
+    path = os.environ.get("ISA_PARITY_RECORDS")
+    if not path:
+        return
     try:
-        os.makedirs(out, exist_ok=True)
-        with open(os.path.join(out, "parity_records.json"), "w") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "w") as f:
             json.dump(_RECORDS, f, indent=1, sort_keys=True)
     except OSError:
         pass
