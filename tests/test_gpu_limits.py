@@ -1,0 +1,114 @@
+"""GPU parity at the largest head count the library accepts, B*H = 65535.
+
+Several launches put B*H on grid y (the saliency pass, the backward's
+pruned-row zeroing), or run one workgroup per head on grid x (the two
+selections), and the persistent kernels deal heads out in turn, so the last
+heads are where an indexing or grid limit would show.  The heads are tiny
+(a few rows, ragged blocks), so the check is cheap per head: a fixed sample
+of about 1700 heads -- the first and last 512 and every 97th one -- is
+compared with the oracle as in test_gpu_parity (pooled means, scores, index
+sets, every output row), and every head's output must be finite and inside
+the range of its value rows (each output row is a convex combination of
+them, up to bf16 rounding).  Pooled vectors of two or three tokens with
+sharp queries are long, so the bf16 hi + lo representation of the pooled
+operands moves saliency and sharpness by up to a few 1e-6 here: both
+tolerances, and the bands of the two set checks, widen to the bounds of
+_saliency_bound and _sharpness_bound where those exceed 1e-6 (recorded)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import isa_oracle as orc
+from oracle import isa_oracle_backward as bwd
+from sparse_attention_context_amd import isa
+from sparse_attention_context_amd.synth import make_inputs, round_to_bf16
+from tests.parity_util import assert_output, device_tensor
+from tests.test_gpu_backward import GRAD_MAXREL, GRAD_RELL2, _grad_errors
+from tests.test_gpu_parity import _host_views, _plan_checks
+
+pytestmark = pytest.mark.gpu
+
+MAX_BH = 65535
+
+
+def _sample_heads(n):
+    return sorted(set(range(min(512, n))) | set(range(max(0, n - 512), n)) | set(range(0, n, 97)))
+
+
+def _in_value_range(O, V):
+    """O [heads, rows, d], V [heads, keys, d]: every output entry lies within
+    [min, max] of its head's value column (plus bf16 slack)."""
+    lo = V.min(axis=1, keepdims=True)   # [heads, 1, d]
+    hi = V.max(axis=1, keepdims=True)
+    slack = 2.0 ** -7 * np.maximum(np.abs(lo), np.abs(hi)) + 1e-6
+    return bool(np.all(np.isfinite(O)) and np.all(O >= lo - slack) and np.all(O <= hi + slack))
+
+
+CASES = [
+    # B, H, d, Ns, Nc, b, rho, gamma
+    (3, 21845, 64, 5, 3, 2, 0.5, 0.5),
+    (1, 65535, 128, 7, 5, 3, 0.5, 0.4),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dH%dd%d_Ns%d_Nc%d_b%d_r%g_g%g" % c)
+def test_most_heads_forward(case, parity_record):
+    B, H, d, Ns, Nc, b, rho, gamma = case
+    assert B * H == MAX_BH
+    print("heads limit case %s" % (case,), flush=True)
+    Q, K, V = make_inputs(B, H, d, Ns, Nc, seed=Ns + Nc + d, dtype="bf16")
+    Qd, Kd, Vd = (device_tensor(t, "bf16") for t in (Q, K, V))
+    O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
+    torch.cuda.synchronize()
+    Oh = O.float().cpu().numpy()
+    assert _in_value_range(Oh.reshape(B * H, Ns, d), V.reshape(B * H, Ns + Nc, d))
+    hv = _host_views(isa.plan_views(Qd, Kd, ws, b, rho, gamma))
+    rec = {"case": "heads limit B%dH%dd%d_Ns%d_Nc%d_b%d" % (B, H, d, Ns, Nc, b), "maxabs": 0.0, "rel_l2": 0.0,
+           "max_sal_err": 0.0, "max_sh_err": 0.0, "sal_bound": 0.0, "sh_bound": 0.0, "ambiguous_ctx": 0,
+           "ambiguous_q": 0, "heads_compared": 0}
+    heads = _sample_heads(B * H)
+    for i, g in enumerate(heads):
+        x, h = divmod(g, H)
+        st, kept, full = _plan_checks(Q[x, h], K[x, h], V[x, h], b, rho, gamma, hv, x, h, sh_bound=True,
+                                      sal_bound=True)
+        Oref = orc.oracle_forward_head(Q[x, h], K[x, h], V[x, h], b, kept, full)
+        maxabs, rel = assert_output(Oh[x, h], Oref, "bf16")
+        rec["maxabs"] = max(rec["maxabs"], maxabs)
+        rec["rel_l2"] = max(rec["rel_l2"], rel)
+        rec["max_sal_err"] = max(rec["max_sal_err"], st["sal_err"])
+        rec["max_sh_err"] = max(rec["max_sh_err"], st["sh_err"])
+        rec["sal_bound"] = max(rec["sal_bound"], st.get("sal_bound", 0.0))
+        rec["sh_bound"] = max(rec["sh_bound"], st.get("sh_bound", 0.0))
+        rec["ambiguous_ctx"] += st["amb_ctx"]
+        rec["ambiguous_q"] += st["amb_q"]
+        if i % 500 == 499:
+            print("  %d heads compared" % (i + 1), flush=True)
+    rec["heads_compared"] = len(heads)
+    parity_record(rec)
+
+
+def test_most_heads_backward():
+    B, H, d, Ns, Nc, b, rho, gamma = 1, MAX_BH, 128, 7, 5, 3, 0.5, 0.4
+    print("heads limit backward", flush=True)
+    Q, K, V = make_inputs(B, H, d, Ns, Nc, seed=77, dtype="bf16")
+    dO = round_to_bf16(np.random.default_rng(78).standard_normal((B, H, Ns, d)).astype(np.float32))
+    Qd, Kd, Vd, dOd = (device_tensor(t, "bf16") for t in (Q, K, V, dO))
+    O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
+    dQ, dK, dV, _ = isa.backward(Qd, Kd, Vd, O, dOd, ws, b, rho, gamma)
+    torch.cuda.synchronize()
+    views = isa.plan_views(Qd, Kd, ws, b, rho, gamma)
+    kept = views["kept_ctx"].cpu().numpy()
+    full = views["full_q"].cpu().numpy()
+    heads = _sample_heads(H)
+    got = [g.float().cpu().numpy()[0, heads] for g in (dQ, dK, dV)]
+    assert all(np.all(np.isfinite(g)) for g in got)
+    ref = [np.zeros_like(g, dtype=np.float64) for g in got]
+    for i, h in enumerate(heads):
+        r = bwd.oracle_backward_head(Q[0, h], K[0, h], V[0, h], dO[0, h], b, kept[0, h], full[0, h])
+        for t in range(3):
+            ref[t][i] = r[t]
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        maxrel, rel = _grad_errors(g, r)
+        print("  %s max/scale %.2e rel-L2 %.2e over %d heads" % (name, maxrel, rel, len(heads)), flush=True)
+        assert maxrel <= GRAD_MAXREL and rel <= GRAD_RELL2, (name, maxrel, rel)

@@ -61,12 +61,47 @@ def _sharpness_bound(Qh, kbar_gpu, kbar_ref, n, src):
     return max(float(row[a:e].mean()) for a, e in src) + 2e-7
 
 
-def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol=BAND, sh_bound=False):
+def _saliency_bound(qbar_gpu, kbar_gpu, qbar_ref, kbar_ref, n, nb_s):
+    """Bound on the part of |sal_gpu - sal_ref| that the saliency pass's
+    operand representation causes.
+
+    The kernel splits every fp32 pooled query and key into bf16 hi + lo and
+    forms hi.hi + hi.lo + lo.hi, so each logit is off by e_ij = (qbar_i .
+    kbar_j - that sum) / sqrt(d), computed here exactly from the GPU's own
+    fp32 means (the split) and the oracle's fp64 ones (the exact logit).
+    Logits of a row moved by at most E_i = max_j |e_ij| change each of its
+    n-weighted softmax probabilities by at most a factor exp(+-2 E_i); a
+    context block's saliency sums its column over the pooled queries.  The
+    2e-7 added is an allowance for the fp32 exponentials, as in
+    _sharpness_bound.  The representation term stays below 1e-7 on the
+    benchmark shapes and reaches a few 1e-6 for blocks of two or three tokens
+    with sharp queries, whose pooled vectors are long."""
+    def split(a):
+        a32 = np.asarray(a, dtype=np.float32)
+        hi = torch.from_numpy(np.ascontiguousarray(a32)).to(torch.bfloat16).float().numpy()
+        lo = torch.from_numpy(np.ascontiguousarray(a32 - hi)).to(torch.bfloat16).float().numpy()
+        return hi.astype(np.float64), lo.astype(np.float64)
+    qh, ql = split(qbar_gpu)
+    kh, kl = split(kbar_gpu)
+    qr = np.asarray(qbar_ref, np.float64)
+    kr = np.asarray(kbar_ref, np.float64)
+    d = qr.shape[1]
+    E = np.abs(qr @ kr.T - (qh @ kh.T + qh @ kl.T + ql @ kh.T)).max(axis=1) / np.sqrt(d)
+    z = qr @ kr.T / np.sqrt(d) + np.log(n)[None, :]
+    z -= z.max(axis=1, keepdims=True)
+    P = np.exp(z)
+    P /= P.sum(axis=1, keepdims=True)
+    return float((P[:, nb_s:] * np.expm1(2.0 * E)[:, None]).sum(axis=0).max(initial=0.0)) + 2e-7
+
+
+def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol=BAND, sh_bound=False,
+                 sal_bound=False):
     """Checks pooled means, scores and index sets of one (batch, head) of a
     GPU run (host views hv) against the oracle.  Scores must lie within
     score_tol of the oracle's (at most the 1e-6 band of the set check).
-    sh_bound: the sharpness tolerance, and the band of the query-set check,
-    may widen to the bound of _sharpness_bound for inputs whose pooled-key
+    sh_bound (sal_bound): the sharpness (saliency) tolerance, and the band of
+    the query-set (context-set) check, may widen to the bound of
+    _sharpness_bound (_saliency_bound) for inputs whose pooled-vector
     rounding moves the scores by more than the band.
     Returns the head's figures and its GPU lists (kept, full)."""
     Ns = Qh.shape[0]
@@ -91,10 +126,15 @@ def _plan_checks(Qh, Kh, Vh, b, rho, gamma, hv, x, h, check_pool=True, score_tol
         assert stats["pool_err"] <= 2e-6, errs
 
     sal = hv["sal"][x, h]
+    sal_tol, c_band = score_tol, BAND
+    if sal_bound and nb_c:
+        bound = _saliency_bound(hv["qbar"][x, h], hv["kbar"][x, h], ref["qbar"], ref["kbar"], ref["n"], nb_s)
+        stats["sal_bound"] = bound
+        sal_tol, c_band = max(score_tol, bound), max(BAND, bound)
     if nb_c:
         stats["sal_err"] = float(np.max(np.abs(sal - ref["sal"])))
-        assert stats["sal_err"] < score_tol, stats["sal_err"]
-    stats["amb_ctx"] = check_set(kept, ref["sal"], kc)
+        assert stats["sal_err"] < sal_tol, (stats["sal_err"], sal_tol)
+    stats["amb_ctx"] = check_set(kept, ref["sal"], kc, band=c_band)
 
     # sharpness against the oracle on the GPU's kept set
     keyset = np.concatenate([np.arange(nb_s), nb_s + kept.astype(np.int64)])
