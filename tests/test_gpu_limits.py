@@ -22,8 +22,8 @@ import torch
 from oracle import isa_oracle as orc
 from oracle import isa_oracle_backward as bwd
 from sparse_attention_context_amd import isa
-from sparse_attention_context_amd.synth import make_inputs, round_to_bf16
-from tests.parity_util import assert_output, device_tensor
+from sparse_attention_context_amd.synth import make_inputs, make_inputs_device, round_to_bf16
+from tests.parity_util import assert_output, check_set, device_tensor
 from tests.test_gpu_backward import GRAD_MAXREL, GRAD_RELL2, _grad_errors
 from tests.test_gpu_parity import _host_views, _plan_checks
 
@@ -112,3 +112,74 @@ def test_most_heads_backward():
         maxrel, rel = _grad_errors(g, r)
         print("  %s max/scale %.2e rel-L2 %.2e over %d heads" % (name, maxrel, rel, len(heads)), flush=True)
         assert maxrel <= GRAD_MAXREL and rel <= GRAD_RELL2, (name, maxrel, rel)
+
+
+def test_largest_head_span(parity_record):
+    """One head at d = 128 whose K and V each span just under 2^31 bytes,
+    the most the kernels' 32-bit offsets address (Ns + Nc = 8388300 rows of
+    256 bytes), b = 256 with ragged last blocks on both sides, 1/4 of the
+    context kept and 0.2 % of the query blocks on the full route (33 blocks,
+    each over 5.2 M keys).  The oracle checks what it can at this size: every
+    pooled query and key mean, every saliency score and the kept set; the
+    sharpness of 16 blocks (the first, the last, the full route's first and
+    last, and spread ones); the query set as the top-k of the GPU's own
+    scores under the tie rule; and 264 output rows (two of each of four full
+    blocks, 256 Taylor rows), element by element."""
+    B, H, d, Ns, Nc, b, rho, gamma = 1, 1, 128, 4194000, 4194300, 256, 0.25, 0.002
+    assert (Ns + Nc) * d * 2 < 1 << 31 <= (Ns + Nc + 8192) * d * 2
+    print("largest head span: Ns %d Nc %d" % (Ns, Nc), flush=True)
+    dev = torch.device("cuda:0")
+    Qd, Kd, Vd = make_inputs_device(B, H, d, Ns, Nc, 4242, dev, "bf16")
+    O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
+    torch.cuda.synchronize()
+    hv = _host_views(isa.plan_views(Qd, Kd, ws, b, rho, gamma))
+    Q = Qd[0, 0].double().cpu().numpy()
+    K = Kd[0, 0].double().cpu().numpy()
+    V = Vd[0, 0].double().cpu().numpy()
+    Oh = O[0, 0].float().cpu().numpy()
+    del Qd, Kd, Vd, O, ws
+    torch.cuda.empty_cache()
+    print("  layer ran; oracle pooling", flush=True)
+    src, ctx = orc.block_ranges(Ns, Nc, b)
+    nb_s, nb_c = len(src), len(ctx)
+    kc, kq = orc.count_rule(rho, nb_c), orc.count_rule(gamma, nb_s)
+    qbar, _ = orc.pool_blocks(Q, src)
+    kbar, n = orc.pool_blocks(K, src + ctx)
+    kept = hv["kept_ctx"][0, 0]
+    full = hv["full_q"][0, 0]
+    assert len(kept) == kc and len(full) == kq
+    have = list(range(nb_s)) + [nb_s + int(c) for c in kept]
+    vbar, _ = orc.pool_blocks(V, [(src + ctx)[j] for j in have])
+    pool_err = max(float(np.abs(hv["qbar"][0, 0] - qbar).max()), float(np.abs(hv["kbar"][0, 0] - kbar).max()),
+                   float(np.abs(hv["vbar"][0, 0][have] - vbar).max()))
+    assert pool_err <= 2e-6, pool_err
+    print("  saliency", flush=True)
+    sal = orc.saliency_scores(qbar, kbar, n, nb_s)
+    sal_err = float(np.abs(hv["sal"][0, 0] - sal).max())
+    assert sal_err < 1e-6, sal_err
+    amb_ctx = check_set(kept, sal, kc)
+    print("  sharpness of sampled blocks", flush=True)
+    keyset = np.concatenate([np.arange(nb_s), nb_s + kept.astype(np.int64)])
+    blocks = sorted({0, nb_s - 1, int(full[0]), int(full[-1])} | set(range(0, nb_s, nb_s // 12)))
+    sh_ref = orc.sharpness_scores(Q, [src[i] for i in blocks], kbar[keyset], n[keyset])
+    sh = hv["sh"][0, 0]
+    sh_err = float(np.abs(sh[blocks] - sh_ref).max())
+    assert sh_err < 1e-6, sh_err
+    # the query set is the top-kq of the GPU's own scores, ties to the lower index
+    assert full.tolist() == orc.top_indices(sh, kq).tolist()
+    tayl = hv["taylor_q"][0, 0]
+    assert sorted(set(full.tolist()) | set(tayl.tolist())) == list(range(nb_s))
+    print("  sampled output rows", flush=True)
+    rng = np.random.default_rng(5)
+    rows = set()
+    for i in (int(full[0]), int(full[1]), int(full[-2]), int(full[-1])):
+        s, e = src[i]
+        rows |= {s, e - 1}
+    taylor_rows = np.concatenate([np.arange(s, e) for s, e in (src[int(t)] for t in tayl[:: max(1, len(tayl) // 64)])])
+    rows |= set(rng.choice(taylor_rows, 255, replace=False).tolist()) | {Ns - 1}
+    rows = np.array(sorted(rows))
+    Oref = orc.oracle_forward_head(Q, K, V, b, kept, full, rows=rows)
+    maxabs, rel = assert_output(Oh[rows], Oref, "bf16")
+    parity_record({"case": "largest head span Ns %d Nc %d b %d" % (Ns, Nc, b), "maxabs": maxabs, "rel_l2": rel,
+                   "max_pool_err": pool_err, "max_sal_err": sal_err, "max_sh_err": sh_err,
+                   "ambiguous_ctx": amb_ctx, "rows_compared": int(rows.size), "sh_blocks_compared": len(blocks)})
