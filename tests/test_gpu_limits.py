@@ -114,22 +114,32 @@ def test_most_heads_backward():
         assert maxrel <= GRAD_MAXREL and rel <= GRAD_RELL2, (name, maxrel, rel)
 
 
-def test_largest_head_span(parity_record):
-    """One head at d = 128 whose K and V each span just under 2^31 bytes,
-    the most the kernels' 32-bit offsets address (Ns + Nc = 8388300 rows of
-    256 bytes), b = 256 with ragged last blocks on both sides, 1/4 of the
-    context kept and 0.2 % of the query blocks on the full route (33 blocks,
-    each over 5.2 M keys).  The oracle checks what it can at this size: every
-    pooled query and key mean, every saliency score and the kept set; the
-    sharpness of 16 blocks (the first, the last, the full route's first and
-    last, and spread ones); the query set as the top-k of the GPU's own
-    scores under the tie rule; and 264 output rows (two of each of four full
-    blocks, 256 Taylor rows), element by element."""
-    B, H, d, Ns, Nc, b, rho, gamma = 1, 1, 128, 4194000, 4194300, 256, 0.25, 0.002
-    assert (Ns + Nc) * d * 2 < 1 << 31 <= (Ns + Nc + 8192) * d * 2
-    print("largest head span: Ns %d Nc %d" % (Ns, Nc), flush=True)
+SPAN_CASES = [
+    # d, Ns, Nc, rho, gamma: K and V span just under 2^31 bytes per head
+    (128, 4194000, 4194300, 0.25, 0.002),
+    (64, 8388000, 8389215, 0.25, 0.001),    # also the largest row count, Ns + Nc = 2^24 - 1
+]
+
+
+@pytest.mark.parametrize("case", SPAN_CASES, ids=lambda c: "d%d_Ns%d_Nc%d" % c[:3])
+def test_largest_head_span(case, parity_record):
+    """One head whose K and V each span just under 2^31 bytes, the most the
+    kernels' 32-bit offsets address (at d = 64 also the largest row count
+    the library accepts), b = 256 with ragged last blocks on both sides, a
+    quarter of the context kept and 33 query blocks on the full route, each
+    over millions of keys.  The oracle checks what it can at this size:
+    every pooled query and key mean, every saliency score (the oracle run on
+    chunks of the pooled queries, whose column sums add up) and the kept
+    set; the sharpness of 16 blocks (the first, the last, the full route's
+    first and last, and spread ones); the query set as the top-k of the GPU's
+    own scores under the tie rule; and 264 output rows (two of each of four
+    full blocks, 256 Taylor rows), element by element."""
+    d, Ns, Nc, rho, gamma = case
+    B, H, b = 1, 1, 256
+    assert Ns + Nc < 1 << 24 and (Ns + Nc) * d * 2 < 1 << 31 <= (Ns + Nc + 8192) * d * 2
+    print("largest head span: d %d Ns %d Nc %d" % (d, Ns, Nc), flush=True)
     dev = torch.device("cuda:0")
-    Qd, Kd, Vd = make_inputs_device(B, H, d, Ns, Nc, 4242, dev, "bf16")
+    Qd, Kd, Vd = make_inputs_device(B, H, d, Ns, Nc, 4242 + d, dev, "bf16")
     O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
     torch.cuda.synchronize()
     hv = _host_views(isa.plan_views(Qd, Kd, ws, b, rho, gamma))
@@ -154,7 +164,7 @@ def test_largest_head_span(parity_record):
                    float(np.abs(hv["vbar"][0, 0][have] - vbar).max()))
     assert pool_err <= 2e-6, pool_err
     print("  saliency", flush=True)
-    sal = orc.saliency_scores(qbar, kbar, n, nb_s)
+    sal = sum(orc.saliency_scores(qbar[i:i + 4096], kbar, n, nb_s) for i in range(0, nb_s, 4096))
     sal_err = float(np.abs(hv["sal"][0, 0] - sal).max())
     assert sal_err < 1e-6, sal_err
     amb_ctx = check_set(kept, sal, kc)
@@ -180,6 +190,6 @@ def test_largest_head_span(parity_record):
     rows = np.array(sorted(rows))
     Oref = orc.oracle_forward_head(Q, K, V, b, kept, full, rows=rows)
     maxabs, rel = assert_output(Oh[rows], Oref, "bf16")
-    parity_record({"case": "largest head span Ns %d Nc %d b %d" % (Ns, Nc, b), "maxabs": maxabs, "rel_l2": rel,
-                   "max_pool_err": pool_err, "max_sal_err": sal_err, "max_sh_err": sh_err,
+    parity_record({"case": "largest head span d %d Ns %d Nc %d b %d" % (d, Ns, Nc, b), "maxabs": maxabs,
+                   "rel_l2": rel, "max_pool_err": pool_err, "max_sal_err": sal_err, "max_sh_err": sh_err,
                    "ambiguous_ctx": amb_ctx, "rows_compared": int(rows.size), "sh_blocks_compared": len(blocks)})
