@@ -193,3 +193,105 @@ def test_largest_head_span(case, parity_record):
     parity_record({"case": "largest head span d %d Ns %d Nc %d b %d" % (d, Ns, Nc, b), "maxabs": maxabs,
                    "rel_l2": rel, "max_pool_err": pool_err, "max_sal_err": sal_err, "max_sh_err": sh_err,
                    "ambiguous_ctx": amb_ctx, "rows_compared": int(rows.size), "sh_blocks_compared": len(blocks)})
+
+
+@pytest.mark.parametrize("case", SPAN_CASES, ids=lambda c: "d%d_Ns%d_Nc%d" % c[:3])
+def test_largest_head_span_backward(case):
+    """The backward pass on the largest head span (the shapes above).
+
+    Rows of pruned context blocks must be exactly zero, and two sums that
+    hold at any size are checked per feature c in fp64:
+      sum_t dV_t = sum_i dO_i: the kernels round p to bf16 before dV = p^T dO
+        (a row's weights then sum to 1 within 2^-9) and round dV to bf16, so
+        |sum_t dV_tc - sum_i dO_ic| <= 2^-9 (sum_i |dO_ic| + sum_t |dV_tc|);
+      sum_t dK_t = 0: with ds_it = p_it (dP_it - D_i), sum_t ds_it vanishes
+        up to the bf16 rounding of ds (2^-9 of sum_t |ds_it| <= 2 max_t |dP_it|
+        <= 2 |dO_i|_1 max|V|) and of the output in D_i (2^-9 |o_i| |dO_i|_1), so
+        |sum_t dK_tc| <= 2^-9 sum_t |dK_tc| + 2^-7 max|V| sum_i |dO_i|_1 |q_ic| / sqrt d.
+    (Both are worst-case bounds of the roundings; the measured sums sit far
+    inside them and are printed.)
+
+    dQ of 264 sampled rows (8 full-route rows over all 5.2 M or 10.5 M kept
+    tokens, 256 Taylor rows) against the oracle's row gradients.  The
+    kernels take D_i = dO_i . o_i from the layer's bf16 output, as flash
+    attention does; the oracle takes it from the exact output.  Since dq_i
+    is linear in D_i (dq_i = sum_t p_it (dP_it - D_i) k_t / sqrt d), the
+    oracle's gradient is moved by -(D~_i - D_i) kt_i / sqrt d, kt_i the
+    row's probability-weighted key (the oracle's attention with the keys as
+    values), and the GPU's rows are held to that within the backward's bf16
+    bound.  On a sharp row (one key takes almost all the weight) dP_it - D_i
+    nearly cancels, so this shift is the whole gradient there: a few 1e-2
+    at most, against ~4e-3 for an ordinary row of a 10 M-key head (printed).
+    """
+    d, Ns, Nc, rho, gamma = case
+    B, H, b = 1, 1, 256
+    print("largest head span backward: d %d Ns %d Nc %d" % (d, Ns, Nc), flush=True)
+    dev = torch.device("cuda:0")
+    Qd, Kd, Vd = make_inputs_device(B, H, d, Ns, Nc, 5252 + d, dev, "bf16")
+    g = torch.Generator(device=dev).manual_seed(53 + d)
+    dOd = torch.randn(Qd.shape, generator=g, device=dev).to(torch.bfloat16)
+    O, ws = isa.attention(Qd, Kd, Vd, b, rho, gamma)
+    dQ, dK, dV, _ = isa.backward(Qd, Kd, Vd, O, dOd, ws, b, rho, gamma)
+    torch.cuda.synchronize()
+    views = isa.plan_views(Qd, Kd, ws, b, rho, gamma)
+    kept = views["kept_ctx"][0, 0].cpu().numpy()
+    full = views["full_q"][0, 0].cpu().numpy()
+    tayl = views["taylor_q"][0, 0].cpu().numpy()
+    src, ctx = orc.block_ranges(Ns, Nc, b)
+    # the two sums and the pruned rows, on the GPU in fp64
+    dK64, dV64, dO64 = dK[0, 0].double(), dV[0, 0].double(), dOd[0, 0].double()
+    vmax = float(Vd.float().abs().max())
+    dv_gap = (dV64.sum(0) - dO64.sum(0)).abs()
+    dv_tol = 2.0 ** -9 * (dO64.abs().sum(0) + dV64.abs().sum(0))
+    dk_gap = dK64.sum(0).abs()
+    dk_tol = 2.0 ** -9 * dK64.abs().sum(0) + 2.0 ** -7 * vmax * (
+        dO64.abs().sum(1, keepdim=True) * Qd[0, 0].double().abs()).sum(0) / np.sqrt(d)
+    print("  sum dV - sum dO: max %.3g (bound %.3g); sum dK: max %.3g (bound %.3g)" % (
+        float(dv_gap.max()), float(dv_tol.min()), float(dk_gap.max()), float(dk_tol.min())), flush=True)
+    assert bool((dv_gap <= dv_tol).all()) and bool((dk_gap <= dk_tol).all())
+    keep = set(int(c) for c in kept)
+    for c, (s, e) in enumerate(ctx):
+        if c not in keep:
+            assert not bool(dK[0, 0, s:e].any()) and not bool(dV[0, 0, s:e].any()), c
+    del dK64, dV64, dO64
+    # dQ of sampled rows against the oracle's row gradients
+    rng = np.random.default_rng(6)
+    full_rows = []
+    for i in (int(full[0]), int(full[1]), int(full[-2]), int(full[-1])):
+        s, e = src[i]
+        full_rows += [s, e - 1]
+    taylor_rows = np.concatenate([np.arange(s, e) for s, e in (src[int(t)] for t in tayl[:: max(1, len(tayl) // 64)])])
+    tay_rows = np.array(sorted(set(rng.choice(taylor_rows, 256, replace=False).tolist())))
+    full_rows = np.array(sorted(full_rows))
+    Q = Qd[0, 0].double().cpu().numpy()
+    K = Kd[0, 0].double().cpu().numpy()
+    V = Vd[0, 0].double().cpu().numpy()
+    dO = dOd[0, 0].double().cpu().numpy()
+    dQh = dQ[0, 0].float().cpu().numpy()
+    Oh = O[0, 0].double().cpu().numpy()
+    del Qd, Kd, Vd, O, ws, dQ, dK, dV, dOd
+    torch.cuda.empty_cache()
+    print("  oracle row gradients", flush=True)
+    kept_blocks = src + [ctx[int(c)] for c in kept]
+    tok = np.concatenate([np.arange(s, e) for s, e in kept_blocks])
+    Kt, Vt = K[tok], V[tok]
+    qf, gf = Q[full_rows], dO[full_rows]
+    dq_full, _, _ = bwd.full_attention_rows_backward(qf, Kt, Vt, gf)
+    o_full, kt_full = orc.full_attention_rows(qf, Kt, Vt), orc.full_attention_rows(qf, Kt, Kt)
+    del Kt, Vt
+    kbar, n = orc.pool_blocks(K, kept_blocks)
+    vbar, _ = orc.pool_blocks(V, kept_blocks)
+    qt, gt = Q[tay_rows], dO[tay_rows]
+    dq_tay, _, _ = bwd.taylor_attention_rows_backward(qt, kbar, vbar, n, gt)
+    o_tay, kt_tay = orc.taylor_attention_rows(qt, kbar, vbar, n), orc.taylor_attention_rows(qt, kbar, kbar, n)
+    rows = np.concatenate([full_rows, tay_rows])
+    ref = np.concatenate([dq_full, dq_tay])
+    dD = (np.concatenate([gf, gt]) * (Oh[rows] - np.concatenate([o_full, o_tay]))).sum(axis=1)
+    shift = -dD[:, None] * np.concatenate([kt_full, kt_tay]) / np.sqrt(d)
+    raw_maxrel, raw_rel = _grad_errors(dQh[rows], ref)
+    maxrel, rel = _grad_errors(dQh[rows], ref + shift)
+    print("  dQ rows against the exact-D oracle: max/scale %.2e rel-L2 %.2e; largest D shift %.2e (row gradients "
+          "up to %.2e)" % (raw_maxrel, raw_rel, float(np.abs(shift).max()), float(np.abs(ref).max())), flush=True)
+    print("  dQ rows against the oracle moved to the output's D: max/scale %.2e rel-L2 %.2e" % (maxrel, rel),
+          flush=True)
+    assert maxrel <= GRAD_MAXREL and rel <= GRAD_RELL2, (maxrel, rel)
