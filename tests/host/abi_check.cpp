@@ -216,7 +216,7 @@ int main() {
       agree += got == want;
       disjoint += want;
     }
-    printf("overlap test: %d of 4000 layouts disjoint, verdict agrees with brute force on %d\n", disjoint, agree);
+    printf("overlap test: %d of 4000 layouts disjoint, the check agrees with brute force on %d\n", disjoint, agree);
     CHECK(disjoint > 200 && agree > 3000);
   }
 
