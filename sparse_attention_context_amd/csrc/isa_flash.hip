@@ -146,11 +146,13 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  // work item lid: row tile fastest, then key split, then head, so that the
+  // workgroups running at once on an XCD share one K/V range in its L2
   const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int split = lid % a.nsplit;
-  const int rest = lid / a.nsplit;
-  const int bh = rest / a.row_tiles;
-  const int rt = rest - bh * a.row_tiles;
+  const int rt = lid % a.row_tiles;
+  const int rest = lid / a.row_tiles;
+  const int split = rest % a.nsplit;
+  const int bh = rest / a.nsplit;
 
   // ---- query row of this lane (invalid rows read row 0 and store nothing)
   const long long vrow = (long long)rt * BM + w * 32 + l32;
@@ -506,11 +508,13 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
+  // work item lid: row tile fastest, then key split, then head, so that the
+  // workgroups running at once on an XCD share one K/V range in its L2
   const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int split = lid % a.nsplit;
-  const int rest = lid / a.nsplit;
-  const int bh = rest / a.row_tiles;
-  const int rt = rest - bh * a.row_tiles;
+  const int rt = lid % a.row_tiles;
+  const int rest = lid / a.row_tiles;
+  const int split = rest % a.nsplit;
+  const int bh = rest / a.nsplit;
 
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   int qrow;
@@ -884,12 +888,14 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
 
   struct Item { int bh, rt, split, t_begin, nt; };
   auto item_of = [&](int r) -> Item {
+    // (item order of isa_flash_pp_kernel: row tile fastest, then split, then head)
     const int lid = xcd_remap((int)blockIdx.x + r * G, n_items);
-    const int split = lid % a.nsplit;
-    const int rest = lid / a.nsplit;
-    const int bh = rest / a.row_tiles;
+    const int rt = lid % a.row_tiles;
+    const int rest = lid / a.row_tiles;
+    const int split = rest % a.nsplit;
+    const int bh = rest / a.nsplit;
     const int tb = split * a.tiles_per_split;
-    return Item{bh, rest - bh * a.row_tiles, split, tb, min(a.tiles_per_split, ntiles - tb)};
+    return Item{bh, rt, split, tb, min(a.tiles_per_split, ntiles - tb)};
   };
   // per item: each lane's query row and the head's valid key count
   for (int r = 0; r < nr; ++r) {

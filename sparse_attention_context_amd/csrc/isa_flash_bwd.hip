@@ -173,11 +173,14 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  // work item lid: row tile fastest, then key split, then head (as the
+  // forward flash kernels), so that the workgroups running at once on an XCD
+  // share one K/V range in its L2
   const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int split = lid % a.nsplit;
-  const int rest = lid / a.nsplit;
-  const int bh = rest / a.row_tiles;
-  const int rt = rest - bh * a.row_tiles;
+  const int rt = lid % a.row_tiles;
+  const int rest = lid / a.row_tiles;
+  const int split = rest % a.nsplit;
+  const int bh = rest / a.nsplit;
 
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   const int qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
@@ -1146,11 +1149,14 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
+  // work item lid: row tile fastest, then key split, then head (as the
+  // forward flash kernels), so that the workgroups running at once on an XCD
+  // share one K/V range in its L2
   const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int split = lid % a.nsplit;
-  const int rest = lid / a.nsplit;
-  const int bh = rest / a.row_tiles;
-  const int rt = rest - bh * a.row_tiles;
+  const int rt = lid % a.row_tiles;
+  const int rest = lid / a.row_tiles;
+  const int split = rest % a.nsplit;
+  const int bh = rest / a.nsplit;
 
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   const int qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);

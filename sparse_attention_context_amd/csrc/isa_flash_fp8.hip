@@ -196,11 +196,14 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_kernel(Fp8Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  // work item lid: row tile fastest, then key split, then head (as the
+  // forward flash kernels), so that the workgroups running at once on an XCD
+  // share one K/V range in its L2
   const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int split = lid % a.nsplit;
-  const int rest = lid / a.nsplit;
-  const int bh = rest / a.row_tiles;
-  const int rt = rest - bh * a.row_tiles;
+  const int rt = lid % a.row_tiles;
+  const int rest = lid / a.row_tiles;
+  const int split = rest % a.nsplit;
+  const int bh = rest / a.nsplit;
 
   // ---- query row, quantised: byte t of lane half h in MFMA u is d = 64u + 32(t/16) + 16h + t%16
   const long long vrow = (long long)rt * BM + w * 32 + l32;
@@ -447,11 +450,14 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_pp_kernel(Fp8Args a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
+  // work item lid: row tile fastest, then key split, then head (as the
+  // forward flash kernels), so that the workgroups running at once on an XCD
+  // share one K/V range in its L2
   const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int split = lid % a.nsplit;
-  const int rest = lid / a.nsplit;
-  const int bh = rest / a.row_tiles;
-  const int rt = rest - bh * a.row_tiles;
+  const int rt = lid % a.row_tiles;
+  const int rest = lid / a.row_tiles;
+  const int split = rest % a.nsplit;
+  const int bh = rest / a.nsplit;
 
   // ---- query row, quantised as in isa_flash_fp8_kernel
   const long long vrow = (long long)rt * BM + w * 32 + l32;
