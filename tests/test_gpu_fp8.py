@@ -41,16 +41,21 @@ def _pi_max(q, Kt):
     return p.max(axis=1) / p.sum(axis=1)
 
 
-def _assert_fp8(got, ref, q, Kt, Vt):
-    """Per-row bound of the module docstring; returns (maxabs, rel, worst
-    ratio of a row's error to its bound, largest bound)."""
+def _fp8_row_ratio(got, ref, q, Kt, Vt):
+    """Worst ratio of an entry's error to the per-row bound of the module
+    docstring, and the largest bound."""
     got = np.asarray(got, np.float64)
     bound = (2.0 * _pi_max(q, Kt) * float(np.abs(Vt).max()) / 8.0)[:, None] + 2.0 ** -8 * np.abs(ref) + 2e-3
-    err = np.abs(got - ref)
-    ratio = float((err / bound).max())
+    return float((np.abs(got - ref) / bound).max()), float(bound.max())
+
+
+def _assert_fp8(got, ref, q, Kt, Vt):
+    """Per-row bound of the module docstring and the rows' rel-L2; returns
+    (maxabs, rel, worst ratio of a row's error to its bound, largest bound)."""
+    ratio, bmax = _fp8_row_ratio(got, ref, q, Kt, Vt)
     maxabs, rel = out_errors(got, ref)
     assert ratio <= 1.0 and rel <= BF16_RELL2, (maxabs, ratio, rel)
-    return maxabs, rel, ratio, float(bound.max())
+    return maxabs, rel, ratio, bmax
 
 
 def _full_rows(full_q, b, Ns):
