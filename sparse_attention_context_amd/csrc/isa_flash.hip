@@ -100,7 +100,29 @@ struct FlashArgs {
   int row_tiles;
   int n_wg;
   float scale_log2;     // log2(e)/sqrt(d)
+  // full route at d = 128 (row tiles Ri = bh * row_tiles + rt): row tiles
+  // below sk_R0 whole, sk_K per persistent workgroup; the units
+  // u = (Ri - sk_R0) * sk_T + t of the rest (sk_U of them) in sk_G equal
+  // ranges, a row tile in at most sk_P of them
+  long long sk_U;
+  int sk_G, sk_P, sk_T, sk_R0, sk_K;
 };
+
+// Stream-K split of the full route (Osama et al., "Stream-K: Work-centric
+// Parallel Decomposition for Dense Matrix-Matrix Multiplication on the GPU",
+// its data-parallel + stream-K hybrid, applied to the key tiles of the
+// route's row tiles): whole row tiles in rounds of one per workgroup, so
+// that the workgroups of an XCD sweep one head's keys together, then the
+// units of the remaining row tiles in equal ranges, range g covering units
+// [sk_bound(g), sk_bound(g + 1)).  A row tile inside one range is finished
+// by that range's workgroup; one that meets several ranges is cut into
+// parts there, part p taken by range sk_range_of(first unit) + p, and
+// merged.
+__device__ __forceinline__ long long sk_bound(const FlashArgs& a, long long g) { return g * a.sk_U / a.sk_G; }
+// the range holding unit u: the largest g with sk_bound(g) <= u
+__device__ __forceinline__ int sk_range_of(const FlashArgs& a, long long u) {
+  return (int)(((u + 1) * a.sk_G + a.sk_U - 1) / a.sk_U - 1);
+}
 
 // Pooled mode: key tile kt of the packed kept set (keys 64 kt .. 64 kt + 63)
 // is uniform when every one of its blocks holds b rows, so that its bias is
@@ -508,13 +530,39 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  // work item lid: row tile fastest, then key split, then head, so that the
-  // workgroups running at once on an XCD share one K/V range in its L2
-  const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int rt = lid % a.row_tiles;
-  const int rest = lid / a.row_tiles;
-  const int split = rest % a.nsplit;
-  const int bh = rest / a.nsplit;
+  // Work item: gather mode (the full route), row tile Ri = bh * row_tiles +
+  // rt whole (lid = Ri < sk_R0), or part p of row tile Ri = sk_R0 + Rs under
+  // the stream-K ranges (lid = sk_R0 + Rs * sk_P + p; a row tile with fewer
+  // parts leaves its last workgroups without work); dense mode, row tile rt
+  // of head bh (one key range).  Consecutive items run on one XCD and share
+  // its L2.
+  int bh, rt, part = -1;   // part < 0: the whole row tile (output written here)
+  int Rs = 0;              // the row tile's index in the partial buffer
+  int t_begin = 0, t_end = 0;   // key tiles of the item (gather)
+  if constexpr (GATHER) {
+    const int lid = xcd_remap(blockIdx.x, a.n_wg);
+    int Ri = lid;
+    t_end = a.sk_T;
+    if (lid >= a.sk_R0) {
+      Rs = (lid - a.sk_R0) / a.sk_P;
+      const int p = lid - a.sk_R0 - Rs * a.sk_P;
+      Ri = a.sk_R0 + Rs;
+      const long long u0 = (long long)Rs * a.sk_T;
+      // (64-bit quotients come out in vector registers: made scalar again)
+      const int gf = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0));
+      const int gl = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0 + a.sk_T - 1));
+      if (p > gl - gf) return;
+      t_begin = __builtin_amdgcn_readfirstlane((int)max(sk_bound(a, gf + p) - u0, 0LL));
+      t_end = __builtin_amdgcn_readfirstlane((int)min(sk_bound(a, gf + p + 1) - u0, (long long)a.sk_T));
+      part = gl > gf ? p : -1;
+    }
+    bh = Ri / a.row_tiles;
+    rt = Ri - bh * a.row_tiles;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, a.n_wg);
+    rt = lid % a.row_tiles;
+    bh = lid / a.row_tiles;
+  }
 
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   int qrow;
@@ -535,9 +583,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   } else {
     n_keys = n_valid = a.Nk;
   }
-  const int ntiles = (n_keys + BN - 1) / BN;
-  const int t_begin = split * a.tiles_per_split;
-  const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
+  const int nt = GATHER ? t_end - t_begin : (n_keys + BN - 1) / BN;
 
   const char* Kg = (const char*)a.K + rm_head(a.rmk, bh) * 2;
   const char* Vg = (const char*)a.V + rm_head(a.rmv, bh) * 2;
@@ -831,36 +877,34 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
     }
   };
   const float l_tot = l_run + wave_shfl_xor(l_run, 32);
-  if (a.nsplit == 1) {
+  if (part < 0) {
     if (qrow >= 0) {
       store_row((bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn, 1.0f / l_tot);
       if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref * sc + __builtin_log2f(l_tot);
     }
   } else {
-    const long long prow = ((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split;
+    // part `part` of the row tile: [Rs][sk_P][BM][D] partial outputs
+    const long long prow = ((long long)Rs * a.sk_P + part) * BM + w * 32 + l32;
     store_row(a.part_o + prow * D, l_tot > 0.f ? 1.0f / l_tot : 0.f);
     if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref, l_tot};
   }
 }
 
-// Persistent form of the full-route ping-pong kernel: one workgroup per CU
-// takes the work items (row tile, key split) g, g + G, g + 2G, ... (G
-// workgroups; item ids through xcd_remap as the one-item-per-workgroup
-// launch, so an item runs on the XCD it would run on there) and runs the
-// key tiles of all its items as one sequence of steps s: the rings, the
+// Persistent form of the full-route ping-pong kernel: workgroup g takes
+// stream-K range g (units u = Ri * T + t, Ri = bh * row_tiles + rt, T key
+// tiles per row tile), i.e. the row tiles it meets, each over its share of
+// key tiles, and runs them as one sequence of steps s: the rings, the
 // row-table ring and the wait counts are those of isa_flash_pp_kernel with
 // the step index s in place of the tile index, and at an item boundary the
 // pipeline does not drain.  Step s0, the first of item r + 1: X_{s0} ends
 // the P.V sum of item r and starts S of item r + 1 (its queries were loaded
-// in Y_{s0-1}); Y_{s0} writes item r's output (the same normalisation and
-// stores as the epilogue of isa_flash_pp_kernel, through buffer stores, so
-// that every wave issues the same nine stores and the load waits can count
-// them), resets the running state and takes the softmax of item r + 1's
-// first tile.  Used when every item has at least kPpsMinTiles key tiles and
-// a workgroup has at most kPpsMaxItems items; the output is that of
-// isa_flash_pp_kernel bit for bit.
+// in Y_{s0-1}); Y_{s0} writes item r's output or its partial (the same
+// normalisation and stores as the epilogue of isa_flash_pp_kernel, through
+// buffer stores, so that every wave issues the same nine stores and the load
+// waits can count them), resets the running state and takes the softmax of
+// item r + 1's first tile.  Used when a range meets at most kPpsMaxItems row
+// tiles; the output is that of isa_flash_pp_kernel bit for bit.
 constexpr int kPpsMaxItems = 8;
-constexpr int kPpsMinTiles = 8;
 __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   typedef bf16x8 Op;
   constexpr int D = 128, BN = 64, BM = 256, NST = 4;
@@ -880,22 +924,45 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const int G = gridDim.x;
-  const int n_items = a.n_wg;
-  const int nr = n_items > (int)blockIdx.x ? (n_items - 1 - (int)blockIdx.x) / G + 1 : 0;
   const int n_keys = a.Ns + (int)a.ctx_tok;
-  const int ntiles = (n_keys + BN - 1) / BN;
+  // This workgroup's items: whole row tiles g, g + G, ... (sk_K of them;
+  // the workgroups of an XCD take consecutive row tiles), then the row tiles
+  // that its stream-K range meets (ranges of consecutive g on one XCD):
+  // units [u0, u1), i.e. key tiles t00 .. of row tile sk_R0 + R0 through row
+  // tile sk_R0 + R0 + nsk - 1.
+  // (64-bit quotients come out in vector registers: made scalar again)
+  const int G = gridDim.x;
+  const int g = xcd_remap((int)blockIdx.x, G);
+  const int T = a.sk_T;
+  long long u0 = 0, u1 = 0;
+  if (g < a.sk_G) {
+    u0 = sk_bound(a, g);
+    u1 = sk_bound(a, g + 1);
+  }
+  const int R0 = __builtin_amdgcn_readfirstlane((int)(u0 / T));
+  const int nsk = __builtin_amdgcn_readfirstlane(u1 > u0 ? (int)((u1 - 1) / T) - R0 + 1 : 0);
+  const int t00 = (int)(u0 - (long long)R0 * T);   // first key tile of row tile R0 in the range
+  const int t1l = __builtin_amdgcn_readfirstlane((int)(u1 - (long long)(R0 + nsk - 1) * T));   // end tile of the last
+  // the part of row tile R0 that this range takes when the row tile starts
+  // in an earlier range (later items start in this one: part 0 or whole)
+  const int part0 = __builtin_amdgcn_readfirstlane(t00 > 0 ? g - sk_range_of(a, (long long)R0 * T) : 0);
+  const int kdp = a.sk_K;
+  const int nr = kdp + nsk;
 
-  struct Item { int bh, rt, split, t_begin, nt; };
+  struct Item { int bh, rt, part, t_begin, nt; };   // part < 0: the whole row tile
   auto item_of = [&](int r) -> Item {
-    // (item order of isa_flash_pp_kernel: row tile fastest, then split, then head)
-    const int lid = xcd_remap((int)blockIdx.x + r * G, n_items);
-    const int rt = lid % a.row_tiles;
-    const int rest = lid / a.row_tiles;
-    const int split = rest % a.nsplit;
-    const int bh = rest / a.nsplit;
-    const int tb = split * a.tiles_per_split;
-    return Item{bh, rt, split, tb, min(a.tiles_per_split, ntiles - tb)};
+    int Ri, t0 = 0, t1 = T, part = -1;
+    if (r < kdp) {
+      Ri = r * G + g;
+    } else {
+      const int q = r - kdp;
+      Ri = a.sk_R0 + R0 + q;
+      if (q == 0) t0 = t00;
+      if (q == nsk - 1) t1 = t1l;
+      if (t0 > 0 || t1 < T) part = q == 0 ? part0 : 0;
+    }
+    const int bh = Ri / a.row_tiles;
+    return Item{bh, Ri - bh * a.row_tiles, part, t0, t1 - t0};
   };
   // per item: each lane's query row and the head's valid key count
   for (int r = 0; r < nr; ++r) {
@@ -1112,7 +1179,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   auto finish = [&](int r, const Item& it) {
     const float l_tot = l_run + wave_shfl_xor(l_run, 32);
     const int qrow = sq[w][r][lane];
-    if (a.nsplit == 1) {
+    if (it.part < 0) {
       const auto rO = __builtin_amdgcn_make_buffer_rsrc((char*)a.O + uniform64(shead[1][r]), (short)0, a.o_span,
                                                         0x00020000);
       store_rows(rO, qrow >= 0 ? (unsigned)qrow * sstep[1] : kOut, 1.0f / l_tot);
@@ -1121,9 +1188,10 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref * sc + __builtin_log2f(l_tot)), rL,
                                            (qrow >= 0 && h == 0) ? (unsigned)qrow * 4 : kOut, 0, 0);
     } else {
-      const long long prow0 = (long long)it.bh * a.row_tiles * BM * a.nsplit;   // first partial row of the head
-      const int nrow = a.row_tiles * BM * a.nsplit;
-      const int prow = (it.rt * BM + w * 32 + l32) * a.nsplit + it.split;
+      // part it.part of the row tile: [Ri - sk_R0][sk_P][BM][D] partial outputs
+      const long long prow0 = ((long long)it.bh * a.row_tiles + it.rt - a.sk_R0) * a.sk_P * BM;   // its first partial row
+      const int nrow = a.sk_P * BM;
+      const int prow = it.part * BM + w * 32 + l32;
       const auto rP = __builtin_amdgcn_make_buffer_rsrc(a.part_o + prow0 * D, (short)0, nrow * RB, 0x00020000);
       store_rows(rP, (unsigned)prow * RB, l_tot > 0.f ? 1.0f / l_tot : 0.f);
       const auto rM = __builtin_amdgcn_make_buffer_rsrc(a.part_ml + prow0 * 2, (short)0, nrow * 8, 0x00020000);
@@ -1143,7 +1211,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (nr == 0) return;   // (never: the grid has at most n_items workgroups)
+  if (nr == 0) return;   // (never: every range holds at least one unit)
   int total = 0;
   for (int r = 0; r < nr; ++r) total += item_of(r).nt;
   const Item it0 = item_of(0);
@@ -1179,15 +1247,16 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   PTile P = {};
   Item fin = it0;   // the item whose output the next boundary writes
   int fin_r = 0;
-  // One step.  FIRST: the first tile of an item (after item 0, the previous
-  // item's output is written); LAST: its last tile (the next item's queries
-  // are loaded for the step after it); INNER: a tile whose K, V and table
+  // One step.  first: the first tile of an item (after item 0, the previous
+  // item's output is written); last: its last tile (the next item's queries
+  // are loaded for the step after it), both for a one-tile item (uniform
+  // flags, not template arguments: a third copy of the step spills); INNER:
+  // a tile whose K, V and table
   // positions (s + 3, s + 2, s + 6) lie in the same item, so that they are
   // offsets from the compute cursor and the other cursors are not moved
   // (they are set again after the inner run).  nv: valid keys of the item's
   // head, kept in a register for the item.
-  auto step = [&](int s, auto first_c, auto last_c, auto inner_c, int nv, long long ho) {
-    constexpr bool FIRST = decltype(first_c)::value, LAST = decltype(last_c)::value;
+  auto step = [&](int s, bool first, bool last, auto inner_c, int nv, long long ho) {
     constexpr bool INNER = decltype(inner_c)::value;
     const int Z = s & 3;
     __builtin_amdgcn_s_setprio(3);
@@ -1196,7 +1265,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
     __builtin_amdgcn_s_setprio(0);
     phase_barrier();
     // Y_s
-    const bool boundary = FIRST && s > 0;
+    const bool boundary = !INNER && first && s > 0;
     if (boundary) {
       finish(fin_r, fin);
       fin = cc.it;
@@ -1216,7 +1285,7 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       if (s < total) P = softmax((cc.it.t_begin + cc.k) * BN, nv, S);
       rv = rk;
       rk = rn;
-      const bool next_item = LAST && cc.r + 1 < nr;
+      const bool next_item = last && cc.r + 1 < nr;
       if (next_item) load_q(cc.r + 1);
       advance(cc);
       advance(ck);
@@ -1224,9 +1293,10 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       advance(ct);
       // the loads of Y_{s-1} have landed before the barrier that closes Y_s
       // (this step's output stores or query loads were issued too)
-      if (boundary) __builtin_amdgcn_s_waitcnt(0x0f7e);         // vmcnt(14)
-      else if (next_item) __builtin_amdgcn_s_waitcnt(0x0f7d);   // vmcnt(13)
-      else __builtin_amdgcn_s_waitcnt(0x0f75);                  // vmcnt(5)
+      if (boundary && next_item) __builtin_amdgcn_s_waitcnt(0x4f76);   // vmcnt(22): a one-tile item
+      else if (boundary) __builtin_amdgcn_s_waitcnt(0x0f7e);         // vmcnt(14)
+      else if (next_item) __builtin_amdgcn_s_waitcnt(0x0f7d);        // vmcnt(13)
+      else __builtin_amdgcn_s_waitcnt(0x0f75);                       // vmcnt(5)
     }
     phase_barrier();
   };
@@ -1234,22 +1304,25 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   using F_ = std::false_type;
   int s = 0;
   for (int r = 0; r < nr; ++r) {
-    const int ntr = cc.it.nt;   // >= kPpsMinTiles
+    const int ntr = cc.it.nt;   // >= 1
     const int nv = snv[r];
     const long long ho = head_off(r);   // the item's K and V rows (inner steps)
-    step(s++, T_{}, F_{}, F_{}, nv, ho);
+    step(s++, true, ntr == 1, F_{}, nv, ho);   // (a one-tile item: first and last)
+    if (ntr == 1) continue;
     // K, V and table positions stay in the item while k + 6 < ntr
-    for (int k = 1; k + 6 < ntr; ++k) step(s++, F_{}, F_{}, T_{}, nv, ho);
-    ck = cc; advance(ck); advance(ck); advance(ck);
-    cv = cc; advance(cv); advance(cv);
-    ct = cc;
+    if (ntr > 7) {
+      for (int k = 1; k + 6 < ntr; ++k) step(s++, false, false, T_{}, nv, ho);
+      ck = cc; advance(ck); advance(ck); advance(ck);
+      cv = cc; advance(cv); advance(cv);
+      ct = cc;
 #pragma unroll 1
-    for (int j = 0; j < 6; ++j) advance(ct);
+      for (int j = 0; j < 6; ++j) advance(ct);
+    }
 #pragma unroll 1
-    for (int k = ntr - 6; k < ntr - 1; ++k) step(s++, F_{}, F_{}, F_{}, nv, ho);
-    step(s++, F_{}, T_{}, F_{}, nv, ho);
+    for (int k = max(1, ntr - 6); k < ntr - 1; ++k) step(s++, false, false, F_{}, nv, ho);
+    step(s++, false, true, F_{}, nv, ho);
   }
-  step(s, F_{}, F_{}, F_{}, 0, 0);   // s == total: the last P.V (no softmax)
+  step(s, false, false, F_{}, 0, 0);   // s == total: the last P.V (no softmax)
   finish(fin_r, fin);
   __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
   if (grp == 0) phase_barrier();   // balances group 1's extra barrier
@@ -1621,34 +1694,51 @@ template <int D>
 __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   constexpr int TPR = D / 8;           // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;       // rows per workgroup
-  const long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int e = (threadIdx.x % TPR) * 8;
   const long long rows_head = (long long)a.row_tiles * kFlashRows;
+  // the row's np partials: rows prow + s * pstep
+  int np;
+  long long prow, pstep;
+  if (a.sk_G > 0) {
+    // stream-K: the launch covers the rows of row tiles sk_R0 on; row tile
+    // Ri = sk_R0 + Rs met ranges first .. last; one range wrote it whole
+    const long long Rs = gid / kFlashRows, ub = Rs * a.sk_T;
+    if (ub >= a.sk_U) return;
+    np = sk_range_of(a, ub + a.sk_T - 1) - sk_range_of(a, ub) + 1;
+    if (np == 1) return;
+    prow = Rs * a.sk_P * kFlashRows + (gid - Rs * kFlashRows);
+    pstep = kFlashRows;
+    gid += (long long)a.sk_R0 * kFlashRows;
+  } else {
+    np = a.nsplit;
+    prow = gid * a.nsplit;
+    pstep = 1;
+  }
   const long long bh = gid / rows_head;
   const long long vrow = gid - bh * rows_head;
   if (bh >= a.n_wg) return;  // n_wg carries BH here
   const int qrow = route_row(a.q_list + bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
   if (qrow < 0) return;
-  const long long prow = gid * a.nsplit;
   constexpr int MAXS = kMaxSplits;
   float2 ml[MAXS];
   u32x4 po[MAXS];
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
-    if (s < a.nsplit) {
-      ml[s] = *(const float2*)(a.part_ml + (prow + s) * 2);
-      po[s] = *(const u32x4*)(a.part_o + (prow + s) * D + e);
+    if (s < np) {
+      ml[s] = *(const float2*)(a.part_ml + (prow + s * pstep) * 2);
+      po[s] = *(const u32x4*)(a.part_o + (prow + s * pstep) * D + e);
     }
   }
   float mstar = -INFINITY;
 #pragma unroll
   for (int s = 0; s < MAXS; ++s)
-    if (s < a.nsplit) mstar = fmaxf(mstar, ml[s].x);
+    if (s < np) mstar = fmaxf(mstar, ml[s].x);
   // split s weighs in with its sum rescaled to the common max
   float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
-    if (s >= a.nsplit || ml[s].x == -INFINITY) continue;
+    if (s >= np || ml[s].x == -INFINITY) continue;
     const float wgt = __builtin_amdgcn_exp2f((ml[s].x - mstar) * a.scale_log2) * ml[s].y;
     l += wgt;
 #pragma unroll
@@ -1708,17 +1798,30 @@ static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, lo
   a.n_wg = (int)nwg;
   if constexpr (D == 128 && KM != FK_POOLED && WO && !WP && kFlashWaves == 8) {
     if constexpr (KM == FK_GATHER && RM == FR_TABLE) {
-      // persistent form when every work item has enough key tiles
-      const int ntiles = (int)((keys + 63) / 64);
-      const int last = ntiles - (a.nsplit - 1) * a.tiles_per_split;
-      const long long grid = nwg < kCUs ? nwg : kCUs;
-      const long long prows = (long long)a.row_tiles * kFlashRows * a.nsplit;
-      if (kUsePps && a.tiles_per_split >= kPpsMinTiles && last >= kPpsMinTiles &&
-          (nwg + grid - 1) / grid <= kPpsMaxItems && prows * D * 2 < (1LL << 31) && a.rmk.sb == a.rmv.sb &&
-          a.rmk.sh == a.rmv.sh && a.rmk.sn == a.rmv.sn) {
-        hipLaunchKernelGGL(isa_flash_pps_kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
+      // whole row tiles, then stream-K ranges, as the layout set them
+      // (a.sk_K rounds of grid workgroups, a.sk_G ranges)
+      const long long R = (long long)a.row_tiles * BH, grid = a.sk_R0;
+      a.sk_R0 = (int)(grid * a.sk_K);
+      a.sk_T = ntiles;
+      a.sk_U = (R - a.sk_R0) * ntiles;
+      if (grid <= 0 || a.sk_K < 0 || a.sk_R0 > R || (a.sk_U > 0) != (a.sk_G > 0) || a.sk_U < a.sk_G ||
+          a.sk_P < 1 || a.sk_P > kMaxSplits)
+        return hipErrorInvalidValue;
+      // persistent form, one workgroup per round slot and range, when a
+      // workgroup meets at most kPpsMaxItems row tiles and K and V share one
+      // row map
+      long long items = a.sk_K;
+      if (a.sk_G > 0) items += ((a.sk_U + a.sk_G - 1) / a.sk_G - 1 + ntiles - 1) / ntiles + 1;
+      if (kUsePps && items <= kPpsMaxItems && a.rmk.sb == a.rmv.sb && a.rmk.sh == a.rmv.sh &&
+          a.rmk.sn == a.rmv.sn) {
+        hipLaunchKernelGGL(isa_flash_pps_kernel, dim3((unsigned)(a.sk_K > 0 ? grid : a.sk_G)), dim3(512), 0, s, a);
         return hipGetLastError();
       }
+      // else one workgroup per item: whole row tile Ri < sk_R0, or part p of
+      // row tile sk_R0 + Rs as item sk_R0 + Rs * sk_P + p
+      a.n_wg = (int)(a.sk_R0 + (R - a.sk_R0) * a.sk_P);
+      hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM>), dim3((unsigned)a.n_wg), dim3(512), 0, s, a);
+      return hipGetLastError();
     }
     hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM>), dim3((unsigned)nwg), dim3(512), 0, s, a);
     return hipGetLastError();
@@ -1744,18 +1847,33 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
       a.q_list = (const int*)(B.ws + L.off_fullq);
       a.q_k = L.kq;
       a.nsplit = L.full_splits;
+      a.sk_R0 = L.sk_grid;   // (the launch sets sk_R0 = sk_grid * sk_K)
+      a.sk_K = L.sk_rounds;
+      a.sk_G = L.sk_G;
+      a.sk_P = L.sk_P;
       return flash_launch<D, FK_GATHER, FR_TABLE, true, false>(a, L.full_rows, (long long)L.Ns + L.ctx_tok,
                                                                 L.BH, s);
     case FlashWhat::kFullMerge: {
-      if (L.full_splits <= 1 || L.full_rows == 0) return hipSuccess;
+      // the stream-K split of the d = 128 ping-pong kernels, else full_splits equal parts
+      const bool sk = D == 128 && kFlashWaves == 8 && L.sk_grid > 0;
+      if ((sk ? L.sk_P : L.full_splits) <= 1 || L.full_rows == 0) return hipSuccess;
       a.q_list = (const int*)(B.ws + L.off_fullq);
       a.q_k = L.kq;
       a.nsplit = L.full_splits;
       a.n_rows = L.full_rows;
       a.row_tiles = (int)((L.full_rows + kFlashRows - 1) / kFlashRows);
       a.n_wg = (int)L.BH;
+      long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
+      if (sk) {
+        // the rows of the row tiles past the whole rounds
+        a.sk_G = L.sk_G;
+        a.sk_P = L.sk_P;
+        a.sk_T = (int)((L.Ns + L.ctx_tok + 63) / 64);
+        a.sk_R0 = L.sk_grid * L.sk_rounds;
+        a.sk_U = ((long long)a.row_tiles * L.BH - a.sk_R0) * a.sk_T;
+        rows -= (long long)a.sk_R0 * kFlashRows;
+      }
       constexpr int RPB = 256 / (D / 8);
-      const long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
       hipLaunchKernelGGL((isa_flash_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
       return hipGetLastError();
     }

@@ -164,6 +164,31 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
     const int ntiles = (int)((D.Ns + L->ctx_tok + 63) / 64);
     L->full_splits = L->es == 2 ? choose_splits(bh * row_tiles, ntiles) : 1;
     L->n_keytab = ntiles * kTileKeys;
+    L->sk_grid = L->sk_rounds = L->sk_G = L->sk_P = 0;
+    if (L->es == 2 && D.d == 128 && row_tiles > 0) {
+      // whole row tiles in at most 5 rounds of a multiple of the compute
+      // unit count, the rest in ranges of equal length: at least
+      // (T - 1) / (kMaxSplits - 1) units, so that a row tile of T units
+      // meets at most kMaxSplits ranges, and min(8, T) (fixed costs); at
+      // most one range per workgroup.  A range is then shorter than 2 T
+      // units (or than T), so a workgroup meets at most 5 + 3 row tiles.
+      const int64_t R = bh * row_tiles, T = ntiles;
+      const int64_t G = kCUs * ((R + kCUs * 5 - 1) / (kCUs * 5));
+      const int64_t rounds = R / G, rest = R - rounds * G, U = rest * T;
+      L->sk_grid = (int)G;
+      L->sk_rounds = (int)rounds;
+      L->sk_P = 1;
+      if (rest > 0) {
+        int64_t wmin = T > 1 ? (T - 1 + kMaxSplits - 2) / (kMaxSplits - 1) : 1;
+        if (wmin < 8) wmin = T < 8 ? T : 8;
+        int64_t Gs = U / wmin < G ? U / wmin : G;
+        if (Gs < 1) Gs = 1;
+        const int64_t W = U / Gs;   // the shortest range
+        L->sk_G = (int)Gs;
+        L->sk_P = (int)((T - 1 + W - 1) / W + 1);
+        if (L->sk_P > kMaxSplits) L->sk_P = kMaxSplits;   // (not reached: W >= wmin or Gs = 1)
+      }
+    }
   }
 
   const size_t d = (size_t)D.d;
@@ -190,7 +215,14 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
   take(&L->off_fullq, bh * L->kq * 4);
   take(&L->off_taylq, bh * (L->nb_s - L->kq) * 4);
   {
-    const int64_t prow = L->full_splits > 1 ? bh * ((L->full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L->full_splits : 0;
+    // split partials: the FP8 variant and d = 64 split every row tile into
+    // full_splits parts, the d = 128 full route the row tiles past the whole
+    // rounds into up to sk_P
+    const int64_t row_tiles = (L->full_rows + kFlashRows - 1) / kFlashRows;
+    int64_t prow = L->full_splits > 1 ? bh * row_tiles * kFlashRows * L->full_splits : 0;
+    const int64_t prow_sk =
+        L->sk_P > 1 ? (bh * row_tiles - (int64_t)L->sk_rounds * L->sk_grid) * kFlashRows * L->sk_P : 0;
+    if (prow_sk > prow) prow = prow_sk;
     take(&L->off_part_o, prow * d * 2);
     take(&L->off_part_ml, prow * 2 * 4);
   }

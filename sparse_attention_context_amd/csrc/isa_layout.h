@@ -61,7 +61,16 @@ struct Layout {
   int64_t ctx_tok;     // kc*b: context key tokens of the full route (with tail padding)
   int64_t full_rows;   // kq*b virtual full-route query rows
   int64_t taylor_rows; // (nb_s-kq)*b virtual Taylor-route query rows
-  int full_splits;     // key-range splits of the full-route attention (bf16)
+  int full_splits;     // key-range splits of the full-route attention: the FP8 variant, d = 64, the backward's dQ
+  // bf16 full route at d = 128, on sk_grid workgroups (0: off): row tiles
+  // Ri = bh * row tiles + rt.  Workgroup g first takes whole row tiles
+  // g, g + sk_grid, ... (sk_rounds of them, row tiles below sk_rounds *
+  // sk_grid), then range g of the (row tile, key tile) units of the rest,
+  // u = (Ri - sk_rounds * sk_grid) * key tiles + t, cut into sk_G equal
+  // ranges (range g: units [g U / sk_G, (g + 1) U / sk_G)).  A row tile
+  // inside one range needs no merge; one meets at most sk_P ranges (its
+  // parts).
+  int sk_grid, sk_rounds, sk_G, sk_P;
   int n_keytab;        // full-route key rows per head, rounded up to kTileKeys
   // byte offsets into the workspace
   size_t off_qbar, off_kbar, off_vbar, off_salp, off_sal, off_kept;

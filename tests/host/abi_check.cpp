@@ -42,6 +42,55 @@ static int count_rule(double f, int n) {
   return (int)std::min<double>(n, std::max<double>(0, c));
 }
 
+// The work split of the d = 128 bf16 full route: R row tiles of T key tiles;
+// workgroup g of sk_grid takes row tiles g, g + sk_grid, ... whole
+// (sk_rounds of them), then range g of the remaining row tiles' units
+// u = (Ri - sk_rounds sk_grid) T + t, range g covering [g U / G, (g + 1) U / G)
+// for G = sk_G.  By enumeration: every range is non-empty and every
+// workgroup meets at most 8 row tiles (the persistent kernel's limit), every
+// row tile is covered once (whole or by consecutive parts), a row tile meets
+// at most sk_P ranges, the closed form of the range holding a unit agrees
+// with a search, and the partial buffers hold the split row tiles' sk_P rows.
+static void check_stream_k(const isa::Layout& L) {
+  const int64_t R = (L.full_rows + isa::kFlashRows - 1) / isa::kFlashRows * L.BH;
+  const bool on = L.es == 2 && L.d == 128 && R > 0;
+  CHECK(on ? L.sk_grid >= 1 && L.sk_rounds >= 0 && L.sk_P >= 1 && L.sk_P <= isa::kMaxSplits
+           : L.sk_grid == 0 && L.sk_G == 0 && L.sk_P == 0);
+  if (!on) return;
+  const int64_t T = ((int64_t)L.Ns + L.ctx_tok + 63) / 64, R0 = (int64_t)L.sk_rounds * L.sk_grid;
+  const int64_t U = (R - R0) * T, G = L.sk_G;
+  CHECK(R0 <= R && L.sk_rounds <= 5 && (U > 0) == (G > 0) && G <= L.sk_grid);
+  if (L.sk_grid > 100000 || R > 4000000) return;
+  auto bound = [&](int64_t g) { return g * U / G; };
+  std::vector<int> cover(R, 0), parts(R, 0);
+  int max_parts = 0;
+  for (int64_t g = 0; g < L.sk_grid; ++g) {
+    int items = L.sk_rounds;
+    for (int r = 0; r < L.sk_rounds; ++r) cover[r * L.sk_grid + g] += (int)T;
+    if (g < G) {
+      const int64_t lo = bound(g), hi = bound(g + 1);
+      CHECK(hi > lo);
+      if (hi <= lo) return;
+      items += (int)((hi - 1) / T - lo / T + 1);
+      for (int64_t u = lo; u < hi; ++u) ++cover[R0 + u / T];
+      for (int64_t r = lo / T; r <= (hi - 1) / T; ++r) max_parts = std::max(max_parts, ++parts[R0 + r]);
+    }
+    CHECK(items <= 8);
+  }
+  for (int64_t r = 0; r < R; ++r) CHECK(cover[r] == T);
+  CHECK(max_parts <= L.sk_P);
+  // range_of(u) = ((u + 1) G + U - 1) / U - 1: the largest g with bound(g) <= u
+  for (int64_t g = 0; g < G; g += 1 + G / 64)
+    for (int64_t u : {bound(g), bound(g + 1) - 1}) {
+      const int64_t rg = ((u + 1) * G + U - 1) / U - 1;
+      CHECK(bound(rg) <= u && bound(rg + 1) > u);
+    }
+  if (L.sk_P > 1) {
+    CHECK(L.off_part_ml - L.off_part_o >= (size_t)((R - R0) * L.sk_P * isa::kFlashRows * L.d * 2));
+    CHECK(L.off_lse - L.off_part_ml >= (size_t)((R - R0) * L.sk_P * isa::kFlashRows * 8));
+  }
+}
+
 // slices of the forward layout in the order they are carved
 static void check_layout(const isa::Layout& L, const isa_desc& D) {
   const size_t offs[] = {L.off_qbar, L.off_kbar, L.off_vbar, L.off_salp, L.off_sal, L.off_kept, L.off_pkhi,
@@ -68,6 +117,7 @@ static void check_layout(const isa::Layout& L, const isa_desc& D) {
   CHECK(L.mk_pad % isa::kTileKeys == 0 && L.mk_pad >= L.mk);
   CHECK(L.full_splits >= 1 && L.full_splits <= isa::kMaxSplits);
   CHECK((int64_t)L.n_keytab >= (int64_t)L.Ns + L.ctx_tok && L.n_keytab % isa::kTileKeys == 0);
+  check_stream_k(L);
   isa::BwdLayout W;
   if (isa::make_bwd_layout(L, &W) == ISA_OK) {
     CHECK(W.total % isa::kWsAlign == 0 && W.off_rdel < W.total);
@@ -239,6 +289,22 @@ int main() {
     std::mt19937 rng(11);
     for (int i = 0; i < 512; ++i) check_H(1025 + (int)(rng() % 64510));
     check_H(65535);
+  }
+
+  // ---- stream-K ranges at large sizes: the video-DiT layer, and layers with
+  // enough row tiles that the range count passes the compute-unit count
+  {
+    const int shapes[][5] = {{1, 24, 17550, 17550, 64}, {1, 64, 200000, 50000, 64}, {2, 40, 60000, 0, 128},
+                             {1, 1, 4194000, 4194300, 64}, {3, 7, 5000, 123, 16}};
+    for (const auto& sh : shapes)
+      for (double gamma : {0.2, 1.0}) {
+        isa_desc D = base_desc();
+        D.B = sh[0]; D.H = sh[1]; D.Ns = sh[2]; D.Nc = sh[3]; D.b = sh[4]; D.d = 128;
+        D.rho = 0.25; D.gamma = gamma;
+        isa::Layout L;
+        CHECK(isa::make_layout(&D, &L) == ISA_OK);
+        check_layout(L, D);
+      }
   }
 
   // ---- random descriptors: no sanitizer finding, errors only as documented

@@ -184,10 +184,12 @@ SMALL = [
     (1, 2, 128, 500, 0, 32, 0.5, 0.3, "bf16"),        # no context at d = 128: the key-row table is the source rows
     (1, 2, 128, 700, 630, 50, 1.0, 0.5, "bf16"),      # short last context block kept; tiles straddle Ns and the gap
     # more row tiles than compute units: the persistent full-route kernel,
-    # 3 or 4 work items per workgroup, three key splits (the last one shorter)
+    # one whole row tile per workgroup, then ranges of 10 or 11 key tiles
+    # over the last 64 row tiles (41 key tiles each: up to 5 parts)
     (1, 40, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),
-    (2, 32, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),   # the same with one split: 2 items per workgroup, lse written
-    (1, 8, 128, 1500, 1024, 32, 1.0, 1.0, "bf16"),    # persistent kernel with the fewest key tiles it takes (8 per split)
+    (2, 32, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),   # 512 row tiles: two whole each, no range, lse written
+    (1, 8, 128, 1500, 1024, 32, 1.0, 1.0, "bf16"),    # 48 row tiles of 40 key tiles in 240 ranges of 8: five parts each
+    (1, 3, 128, 1595, 500, 64, 1.0, 1.0, "bf16"),     # 21 row tiles of 33 key tiles in 86 ranges: parts of 1 to 9 tiles
     (1, 2, 64, 400, 300, 1, 0.003, 0.997, "bf16"),    # k = 1 of 300 context blocks, k = n - 1 of 400 query blocks
     (1, 2, 64, 400, 300, 1, 0.995, 0.0025, "bf16"),   # k = n - 1 of 300, k = 1 of 400
 ]
@@ -389,11 +391,13 @@ def test_dense_forward_video_dit_sampled():
 
 
 @pytest.mark.timeout(600)
-def test_persistent_full_route_eight_items_per_workgroup(parity_record):
-    """2048 work items on 256 workgroups: the most the persistent full-route
-    kernel takes (its per-item query-row table holds 8); every output row of
-    every head against the oracle."""
-    B, H, d, Ns, Nc, b, rho, gamma = 2, 128, 128, 2048, 0, 64, 0.5, 1.0
+def test_persistent_full_route_many_items_per_workgroup(parity_record):
+    """2240 row tiles of 32 key tiles on 512 workgroups: four whole row tiles
+    each (the most rounds the split takes below 5), then a range of 12 key
+    tiles over the last 192 row tiles, so six items per workgroup and row
+    tiles in up to 4 parts; every output row of every head against the
+    oracle."""
+    B, H, d, Ns, Nc, b, rho, gamma = 2, 140, 128, 2048, 0, 64, 0.5, 1.0
     _report("case %s" % ((B, H, d, Ns, Nc, b, rho, gamma),))
     Q, K, V = make_inputs(B, H, d, Ns, Nc, seed=77, dtype="bf16")
     Qd, Kd, Vd = (device_tensor(t, "bf16") for t in (Q, K, V))
@@ -412,7 +416,8 @@ def test_persistent_full_route_eight_items_per_workgroup(parity_record):
     outs = run_parallel(job, [(x, h) for x in range(B) for h in range(H)])
     maxabs = max(o[0] for o in outs)
     rel = (sum(o[1] for o in outs) / sum(o[2] for o in outs)) ** 0.5
-    parity_record({"case": "persistent full route, 8 items per workgroup", "maxabs": maxabs, "rel_l2": rel})
+    parity_record({"case": "persistent full route, 4 whole row tiles and a range per workgroup", "maxabs": maxabs,
+                   "rel_l2": rel})
     assert maxabs <= BF16_MAXABS and rel <= BF16_RELL2, (maxabs, rel)
 
 
