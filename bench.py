@@ -443,7 +443,7 @@ def main():
             traffic = counted_traffic("isa_flash_pps_kernel full route") or counted_traffic("isa_flash_pp_kernel<1,1> full route")
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                    "kernel": "full-route flash kernel (isa_flash_pps_kernel, persistent, where every work item has >= 8 key tiles, else isa_flash_pp_kernel<1,1>; gathered K/V; split-K merge timed separately)", "flops_per_launch": flops,
+                    "kernel": "full-route flash kernel (isa_flash_pps_kernel, persistent: whole row tiles, then stream-K ranges; isa_flash_pp_kernel<1,1> when K and V have different row maps; gathered K/V; merge of the split row tiles timed separately)", "flops_per_launch": flops,
                     "avg_launch_ms": round(full_ms, 4)}
     dense_flops = 4 * w.d * w.Ns * (w.Ns + w.Nc) * w.B * w.H
 
