@@ -117,7 +117,14 @@ struct FlashArgs {
 // [sk_bound(g), sk_bound(g + 1)).  A row tile inside one range is finished
 // by that range's workgroup; one that meets several ranges is cut into
 // parts there, part p taken by range sk_range_of(first unit) + p, and
-// merged.
+// merged.  A cut row tile's key tiles are taken in rotated order, from the
+// first range boundary inside it: unit t of the row tile is key tile
+// (t - delta) mod T, delta the boundary's offset (0 when a range starts at
+// the row tile).  The range that starts there then reads key tile 0 first,
+// as the whole row tiles of its neighbours on the XCD do, so that ranges
+// with the same offset read the same K/V tiles at about the same time.
+// Every part still covers consecutive key tiles, and the last (padding)
+// tiles come at the end of a part.
 __device__ __forceinline__ long long sk_bound(const FlashArgs& a, long long g) { return g * a.sk_U / a.sk_G; }
 // the range holding unit u: the largest g with sk_bound(g) <= u
 __device__ __forceinline__ int sk_range_of(const FlashArgs& a, long long u) {
@@ -552,8 +559,12 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
       const int gf = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0));
       const int gl = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0 + a.sk_T - 1));
       if (p > gl - gf) return;
-      t_begin = __builtin_amdgcn_readfirstlane((int)max(sk_bound(a, gf + p) - u0, 0LL));
-      t_end = __builtin_amdgcn_readfirstlane((int)min(sk_bound(a, gf + p + 1) - u0, (long long)a.sk_T));
+      const int tb = (int)max(sk_bound(a, gf + p) - u0, 0LL);
+      const int te = (int)min(sk_bound(a, gf + p + 1) - u0, (long long)a.sk_T);
+      // rotated key order of a cut row tile (delta: its first inner range boundary)
+      const int delta = (sk_bound(a, gf) == u0 || gl == gf) ? 0 : (int)(sk_bound(a, gf + 1) - u0);
+      t_begin = __builtin_amdgcn_readfirstlane(tb >= delta ? tb - delta : tb - delta + a.sk_T);
+      t_end = __builtin_amdgcn_readfirstlane(t_begin + te - tb);
       part = gl > gf ? p : -1;
     }
     bh = Ri / a.row_tiles;
@@ -946,12 +957,22 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   // the part of row tile R0 that this range takes when the row tile starts
   // in an earlier range (later items start in this one: part 0 or whole)
   const int part0 = __builtin_amdgcn_readfirstlane(t00 > 0 ? g - sk_range_of(a, (long long)R0 * T) : 0);
+  // rotated first key tile of that part (key tiles of a cut row tile run from
+  // its first inner range boundary, delta units in: t -> t - delta mod T)
+  int tb0 = t00;
+  if (t00 > 0) {
+    const long long base = (long long)R0 * T;
+    if (sk_bound(a, g - part0) != base) tb0 = t00 - (int)(sk_bound(a, g - part0 + 1) - base);
+  }
+  tb0 = __builtin_amdgcn_readfirstlane(tb0);
   const int kdp = a.sk_K;
   const int nr = kdp + nsk;
 
   struct Item { int bh, rt, part, t_begin, nt; };   // part < 0: the whole row tile
+  // (t_begin: the item's first key tile in rotated order; its nt key tiles
+  // follow it without wrapping)
   auto item_of = [&](int r) -> Item {
-    int Ri, t0 = 0, t1 = T, part = -1;
+    int Ri, t0 = 0, t1 = T, tb = 0, part = -1;
     if (r < kdp) {
       Ri = r * G + g;
     } else {
@@ -960,9 +981,12 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       if (q == 0) t0 = t00;
       if (q == nsk - 1) t1 = t1l;
       if (t0 > 0 || t1 < T) part = q == 0 ? part0 : 0;
+      // a later item starts at its row tile's first unit, inside this range:
+      // the boundary is this range's end, t1 units in
+      tb = q == 0 ? tb0 : (t1 < T ? T - t1 : 0);
     }
     const int bh = Ri / a.row_tiles;
-    return Item{bh, Ri - bh * a.row_tiles, part, t0, t1 - t0};
+    return Item{bh, Ri - bh * a.row_tiles, part, tb, t1 - t0};
   };
   // per item: each lane's query row and the head's valid key count
   for (int r = 0; r < nr; ++r) {

@@ -50,7 +50,9 @@ static int count_rule(double f, int n) {
 // workgroup meets at most 8 row tiles (the persistent kernel's limit), every
 // row tile is covered once (whole or by consecutive parts), a row tile meets
 // at most sk_P ranges, the closed form of the range holding a unit agrees
-// with a search, and the partial buffers hold the split row tiles' sk_P rows.
+// with a search, the rotated key order of a cut row tile gives every part
+// one run of key tiles, and the partial buffers hold the split row tiles'
+// sk_P rows.
 static void check_stream_k(const isa::Layout& L) {
   const int64_t R = (L.full_rows + isa::kFlashRows - 1) / isa::kFlashRows * L.BH;
   const bool on = L.es == 2 && L.d == 128 && R > 0;
@@ -85,6 +87,23 @@ static void check_stream_k(const isa::Layout& L) {
       const int64_t rg = ((u + 1) * G + U - 1) / U - 1;
       CHECK(bound(rg) <= u && bound(rg + 1) > u);
     }
+  // the rotated key order of a cut row tile (key tile (t - delta) mod T, delta
+  // its first inner range boundary): every part is one run of consecutive key
+  // tiles inside [0, T), and the parts cover [0, T) once
+  auto range_of = [&](int64_t u) { return ((u + 1) * G + U - 1) / U - 1; };
+  for (int64_t Rs = 0; G > 0 && Rs < R - R0; ++Rs) {
+    const int64_t u0 = Rs * T, gf = range_of(u0), gl = range_of(u0 + T - 1);
+    const int64_t delta = (bound(gf) == u0 || gl == gf) ? 0 : bound(gf + 1) - u0;
+    std::vector<int> seen(T, 0);
+    for (int64_t p = 0; p <= gl - gf; ++p) {
+      const int64_t tb = std::max<int64_t>(bound(gf + p) - u0, 0), te = std::min<int64_t>(bound(gf + p + 1) - u0, T);
+      const int64_t r = tb >= delta ? tb - delta : tb - delta + T;
+      CHECK(r >= 0 && r + (te - tb) <= T);
+      for (int64_t k = r; k < r + (te - tb) && k < T; ++k) ++seen[k];
+    }
+    for (int64_t k = 0; k < T; ++k) CHECK(seen[k] == 1);
+    if (Rs > 2000) break;
+  }
   if (L.sk_P > 1) {
     CHECK(L.off_part_ml - L.off_part_o >= (size_t)((R - R0) * L.sk_P * isa::kFlashRows * L.d * 2));
     CHECK(L.off_lse - L.off_part_ml >= (size_t)((R - R0) * L.sk_P * isa::kFlashRows * 8));
