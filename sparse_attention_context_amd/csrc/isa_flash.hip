@@ -106,6 +106,9 @@ struct FlashArgs {
   // ranges, a row tile in at most sk_P of them
   long long sk_U;
   int sk_G, sk_P, sk_T, sk_R0, sk_K;
+  // row tiles in eight blocks of sk_q or sk_q + 1 (the first sk_x blocks),
+  // one per XCD of the sk_grid persistent workgroups (see sk_round_row)
+  int sk_grid, sk_q, sk_x;
 };
 
 // Stream-K split of the full route (Osama et al., "Stream-K: Work-centric
@@ -129,6 +132,23 @@ __device__ __forceinline__ long long sk_bound(const FlashArgs& a, long long g) {
 // the range holding unit u: the largest g with sk_bound(g) <= u
 __device__ __forceinline__ int sk_range_of(const FlashArgs& a, long long u) {
   return (int)(((u + 1) * a.sk_G + a.sk_U - 1) / a.sk_U - 1);
+}
+// Which row tile a work item takes.  The row tiles are cut into eight
+// consecutive blocks, one per XCD (block x: sk_q + (x < sk_x) row tiles from
+// x sk_q + min(x, sk_x)); the sk_grid / 8 workgroups of XCD x take the first
+// sk_K * sk_grid / 8 of its block whole, in rounds, and the ranges of that
+// XCD's workgroups the rest, so that an XCD's work stays on a few heads.
+// Whole-round item: round r of logical workgroup g (XCD g / (sk_grid / 8)).
+__device__ __forceinline__ int sk_round_row(const FlashArgs& a, int r, int g) {
+  const int per = a.sk_grid >> 3, x = g / per;
+  return x * a.sk_q + min(x, a.sk_x) + r * per + (g - x * per);
+}
+// Range phase: row tile s of the sequence that the ranges cut (the blocks'
+// remainders, in block order).
+__device__ __forceinline__ int sk_rest_row(const FlashArgs& a, int s) {
+  const int per = a.sk_grid >> 3, qq = a.sk_q - a.sk_K * per;   // a block's remainder: qq or qq + 1
+  const int x = s < a.sk_x * (qq + 1) ? s / (qq + 1) : a.sk_x + (s - a.sk_x * (qq + 1)) / max(qq, 1);
+  return s + (x + 1) * a.sk_K * per;
 }
 
 // Pooled mode: key tile kt of the packed kept set (keys 64 kt .. 64 kt + 63)
@@ -537,23 +557,26 @@ __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  // Work item: gather mode (the full route), row tile Ri = bh * row_tiles +
-  // rt whole (lid = Ri < sk_R0), or part p of row tile Ri = sk_R0 + Rs under
-  // the stream-K ranges (lid = sk_R0 + Rs * sk_P + p; a row tile with fewer
-  // parts leaves its last workgroups without work); dense mode, row tile rt
-  // of head bh (one key range).  Consecutive items run on one XCD and share
-  // its L2.
+  // Work item: gather mode (the full route), whole-round item lid < sk_R0
+  // (round lid / sk_grid of workgroup lid % sk_grid), or part p of row tile
+  // Rs of the range phase (lid = sk_R0 + Rs * sk_P + p; a row tile with fewer
+  // parts leaves its last workgroups without work), each on the row tile
+  // Ri = bh * row_tiles + rt that the persistent kernel gives it; dense mode,
+  // row tile rt of head bh (one key range).  Consecutive items run on one XCD
+  // and share its L2.
   int bh, rt, part = -1;   // part < 0: the whole row tile (output written here)
   int Rs = 0;              // the row tile's index in the partial buffer
   int t_begin = 0, t_end = 0;   // key tiles of the item (gather)
   if constexpr (GATHER) {
     const int lid = xcd_remap(blockIdx.x, a.n_wg);
-    int Ri = lid;
+    int Ri;
     t_end = a.sk_T;
-    if (lid >= a.sk_R0) {
+    if (lid < a.sk_R0) {
+      Ri = sk_round_row(a, lid / a.sk_grid, lid % a.sk_grid);
+    } else {
       Rs = (lid - a.sk_R0) / a.sk_P;
       const int p = lid - a.sk_R0 - Rs * a.sk_P;
-      Ri = a.sk_R0 + Rs;
+      Ri = sk_rest_row(a, Rs);
       const long long u0 = (long long)Rs * a.sk_T;
       // (64-bit quotients come out in vector registers: made scalar again)
       const int gf = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0));
@@ -968,19 +991,21 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   const int kdp = a.sk_K;
   const int nr = kdp + nsk;
 
-  struct Item { int bh, rt, part, t_begin, nt; };   // part < 0: the whole row tile
+  // part < 0: the whole row tile; else 8 Rs + part, Rs the row tile's index
+  // in the range phase (its partial buffer slot)
+  struct Item { int bh, rt, part, t_begin, nt; };
   // (t_begin: the item's first key tile in rotated order; its nt key tiles
   // follow it without wrapping)
   auto item_of = [&](int r) -> Item {
     int Ri, t0 = 0, t1 = T, tb = 0, part = -1;
     if (r < kdp) {
-      Ri = r * G + g;
+      Ri = sk_round_row(a, r, g);
     } else {
       const int q = r - kdp;
-      Ri = a.sk_R0 + R0 + q;
+      Ri = sk_rest_row(a, R0 + q);
       if (q == 0) t0 = t00;
       if (q == nsk - 1) t1 = t1l;
-      if (t0 > 0 || t1 < T) part = q == 0 ? part0 : 0;
+      if (t0 > 0 || t1 < T) part = 8 * (R0 + q) + (q == 0 ? part0 : 0);
       // a later item starts at its row tile's first unit, inside this range:
       // the boundary is this range's end, t1 units in
       tb = q == 0 ? tb0 : (t1 < T ? T - t1 : 0);
@@ -1212,10 +1237,10 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref * sc + __builtin_log2f(l_tot)), rL,
                                            (qrow >= 0 && h == 0) ? (unsigned)qrow * 4 : kOut, 0, 0);
     } else {
-      // part it.part of the row tile: [Ri - sk_R0][sk_P][BM][D] partial outputs
-      const long long prow0 = ((long long)it.bh * a.row_tiles + it.rt - a.sk_R0) * a.sk_P * BM;   // its first partial row
+      // part it.part & 7 of the row tile: [Rs][sk_P][BM][D] partial outputs
+      const long long prow0 = (long long)(it.part >> 3) * a.sk_P * BM;   // its first partial row
       const int nrow = a.sk_P * BM;
-      const int prow = it.part * BM + w * 32 + l32;
+      const int prow = (it.part & 7) * BM + w * 32 + l32;
       const auto rP = __builtin_amdgcn_make_buffer_rsrc(a.part_o + prow0 * D, (short)0, nrow * RB, 0x00020000);
       store_rows(rP, (unsigned)prow * RB, l_tot > 0.f ? 1.0f / l_tot : 0.f);
       const auto rM = __builtin_amdgcn_make_buffer_rsrc(a.part_ml + prow0 * 2, (short)0, nrow * 8, 0x00020000);
@@ -1725,15 +1750,15 @@ __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   int np;
   long long prow, pstep;
   if (a.sk_G > 0) {
-    // stream-K: the launch covers the rows of row tiles sk_R0 on; row tile
-    // Ri = sk_R0 + Rs met ranges first .. last; one range wrote it whole
+    // stream-K: the launch covers the rows of the range phase's row tiles;
+    // its row tile Rs met ranges first .. last; one range wrote it whole
     const long long Rs = gid / kFlashRows, ub = Rs * a.sk_T;
     if (ub >= a.sk_U) return;
     np = sk_range_of(a, ub + a.sk_T - 1) - sk_range_of(a, ub) + 1;
     if (np == 1) return;
     prow = Rs * a.sk_P * kFlashRows + (gid - Rs * kFlashRows);
     pstep = kFlashRows;
-    gid += (long long)a.sk_R0 * kFlashRows;
+    gid += ((long long)sk_rest_row(a, (int)Rs) - Rs) * kFlashRows;
   } else {
     np = a.nsplit;
     prow = gid * a.nsplit;
@@ -1826,10 +1851,13 @@ static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, lo
       // (a.sk_K rounds of grid workgroups, a.sk_G ranges)
       const long long R = (long long)a.row_tiles * BH, grid = a.sk_R0;
       a.sk_R0 = (int)(grid * a.sk_K);
+      a.sk_grid = (int)grid;
+      a.sk_q = (int)(R / 8);
+      a.sk_x = (int)(R % 8);
       a.sk_T = ntiles;
       a.sk_U = (R - a.sk_R0) * ntiles;
-      if (grid <= 0 || a.sk_K < 0 || a.sk_R0 > R || (a.sk_U > 0) != (a.sk_G > 0) || a.sk_U < a.sk_G ||
-          a.sk_P < 1 || a.sk_P > kMaxSplits)
+      if (grid <= 0 || grid % 8 != 0 || a.sk_K < 0 || a.sk_R0 > R || (a.sk_U > 0) != (a.sk_G > 0) ||
+          a.sk_U < a.sk_G || a.sk_P < 1 || a.sk_P > kMaxSplits)
         return hipErrorInvalidValue;
       // persistent form, one workgroup per round slot and range, when a
       // workgroup meets at most kPpsMaxItems row tiles and K and V share one
@@ -1894,6 +1922,10 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
         a.sk_P = L.sk_P;
         a.sk_T = (int)((L.Ns + L.ctx_tok + 63) / 64);
         a.sk_R0 = L.sk_grid * L.sk_rounds;
+        a.sk_K = L.sk_rounds;
+        a.sk_grid = L.sk_grid;
+        a.sk_q = (int)((long long)a.row_tiles * L.BH / 8);
+        a.sk_x = (int)((long long)a.row_tiles * L.BH % 8);
         a.sk_U = ((long long)a.row_tiles * L.BH - a.sk_R0) * a.sk_T;
         rows -= (long long)a.sk_R0 * kFlashRows;
       }
