@@ -124,6 +124,13 @@ __device__ __forceinline__ void dma4(unsigned lds, const void* base, unsigned vo
 // c of row r sits at chunk c ^ lds_swz(r).
 __device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// The same for 128-byte rows (d = 64), two rows to the 64 banks: chunk c of
+// row r sits at chunk c ^ lds_swz64(r).  Over 16 consecutive rows the rows of
+// one parity take 8 distinct values (the K operand reads: 16 rows at one
+// chunk on 16 distinct 16-byte bank groups), and rows r, r + 2 of a 4-row
+// group differ above bit 0 (the V^T transpose reads: 4 rows at a chunk pair).
+__device__ __forceinline__ int lds_swz64(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+
 // Two direct loads of 16 bytes per lane from base + v0 / v1 into LDS at
 // l0 / l1 + 16 x lane, in one asm block; waited for by count.
 __device__ __forceinline__ void dma16x2(unsigned l0, unsigned l1, const void* base, unsigned v0, unsigned v1) {

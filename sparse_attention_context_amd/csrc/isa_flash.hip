@@ -17,9 +17,11 @@
 //    softmax, exp2(max - ref) / l, is the query sharpness.  Pooled keys come
 //    as bf16 hi + lo parts (two MFMAs) so the logits carry ~2^-17.
 //
-// Two kernels: isa_flash_kernel (below) runs the pooled pass and d = 64;
-// isa_flash_pp_kernel runs the token modes at d = 128 with the same
-// arithmetic on a ping-pong wave schedule and direct global->LDS loads.
+// Two kernels: isa_flash_kernel (below) runs the pooled pass at d = 64 and
+// the stand-alone pooled stages; isa_flash_pp_kernel runs the token modes
+// (d = 128 and 64) with the same arithmetic on a ping-pong wave schedule and
+// direct global->LDS loads, and isa_flash_pp_pooled_kernel the pooled pass at
+// d = 128.
 //
 // Workgroup: NW waves, 32 query rows each; key tiles of 64.  Each wave
 // computes S^T = K Q^T with 32x32x16 MFMAs (lane = one query, 32 keys), the
@@ -149,6 +151,63 @@ __device__ __forceinline__ int sk_rest_row(const FlashArgs& a, int s) {
   const int per = a.sk_grid >> 3, qq = a.sk_q - a.sk_K * per;   // a block's remainder: qq or qq + 1
   const int x = s < a.sk_x * (qq + 1) ? s / (qq + 1) : a.sk_x + (s - a.sk_x * (qq + 1)) / max(qq, 1);
   return s + (x + 1) * a.sk_K * per;
+}
+// The work of stream-K workgroup g (logical id) of a grid of G: kdp whole
+// row tiles (round r: sk_round_row(r, g)), then the nsk row tiles that its
+// range [u0, u1) meets, key tiles t00 .. of range-phase row tile R0 through
+// row tile R0 + nsk - 1 (t1l key tiles of the last).  part0: the part of row
+// tile R0 that the range takes when that row tile starts in an earlier
+// range (later items start in this one: part 0 or whole); tb0: its first
+// key tile in rotated order.  (64-bit quotients come out in vector
+// registers: made scalar again.)
+struct SkItems { int g, kdp, nsk, R0, t00, t1l, part0, tb0; };
+__device__ __forceinline__ SkItems sk_items(const FlashArgs& a, int g) {
+  SkItems s;
+  s.g = g;
+  s.kdp = a.sk_K;
+  const int T = a.sk_T;
+  long long u0 = 0, u1 = 0;
+  if (g < a.sk_G) {
+    u0 = sk_bound(a, g);
+    u1 = sk_bound(a, g + 1);
+  }
+  s.R0 = __builtin_amdgcn_readfirstlane((int)(u0 / T));
+  s.nsk = __builtin_amdgcn_readfirstlane(u1 > u0 ? (int)((u1 - 1) / T) - s.R0 + 1 : 0);
+  s.t00 = __builtin_amdgcn_readfirstlane((int)(u0 - (long long)s.R0 * T));
+  s.t1l = __builtin_amdgcn_readfirstlane((int)(u1 - (long long)(s.R0 + s.nsk - 1) * T));
+  s.part0 = __builtin_amdgcn_readfirstlane(s.t00 > 0 ? g - sk_range_of(a, (long long)s.R0 * T) : 0);
+  // key tiles of a cut row tile run from its first inner range boundary,
+  // delta units in: t -> t - delta mod T
+  int tb0 = s.t00;
+  if (s.t00 > 0) {
+    const long long base = (long long)s.R0 * T;
+    if (sk_bound(a, g - s.part0) != base) tb0 = s.t00 - (int)(sk_bound(a, g - s.part0 + 1) - base);
+  }
+  s.tb0 = __builtin_amdgcn_readfirstlane(tb0);
+  return s;
+}
+// Item r of those: row tile (bh, rt); part < 0 for the whole row tile, else
+// 8 Rs + p for part p of range-phase row tile Rs (its partial buffer slot);
+// t_begin: its first key tile in rotated order, the nt key tiles following
+// it without wrapping.
+struct SkItem { int bh, rt, part, t_begin, nt; };
+__device__ __forceinline__ SkItem sk_item(const FlashArgs& a, const SkItems& s, int r) {
+  const int T = a.sk_T;
+  int Ri, t0 = 0, t1 = T, tb = 0, part = -1;
+  if (r < s.kdp) {
+    Ri = sk_round_row(a, r, s.g);
+  } else {
+    const int q = r - s.kdp;
+    Ri = sk_rest_row(a, s.R0 + q);
+    if (q == 0) t0 = s.t00;
+    if (q == s.nsk - 1) t1 = s.t1l;
+    if (t0 > 0 || t1 < T) part = 8 * (s.R0 + q) + (q == 0 ? s.part0 : 0);
+    // a later item starts at its row tile's first unit, inside this range:
+    // the boundary is this range's end, t1 units in
+    tb = q == 0 ? s.tb0 : (t1 < T ? T - t1 : 0);
+  }
+  const int bh = Ri / a.row_tiles;
+  return SkItem{bh, Ri - bh * a.row_tiles, part, tb, t1 - t0};
 }
 
 // Pooled mode: key tile kt of the packed kept set (keys 64 kt .. 64 kt + 63)
@@ -514,7 +573,7 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 }
 
 // Ping-pong schedule for the token modes (full route, dense, context rows),
-// d = 128.
+// d = 128 and d = 64.
 //
 // Two groups of four waves (waves w and w+4 share a SIMD) run the same tile
 // loop one phase apart, so that one group's MFMA cluster overlaps the other
@@ -531,397 +590,406 @@ __global__ __launch_bounds__(NW * 64) void isa_flash_kernel(FlashArgs a) {
 // wave waits for its loads of Y_{j-1} before the barrier that closes Y_j, so
 // every tile is in LDS two phases before its first read.
 //
-// LDS rows are 256 bytes, unpadded; the 16-byte chunk c of row r is stored
-// at chunk c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3).  Sixteen
-// consecutive rows at one chunk (the K operand reads) and four consecutive
-// rows at four consecutive chunks (the V^T transpose reads) then fall on
-// distinct banks.  Operand addresses are per-lane offsets computed once.
+// LDS rows are 2d bytes, unpadded; the 16-byte chunk c of row r is stored
+// at chunk c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3) for 256-byte
+// rows (lds_swz64 for 128-byte rows).  Sixteen consecutive rows at one chunk
+// (the K operand reads) and four consecutive rows at four consecutive chunks
+// (the V^T transpose reads) then fall on distinct banks.  A wave loads 8 rows
+// of each tile: two loads of 4 rows (d = 128) or one of 8 (d = 64).  Operand
+// addresses are per-lane offsets computed once.
 // Numerics are those of isa_flash_kernel: the same per-row reference max,
 // sums and bf16 roundings.
 // (lds_swz, dma16x2 and pp_issue_order are in isa_device.h)
 
-template <int KM, int RM>
+template <int KM, int RM, int D>
 __global__ __launch_bounds__(512) void isa_flash_pp_kernel(FlashArgs a) {
   typedef bf16x8 Op;
-  constexpr int D = 128;
+  static_assert(D == 128 || D == 64, "head sizes of the ping-pong kernel");
   constexpr bool GATHER = KM == FK_GATHER;
   static_assert(KM != FK_POOLED, "token modes only");
   constexpr int BN = 64, BM = 256, NST = 4;
   constexpr int RB = D * 2;                      // row bytes (global and LDS)
   constexpr int TB = BN * RB;                    // tile bytes
   constexpr int NT = D / 32;
+  constexpr int LPR = RB / 16;                   // lanes per row of one 16-byte load
+  constexpr int NLD = LPR / 8;                   // loads per wave and tile (8 rows)
   static_assert(BM == kFlashRows, "tile mapping");
+  auto swz = [](int r) { return D == 128 ? lds_swz(r) : lds_swz64(r); };
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TB];   // K ring, then V ring
+  __shared__ __attribute__((aligned(16))) int stab[GATHER ? 8 : 1][4][64];   // per-wave key-table ring (gather)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  // Work item: gather mode (the full route), whole-round item lid < sk_R0
-  // (round lid / sk_grid of workgroup lid % sk_grid), or part p of row tile
-  // Rs of the range phase (lid = sk_R0 + Rs * sk_P + p; a row tile with fewer
-  // parts leaves its last workgroups without work), each on the row tile
-  // Ri = bh * row_tiles + rt that the persistent kernel gives it; dense mode,
-  // row tile rt of head bh (one key range).  Consecutive items run on one XCD
-  // and share its L2.
-  int bh, rt, part = -1;   // part < 0: the whole row tile (output written here)
-  int Rs = 0;              // the row tile's index in the partial buffer
-  int t_begin = 0, t_end = 0;   // key tiles of the item (gather)
+  // Work items: gather mode (the full route), the items of stream-K
+  // workgroup g (the logical id), as the persistent kernel takes them -- its
+  // whole row tiles, then the row tiles that its range meets -- one after
+  // the other, the pipeline drained between them; dense mode, row tile rt of
+  // head bh (one key range).  Consecutive workgroups run on one XCD and share
+  // its L2.
+  int n_items = 1;
+  SkItems sk = {};
   if constexpr (GATHER) {
-    const int lid = xcd_remap(blockIdx.x, a.n_wg);
-    int Ri;
-    t_end = a.sk_T;
-    if (lid < a.sk_R0) {
-      Ri = sk_round_row(a, lid / a.sk_grid, lid % a.sk_grid);
+    sk = sk_items(a, xcd_remap((int)blockIdx.x, (int)gridDim.x));
+    n_items = sk.kdp + sk.nsk;
+  }
+#pragma unroll 1
+  for (int item = 0; item < n_items; ++item) {
+    int bh, rt, part = -1;   // part < 0: the whole row tile (output written here)
+    int Rs = 0;              // else part `part` of range-phase row tile Rs (its partial buffer slot)
+    int t_begin = 0, t_end = 0;   // key tiles of the item (gather)
+    if constexpr (GATHER) {
+      const SkItem it = sk_item(a, sk, item);
+      bh = it.bh;
+      rt = it.rt;
+      t_begin = it.t_begin;
+      t_end = it.t_begin + it.nt;
+      if (it.part >= 0) {
+        part = it.part & 7;
+        Rs = it.part >> 3;
+      }
+      if (item > 0) __syncthreads();   // the previous item's LDS reads are done
     } else {
-      Rs = (lid - a.sk_R0) / a.sk_P;
-      const int p = lid - a.sk_R0 - Rs * a.sk_P;
-      Ri = sk_rest_row(a, Rs);
-      const long long u0 = (long long)Rs * a.sk_T;
-      // (64-bit quotients come out in vector registers: made scalar again)
-      const int gf = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0));
-      const int gl = __builtin_amdgcn_readfirstlane(sk_range_of(a, u0 + a.sk_T - 1));
-      if (p > gl - gf) return;
-      const int tb = (int)max(sk_bound(a, gf + p) - u0, 0LL);
-      const int te = (int)min(sk_bound(a, gf + p + 1) - u0, (long long)a.sk_T);
-      // rotated key order of a cut row tile (delta: its first inner range boundary)
-      const int delta = (sk_bound(a, gf) == u0 || gl == gf) ? 0 : (int)(sk_bound(a, gf + 1) - u0);
-      t_begin = __builtin_amdgcn_readfirstlane(tb >= delta ? tb - delta : tb - delta + a.sk_T);
-      t_end = __builtin_amdgcn_readfirstlane(t_begin + te - tb);
-      part = gl > gf ? p : -1;
+      const int lid = xcd_remap(blockIdx.x, a.n_wg);
+      rt = lid % a.row_tiles;
+      bh = lid / a.row_tiles;
     }
-    bh = Ri / a.row_tiles;
-    rt = Ri - bh * a.row_tiles;
-  } else {
-    const int lid = xcd_remap(blockIdx.x, a.n_wg);
-    rt = lid % a.row_tiles;
-    bh = lid / a.row_tiles;
-  }
 
-  const long long vrow = (long long)rt * BM + w * 32 + l32;
-  int qrow;
-  if constexpr (RM == FR_TABLE) qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
-  else qrow = vrow < a.Ns ? (int)vrow : -1;
-  Op qB[D / 16];
-  {
-    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
+    const long long vrow = (long long)rt * BM + w * 32 + l32;
+    int qrow;
+    if constexpr (RM == FR_TABLE) qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
+    else qrow = vrow < a.Ns ? (int)vrow : -1;
+    Op qB[D / 16];
+    {
+      const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn + 8 * h;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
-  }
-
-  int n_keys, n_valid;
-  if constexpr (GATHER) {
-    n_keys = a.Ns + (int)a.ctx_tok;
-    const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
-    n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
-  } else {
-    n_keys = n_valid = a.Nk;
-  }
-  const int nt = GATHER ? t_end - t_begin : (n_keys + BN - 1) / BN;
-
-  const char* Kg = (const char*)a.K + rm_head(a.rmk, bh) * 2;
-  const char* Vg = (const char*)a.V + rm_head(a.rmv, bh) * 2;
-  const unsigned krs = (unsigned)a.rmk.sn * 2u, vrs = (unsigned)a.rmv.sn * 2u;   // row steps in bytes (< 2^24)
-  const int* tab = GATHER ? a.key_rows + (long long)bh * a.n_keytab : nullptr;
-
-  // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
-  // tile, one 16-byte chunk each: physical chunk lane%16 of the row, which
-  // holds logical chunk (lane%16) ^ f(row).
-  const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
-  struct Rows { int r[2]; };
-  // Gather: the key-row table entries of the wave's 8 rows of tile t come to a
-  // per-wave LDS ring (slot t % 4) by a direct load in step t-6, entry
-  // 2q + i holding row 32*grp + 8*wg + q + 4i, are read into registers in
-  // step t-4 and used in steps t-3 (K) and t-2 (V); so no load result is
-  // waited for inside the tile loop.
-  __shared__ __attribute__((aligned(16))) int stab[GATHER ? 8 : 1][4][64];
-  // (slots are indexed by the tile's position j in this workgroup's range)
-  const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
-                          __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
-  auto fetch_rows = [&](int j, int tile) {
-    if constexpr (GATHER) {
-      const int k = 4 * (lane & 1) + ((lane >> 1) & 3);
-      const int idx = tile * BN + 32 * grp + 8 * wg + k;
-      dma4(stab_w + (unsigned)(j & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)idx * 4u);
+      for (int s = 0; s < D / 16; ++s) qB[s] = *(const Op*)(qp + 16 * s);
     }
-  };
-  auto rows_of = [&](int j) -> Rows {
-    Rows rows = {};
+
+    int n_keys, n_valid;
     if constexpr (GATHER) {
-      const int2 v = *(const int2*)&stab[w][j & 3][2 * (lane >> 4)];
-      rows.r[0] = v.x;
-      rows.r[1] = v.y;
-    }
-    return rows;
-  };
-  const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
-  const unsigned lds_v = lds_k + NST * TB;
-  // Lane part of the i-th load: row lrow0 + 4i (its offset within a tile,
-  // in K and in V rows) and the 16-byte chunk that the swizzle puts at this
-  // lane.
-  unsigned lchunk[2], lrowk[2], lrowv[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    lchunk[i] = (unsigned)(((lane & 15) ^ lds_swz(lrow0 + 4 * i)) * 16);
-    lrowk[i] = __umul24((unsigned)(lrow0 + 4 * i), krs) + lchunk[i];
-    lrowv[i] = __umul24((unsigned)(lrow0 + 4 * i), vrs) + lchunk[i];
-  }
-  // Global offsets of the wave's two loads of a tile (rows rs bytes apart;
-  // lro: the lane parts for that tensor): gathered rows come from the
-  // key-row table (whose padding reads row 0), dense tiles of valid rows
-  // only are a contiguous row range (a uniform branch).
-  auto src_offs = [&](Rows rows, int tile, unsigned* o, unsigned rs, const unsigned* lro) {
-    const int t0 = tile * BN;
-    if constexpr (GATHER) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) o[i] = __umul24((unsigned)rows.r[i], rs) + lchunk[i];
+      n_keys = a.Ns + (int)a.ctx_tok;
+      const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
+      n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
     } else {
-      if (t0 + BN <= n_valid) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) o[i] = (unsigned)t0 * rs + lro[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int t = t0 + lrow0 + 4 * i;
-          o[i] = __umul24((unsigned)(t < n_valid ? t : 0), rs) + lchunk[i];
+      n_keys = n_valid = a.Nk;
+    }
+    const int nt = GATHER ? t_end - t_begin : (n_keys + BN - 1) / BN;
+
+    const char* Kg = (const char*)a.K + rm_head(a.rmk, bh) * 2;
+    const char* Vg = (const char*)a.V + rm_head(a.rmv, bh) * 2;
+    const unsigned krs = (unsigned)a.rmk.sn * 2u, vrs = (unsigned)a.rmv.sn * 2u;   // row steps in bytes (< 2^24)
+    const int* tab = GATHER ? a.key_rows + (long long)bh * a.n_keytab : nullptr;
+
+    // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
+    // tile (d = 64: rows 32*grp + 8*wg + lane/8), one 16-byte chunk each:
+    // physical chunk lane%16 (lane%8) of the row, which holds logical chunk
+    // (lane%16) ^ f(row).
+    const int lrow0 = 32 * grp + 8 * wg + lane / LPR;
+    struct Rows { int r[NLD]; };
+    // Gather: the key-row table entries of the wave's 8 rows of tile t come to a
+    // per-wave LDS ring (slot t % 4) by a direct load in step t-6, entry
+    // 2q + i holding row 32*grp + 8*wg + q + 4i (d = 64: entry q row
+    // 32*grp + 8*wg + q), are read into registers in step t-4 and used in
+    // steps t-3 (K) and t-2 (V); so no load result is waited for inside the
+    // tile loop.
+    // (slots are indexed by the tile's position j in this workgroup's range)
+    const unsigned stab_w = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)&stab[0][0][0]) +
+                            __builtin_amdgcn_readfirstlane(w) * (unsigned)sizeof(stab[0]);
+    auto fetch_rows = [&](int j, int tile) {
+      if constexpr (GATHER) {
+        const int k = D == 128 ? 4 * (lane & 1) + ((lane >> 1) & 3) : (lane & 7);
+        const int idx = tile * BN + 32 * grp + 8 * wg + k;
+        dma4(stab_w + (unsigned)(j & 3) * (unsigned)sizeof(stab[0][0]), tab, (unsigned)idx * 4u);
+      }
+    };
+    auto rows_of = [&](int j) -> Rows {
+      Rows rows = {};
+      if constexpr (GATHER) {
+        if constexpr (D == 128) {
+          const int2 v = *(const int2*)&stab[w][j & 3][2 * (lane >> 4)];
+          rows.r[0] = v.x;
+          rows.r[NLD - 1] = v.y;
+        } else {
+          rows.r[0] = stab[w][j & 3][lane >> 3];
         }
       }
+      return rows;
+    };
+    const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem;
+    const unsigned lds_v = lds_k + NST * TB;
+    // Lane part of the i-th load: row lrow0 + 4i (its offset within a tile,
+    // in K and in V rows) and the 16-byte chunk that the swizzle puts at this
+    // lane.
+    unsigned lchunk[NLD], lrowk[NLD], lrowv[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      lchunk[i] = (unsigned)(((lane & (LPR - 1)) ^ swz(lrow0 + 4 * i)) * 16);
+      lrowk[i] = __umul24((unsigned)(lrow0 + 4 * i), krs) + lchunk[i];
+      lrowv[i] = __umul24((unsigned)(lrow0 + 4 * i), vrs) + lchunk[i];
     }
-  };
-  // LDS base of this wave's first load into a ring stage (the second is 4
-  // rows further)
-  const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
-  auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, int tile, unsigned rs,
-                        const unsigned* lro) {
-    unsigned o[2];
-    src_offs(rows, tile, o, rs, lro);
-    const unsigned d0 = ring + wrow + (unsigned)stage * TB;
-    dma16x2(d0, d0 + 4 * RB, base, o[0], o[1]);
-  };
-  auto issue = [&](int sk, Rows rk, int tk, int sv, Rows rv, int tv) {
-    issue_tile(lds_k, sk, Kg, rk, tk, krs, lrowk);
-    issue_tile(lds_v, sv, Vg, rv, tv, vrs, lrowv);
-  };
+    // Global offsets of the wave's two loads of a tile (rows rs bytes apart;
+    // lro: the lane parts for that tensor): gathered rows come from the
+    // key-row table (whose padding reads row 0), dense tiles of valid rows
+    // only are a contiguous row range (a uniform branch).
+    auto src_offs = [&](Rows rows, int tile, unsigned* o, unsigned rs, const unsigned* lro) {
+      const int t0 = tile * BN;
+      if constexpr (GATHER) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) o[i] = __umul24((unsigned)rows.r[i], rs) + lchunk[i];
+      } else {
+        if (t0 + BN <= n_valid) {
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) o[i] = (unsigned)t0 * rs + lro[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) {
+            const int t = t0 + lrow0 + 4 * i;
+            o[i] = __umul24((unsigned)(t < n_valid ? t : 0), rs) + lchunk[i];
+          }
+        }
+      }
+    };
+    // LDS base of this wave's first load into a ring stage (the second is 4
+    // rows further)
+    const unsigned wrow = __builtin_amdgcn_readfirstlane((32 * grp + 8 * wg) * RB);
+    auto issue_tile = [&](unsigned ring, int stage, const char* base, Rows rows, int tile, unsigned rs,
+                          const unsigned* lro) {
+      unsigned o[NLD];
+      src_offs(rows, tile, o, rs, lro);
+      const unsigned d0 = ring + wrow + (unsigned)stage * TB;
+      if constexpr (NLD == 2) dma16x2(d0, d0 + 4 * RB, base, o[0], o[NLD - 1]);
+      else dma16(d0, base, o[0]);
+    };
+    auto issue = [&](int sk, Rows rk, int tk, int sv, Rows rv, int tv) {
+      issue_tile(lds_k, sk, Kg, rk, tk, krs, lrowk);
+      issue_tile(lds_v, sv, Vg, rv, tv, vrs, lrowv);
+    };
 
-  // operand offsets: K row 32*ti + l32, logical chunk 2s + h; V^T transpose
-  // reads at key rows 16s + 4h + m/4 (+8), d = 32t + 16(g%2) + 4(m%4), with
-  // g = lane/16, m = lane%16 (see isa_flash_kernel)
-  int koff[8], voff[NT][2];
+    // operand offsets: K row 32*ti + l32, logical chunk 2s + h; V^T transpose
+    // reads at key rows 16s + 4h + m/4 (+8), d = 32t + 16(g%2) + 4(m%4), with
+    // g = lane/16, m = lane%16 (see isa_flash_kernel)
+    int koff[D / 16], voff[NT][2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ lds_swz(l32)) * 16));
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int m = lane & 15;
-      const int kr = 4 * h + (m >> 2) + 8 * hi;
-      const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
-      voff[t][hi] = NST * TB + kr * RB + ((c ^ lds_swz(kr)) * 16) + 8 * (m & 1);
-    }
-
-  struct STile { f32x16 t[2]; };
-  struct PTile { Op p[4]; };
-  f32x16 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.f;
-  const float sc = a.scale_log2;
-  const float thresh = 8.0f / sc;
-
-  // X phase with both products as one pipeline of 32 MFMAs (16 of P.V, then
-  // 16 of K.Q^T); the operand reads of each MFMA are issued LA MFMAs ahead.
-  auto pv_qk = [&](int vstage, const PTile& P, int kstage) -> STile {
-    constexpr int LA = ISA_PP_LOOKAHEAD;
-    const lds_char* Vs = (const lds_char*)smem + vstage * TB;
-    const lds_char* Ks = (const lds_char*)smem + kstage * TB;
-    Op opv[16], opk[16];
+    for (int s = 0; s < D / 16; ++s) koff[s] = l32 * RB + ((((2 * s + h) ^ swz(l32)) * 16));
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * q * RB));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * q * RB));
-        opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int hi = 0; hi < 2; ++hi) {
+        const int m = lane & 15;
+        const int kr = 4 * h + (m >> 2) + 8 * hi;
+        const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+        voff[t][hi] = NST * TB + kr * RB + ((c ^ swz(kr)) * 16) + 8 * (m & 1);
       }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) opk[2 * q + ti] = *(const Op*)(Ks + koff[q] + 32 * ti * RB);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) acc[m >> 2] = mma32(opv[m], P.p[m & 3], acc[m >> 2]);
-    STile S;
-    S.t[0] = f32x16{};
-    S.t[1] = f32x16{};
-#pragma unroll
-    for (int m = 0; m < 16; ++m) S.t[m & 1] = mma32(opk[m], qB[m >> 1], S.t[m & 1]);
-    pp_issue_order<LA>();
-    return S;
-  };
-  auto exp_tile = [&](const f32x16* S, PTile& P) -> float {
-    const float msub = m_ref * sc;
-    float psum = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, -msub));
-        psum += p;
-        P.p[s][jj] = (__bf16)p;
-      }
-    }
-    return psum;
-  };
-  // Probabilities are first taken against the current reference max.  Any
-  // probability above 2^8 (the point where isa_flash_kernel moves a row's
-  // reference) makes the lane's tile sum exceed 2^7, so only then is the
-  // row maximum formed and the move rule applied, and the tile recomputed:
-  // the same references, sums and roundings as isa_flash_kernel.
-  auto softmax = [&](int j, STile St) -> PTile {
-    f32x16* S = St.t;
-    const int t0 = (t_begin + j) * BN;
-    if (t0 + BN > n_valid) {
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t0 + 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) S[ti][r] = -INFINITY;
-    }
-    PTile P;
-    float psum = exp_tile(S, P);
-    if (__ballot(!(psum <= 128.f))) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const bool move = mx > m_ref + thresh;
-      if (__ballot(move)) {
-        const float m_new = move ? mx : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sc);
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-        m_ref = m_new;
-        psum = exp_tile(S, P);
-      }
-    }
-    l_run += psum;
-    return P;
-  };
 
-  // Barrier without a memory fence: the direct loads are waited for by
-  // count (s_waitcnt vmcnt), every LDS read has been consumed by an MFMA
-  // before the barrier, and the empty asm keeps the compiler from moving
-  // memory accesses across it.
-  auto phase_barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // ---- tile loop, unrolled by four so that every ring stage is a
-  // compile-time choice.  Positions past the last tile are clamped to it.
-  auto cl = [&](int j) { return min(j, nt - 1); };
-  auto tl = [&](int j) { return t_begin + cl(j); };
-  if (nt > 0) {
-    Rows rk, rv;   // rows of tiles j+3 (K) and j+2 (V) entering step j
-    {
-      fetch_rows(cl(0), tl(0));
-      fetch_rows(cl(1), tl(1));
-      fetch_rows(cl(2), tl(2));
-      fetch_rows(cl(3), tl(3));
-      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-      const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1));
-      rv = rows_of(cl(2));
-      rk = rows_of(cl(3));
-      issue(0, r0, tl(0), 0, r0, tl(0));
-      issue(1, r1, tl(1), 1, r1, tl(1));
-      // K(2) (V(2) is loaded again by the first step, into the same stage)
-      issue(2, rv, tl(2), 2, rv, tl(2));
-      fetch_rows(cl(4), tl(4));
-      fetch_rows(cl(5), tl(5));
-      // V stage 3 is first loaded in step 1; step 0 reads it as zeros
-      u32x4* vz = (u32x4*)(smem + NST * TB + 3 * TB);
+    struct STile { f32x16 t[2]; };
+    struct PTile { Op p[4]; };
+    f32x16 acc[NT];
 #pragma unroll
-      for (int q = 0; q < TB / (16 * 512); ++q) vz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
-      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): prologue loads and the zero fill
-    }
-    phase_barrier();
-    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
-    STile S = {};
-    PTile P = {};
-    // Loads past the last tile re-read it (clamped) into the stage that the
-    // schedule frees for tile j+3 / j+2 and are never read, so every step
-    // issues the same loads and waits by the same count.
-    auto step = [&](int j) {
-      const int Z = j & 3;
-      // X_j, at raised wave priority: the MFMA group's instructions issue
-      // ahead of the softmax group's on the shared SIMD
-      __builtin_amdgcn_s_setprio(3);
-      // (step 0 multiplies the zeroed V stage 3 by P = 0, step nt computes
-      // an S that is never used: every step runs the same pipeline)
-      S = pv_qk((Z + 3) & 3, P, Z);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-      phase_barrier();
-      // Y_j
-      issue((Z + 3) & 3, rk, tl(j + 3), (Z + 2) & 3, rv, tl(j + 2));
-      const Rows rn = rows_of(cl(j + 4));   // used one step later: its LDS latency is hidden
-      fetch_rows(cl(j + 6), tl(j + 6));
-      if (j < nt) P = softmax(j, S);
-      rv = rk;
-      rk = rn;
-      // the loads of Y_{j-1} have landed before the barrier that closes Y_j
-      if constexpr (GATHER) __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
-      else __builtin_amdgcn_s_waitcnt(0x0f74);                    // vmcnt(4)
-      phase_barrier();
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.f;
+    const float sc = a.scale_log2;
+    const float thresh = 8.0f / sc;
+
+    // X phase with both products as one pipeline of D/4 MFMAs (D/8 of P.V,
+    // then D/8 of K.Q^T); the operand reads of each MFMA are issued LA MFMAs
+    // ahead.
+    auto pv_qk = [&](int vstage, const PTile& P, int kstage) -> STile {
+      constexpr int LA = ISA_PP_LOOKAHEAD;
+      constexpr int NM = D / 8;   // MFMAs of each product
+      const lds_char* Vs = (const lds_char*)smem + vstage * TB;
+      const lds_char* Ks = (const lds_char*)smem + kstage * TB;
+      Op opv[NM], opk[NM];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][0] + 16 * q * RB));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vs + voff[t][1] + 16 * q * RB));
+          opv[4 * t + q] = __builtin_bit_cast(Op, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) opk[2 * q + ti] = *(const Op*)(Ks + koff[q] + 32 * ti * RB);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[m >> 2] = mma32(opv[m], P.p[m & 3], acc[m >> 2]);
+      STile S;
+      S.t[0] = f32x16{};
+      S.t[1] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < NM; ++m) S.t[m & 1] = mma32(opk[m], qB[m >> 1], S.t[m & 1]);
+      pp_issue_order<LA, NM, NM>();
+      return S;
     };
-    for (int j = 0; j <= nt; ++j) step(j);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
-    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
-  }
+    auto exp_tile = [&](const f32x16* S, PTile& P) -> float {
+      const float msub = m_ref * sc;
+      float psum = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[s >> 1][8 * (s & 1) + jj], sc, -msub));
+          psum += p;
+          P.p[s][jj] = (__bf16)p;
+        }
+      }
+      return psum;
+    };
+    // Probabilities are first taken against the current reference max.  Any
+    // probability above 2^8 (the point where isa_flash_kernel moves a row's
+    // reference) makes the lane's tile sum exceed 2^7, so only then is the
+    // row maximum formed and the move rule applied, and the tile recomputed:
+    // the same references, sums and roundings as isa_flash_kernel.
+    auto softmax = [&](int j, STile St) -> PTile {
+      f32x16* S = St.t;
+      const int t0 = (t_begin + j) * BN;
+      if (t0 + BN > n_valid) {
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t0 + 32 * ti + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) S[ti][r] = -INFINITY;
+      }
+      PTile P;
+      float psum = exp_tile(S, P);
+      if (__ballot(!(psum <= 128.f))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[ti][r]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const bool move = mx > m_ref + thresh;
+        if (__ballot(move)) {
+          const float m_new = move ? mx : m_ref;
+          const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sc);
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+          m_ref = m_new;
+          psum = exp_tile(S, P);
+        }
+      }
+      l_run += psum;
+      return P;
+    };
 
-  // ---- epilogue (as isa_flash_kernel's).  16-byte chunk c = d / 8 of a
-  // row has its halves in lanes l and l + 32; for the chunk pair (2k, 2k+1)
-  // one permlane32 swap per word gives lane l all of chunk 2k and lane l + 32
-  // all of chunk 2k + 1, so each store writes 32 bytes of a row, not 16.
-  // (Both lanes of a row are active or inactive together.)
-  auto store_row = [&](bf16_t* rowp, float inv) {
+    // Barrier without a memory fence: the direct loads are waited for by
+    // count (s_waitcnt vmcnt), every LDS read has been consumed by an MFMA
+    // before the barrier, and the empty asm keeps the compiler from moving
+    // memory accesses across it.
+    auto phase_barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- tile loop, unrolled by four so that every ring stage is a
+    // compile-time choice.  Positions past the last tile are clamped to it.
+    auto cl = [&](int j) { return min(j, nt - 1); };
+    auto tl = [&](int j) { return t_begin + cl(j); };
+    if (nt > 0) {
+      Rows rk, rv;   // rows of tiles j+3 (K) and j+2 (V) entering step j
+      {
+        fetch_rows(cl(0), tl(0));
+        fetch_rows(cl(1), tl(1));
+        fetch_rows(cl(2), tl(2));
+        fetch_rows(cl(3), tl(3));
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        const Rows r0 = rows_of(cl(0)), r1 = rows_of(cl(1));
+        rv = rows_of(cl(2));
+        rk = rows_of(cl(3));
+        issue(0, r0, tl(0), 0, r0, tl(0));
+        issue(1, r1, tl(1), 1, r1, tl(1));
+        // K(2) (V(2) is loaded again by the first step, into the same stage)
+        issue(2, rv, tl(2), 2, rv, tl(2));
+        fetch_rows(cl(4), tl(4));
+        fetch_rows(cl(5), tl(5));
+        // V stage 3 is first loaded in step 1; step 0 reads it as zeros
+        u32x4* vz = (u32x4*)(smem + NST * TB + 3 * TB);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      unsigned x[2], y[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = 2 * k + u, t = c >> 2, g = c & 3;
-        unsigned* dst = u ? y : x;
-        dst[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
-        dst[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+        for (int q = 0; q < TB / (16 * 512); ++q) vz[tid + 512 * q] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): prologue loads and the zero fill
       }
+      phase_barrier();
+      if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+      STile S = {};
+      PTile P = {};
+      // Loads past the last tile re-read it (clamped) into the stage that the
+      // schedule frees for tile j+3 / j+2 and are never read, so every step
+      // issues the same loads and waits by the same count.
+      auto step = [&](int j) {
+        const int Z = j & 3;
+        // X_j, at raised wave priority: the MFMA group's instructions issue
+        // ahead of the softmax group's on the shared SIMD
+        __builtin_amdgcn_s_setprio(3);
+        // (step 0 multiplies the zeroed V stage 3 by P = 0, step nt computes
+        // an S that is never used: every step runs the same pipeline)
+        S = pv_qk((Z + 3) & 3, P, Z);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        phase_barrier();
+        // Y_j
+        issue((Z + 3) & 3, rk, tl(j + 3), (Z + 2) & 3, rv, tl(j + 2));
+        const Rows rn = rows_of(cl(j + 4));   // used one step later: its LDS latency is hidden
+        fetch_rows(cl(j + 6), tl(j + 6));
+        if (j < nt) P = softmax(j, S);
+        rv = rk;
+        rk = rn;
+        // the loads of Y_{j-1} have landed before the barrier that closes Y_j
+        // (this step's: K and V, NLD each, and the table chunk)
+        if constexpr (GATHER) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NLD + 1));   // vmcnt(5), d = 64 vmcnt(3)
+        else __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NLD));                        // vmcnt(4), d = 64 vmcnt(2)
+        phase_barrier();
+      };
+      for (int j = 0; j <= nt; ++j) step(j);
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+      if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+    }
+
+    // ---- epilogue (as isa_flash_kernel's).  16-byte chunk c = d / 8 of a
+    // row has its halves in lanes l and l + 32; for the chunk pair (2k, 2k+1)
+    // one permlane32 swap per word gives lane l all of chunk 2k and lane l + 32
+    // all of chunk 2k + 1, so each store writes 32 bytes of a row, not 16.
+    // (Both lanes of a row are active or inactive together.)
+    auto store_row = [&](bf16_t* rowp, float inv) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
-        x[e] = sw[0];
-        y[e] = sw[1];
+      for (int k = 0; k < D / 16; ++k) {
+        unsigned x[2], y[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int c = 2 * k + u, t = c >> 2, g = c & 3;
+          unsigned* dst = u ? y : x;
+          dst[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+          dst[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+          x[e] = sw[0];
+          y[e] = sw[1];
+        }
+        *(u32x4*)(rowp + 8 * (2 * k + h)) = u32x4{x[0], x[1], y[0], y[1]};
       }
-      *(u32x4*)(rowp + 8 * (2 * k + h)) = u32x4{x[0], x[1], y[0], y[1]};
+    };
+    const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+    if (part < 0) {
+      if (qrow >= 0) {
+        store_row((bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn, 1.0f / l_tot);
+        if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref * sc + __builtin_log2f(l_tot);
+      }
+    } else {
+      // part `part` of the row tile: [Rs][sk_P][BM][D] partial outputs
+      const long long prow = ((long long)Rs * a.sk_P + part) * BM + w * 32 + l32;
+      store_row(a.part_o + prow * D, l_tot > 0.f ? 1.0f / l_tot : 0.f);
+      if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref, l_tot};
     }
-  };
-  const float l_tot = l_run + wave_shfl_xor(l_run, 32);
-  if (part < 0) {
-    if (qrow >= 0) {
-      store_row((bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn, 1.0f / l_tot);
-      if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref * sc + __builtin_log2f(l_tot);
-    }
-  } else {
-    // part `part` of the row tile: [Rs][sk_P][BM][D] partial outputs
-    const long long prow = ((long long)Rs * a.sk_P + part) * BM + w * 32 + l32;
-    store_row(a.part_o + prow * D, l_tot > 0.f ? 1.0f / l_tot : 0.f);
-    if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref, l_tot};
-  }
+  }  // items
 }
 
 // Persistent form of the full-route ping-pong kernel: workgroup g takes
@@ -959,60 +1027,13 @@ __global__ __launch_bounds__(512) void isa_flash_pps_kernel(FlashArgs a) {
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
   const int n_keys = a.Ns + (int)a.ctx_tok;
-  // This workgroup's items: whole row tiles g, g + G, ... (sk_K of them;
-  // the workgroups of an XCD take consecutive row tiles), then the row tiles
-  // that its stream-K range meets (ranges of consecutive g on one XCD):
-  // units [u0, u1), i.e. key tiles t00 .. of row tile sk_R0 + R0 through row
-  // tile sk_R0 + R0 + nsk - 1.
-  // (64-bit quotients come out in vector registers: made scalar again)
-  const int G = gridDim.x;
-  const int g = xcd_remap((int)blockIdx.x, G);
-  const int T = a.sk_T;
-  long long u0 = 0, u1 = 0;
-  if (g < a.sk_G) {
-    u0 = sk_bound(a, g);
-    u1 = sk_bound(a, g + 1);
-  }
-  const int R0 = __builtin_amdgcn_readfirstlane((int)(u0 / T));
-  const int nsk = __builtin_amdgcn_readfirstlane(u1 > u0 ? (int)((u1 - 1) / T) - R0 + 1 : 0);
-  const int t00 = (int)(u0 - (long long)R0 * T);   // first key tile of row tile R0 in the range
-  const int t1l = __builtin_amdgcn_readfirstlane((int)(u1 - (long long)(R0 + nsk - 1) * T));   // end tile of the last
-  // the part of row tile R0 that this range takes when the row tile starts
-  // in an earlier range (later items start in this one: part 0 or whole)
-  const int part0 = __builtin_amdgcn_readfirstlane(t00 > 0 ? g - sk_range_of(a, (long long)R0 * T) : 0);
-  // rotated first key tile of that part (key tiles of a cut row tile run from
-  // its first inner range boundary, delta units in: t -> t - delta mod T)
-  int tb0 = t00;
-  if (t00 > 0) {
-    const long long base = (long long)R0 * T;
-    if (sk_bound(a, g - part0) != base) tb0 = t00 - (int)(sk_bound(a, g - part0 + 1) - base);
-  }
-  tb0 = __builtin_amdgcn_readfirstlane(tb0);
-  const int kdp = a.sk_K;
-  const int nr = kdp + nsk;
-
-  // part < 0: the whole row tile; else 8 Rs + part, Rs the row tile's index
-  // in the range phase (its partial buffer slot)
-  struct Item { int bh, rt, part, t_begin, nt; };
-  // (t_begin: the item's first key tile in rotated order; its nt key tiles
-  // follow it without wrapping)
-  auto item_of = [&](int r) -> Item {
-    int Ri, t0 = 0, t1 = T, tb = 0, part = -1;
-    if (r < kdp) {
-      Ri = sk_round_row(a, r, g);
-    } else {
-      const int q = r - kdp;
-      Ri = sk_rest_row(a, R0 + q);
-      if (q == 0) t0 = t00;
-      if (q == nsk - 1) t1 = t1l;
-      if (t0 > 0 || t1 < T) part = 8 * (R0 + q) + (q == 0 ? part0 : 0);
-      // a later item starts at its row tile's first unit, inside this range:
-      // the boundary is this range's end, t1 units in
-      tb = q == 0 ? tb0 : (t1 < T ? T - t1 : 0);
-    }
-    const int bh = Ri / a.row_tiles;
-    return Item{bh, Ri - bh * a.row_tiles, part, tb, t1 - t0};
-  };
+  // This workgroup's items: whole row tiles (the workgroups of an XCD take
+  // consecutive row tiles of its block), then the row tiles that its
+  // stream-K range meets (ranges of consecutive g on one XCD)
+  const SkItems sk = sk_items(a, xcd_remap((int)blockIdx.x, (int)gridDim.x));
+  const int nr = sk.kdp + sk.nsk;
+  typedef SkItem Item;
+  auto item_of = [&](int r) -> Item { return sk_item(a, sk, r); };
   // per item: each lane's query row and the head's valid key count
   for (int r = 0; r < nr; ++r) {
     const Item it = item_of(r);
@@ -1836,6 +1857,39 @@ static FlashArgs flash_args(const Layout& L, const Bufs& B) {
   return a;
 }
 
+// The full route (gather mode) on the stream-K split that the layout set:
+// a.sk_K rounds of whole row tiles on a grid of a.sk_R0 workgroups, then
+// a.sk_G ranges over the remaining row tiles' key tiles.
+template <int D, int KM, int RM>
+static hipError_t flash_launch_sk(FlashArgs a, int ntiles, long long BH, hipStream_t s) {
+  const long long R = (long long)a.row_tiles * BH, grid = a.sk_R0;
+  a.sk_R0 = (int)(grid * a.sk_K);
+  a.sk_grid = (int)grid;
+  a.sk_q = (int)(R / 8);
+  a.sk_x = (int)(R % 8);
+  a.sk_T = ntiles;
+  a.sk_U = (R - a.sk_R0) * ntiles;
+  if (grid <= 0 || grid % 8 != 0 || a.sk_K < 0 || a.sk_R0 > R || (a.sk_U > 0) != (a.sk_G > 0) || a.sk_U < a.sk_G ||
+      a.sk_P < 1 || a.sk_P > kMaxSplits)
+    return hipErrorInvalidValue;
+  const unsigned nwg = (unsigned)(a.sk_K > 0 ? grid : a.sk_G);
+  // persistent form, one workgroup per round slot and range, when a
+  // workgroup meets at most kPpsMaxItems row tiles and K and V share one row
+  // map
+  long long items = a.sk_K;
+  if (a.sk_G > 0) items += ((a.sk_U + a.sk_G - 1) / a.sk_G - 1 + ntiles - 1) / ntiles + 1;
+  if constexpr (D == 128) {
+    if (kUsePps && items <= kPpsMaxItems && a.rmk.sb == a.rmv.sb && a.rmk.sh == a.rmv.sh && a.rmk.sn == a.rmv.sn) {
+      hipLaunchKernelGGL(isa_flash_pps_kernel, dim3(nwg), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  // else the per-item kernel on the same grid, each workgroup's items one
+  // after the other (d = 64, or K and V with different row maps)
+  hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM, D>), dim3(nwg), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int KM, int RM, bool WO, bool WP>
 static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, long long BH, hipStream_t s) {
   a.n_rows = n_rows;
@@ -1845,38 +1899,15 @@ static hipError_t flash_launch(FlashArgs a, long long n_rows, long long keys, lo
   const long long nwg = (long long)a.row_tiles * BH * a.nsplit;
   if (nwg == 0) return hipSuccess;
   a.n_wg = (int)nwg;
-  if constexpr (D == 128 && KM != FK_POOLED && WO && !WP && kFlashWaves == 8) {
+  if constexpr ((D == 128 || D == 64) && KM != FK_POOLED && WO && !WP && kFlashWaves == 8) {
     if constexpr (KM == FK_GATHER && RM == FR_TABLE) {
-      // whole row tiles, then stream-K ranges, as the layout set them
-      // (a.sk_K rounds of grid workgroups, a.sk_G ranges)
-      const long long R = (long long)a.row_tiles * BH, grid = a.sk_R0;
-      a.sk_R0 = (int)(grid * a.sk_K);
-      a.sk_grid = (int)grid;
-      a.sk_q = (int)(R / 8);
-      a.sk_x = (int)(R % 8);
-      a.sk_T = ntiles;
-      a.sk_U = (R - a.sk_R0) * ntiles;
-      if (grid <= 0 || grid % 8 != 0 || a.sk_K < 0 || a.sk_R0 > R || (a.sk_U > 0) != (a.sk_G > 0) ||
-          a.sk_U < a.sk_G || a.sk_P < 1 || a.sk_P > kMaxSplits)
-        return hipErrorInvalidValue;
-      // persistent form, one workgroup per round slot and range, when a
-      // workgroup meets at most kPpsMaxItems row tiles and K and V share one
-      // row map
-      long long items = a.sk_K;
-      if (a.sk_G > 0) items += ((a.sk_U + a.sk_G - 1) / a.sk_G - 1 + ntiles - 1) / ntiles + 1;
-      if (kUsePps && items <= kPpsMaxItems && a.rmk.sb == a.rmv.sb && a.rmk.sh == a.rmv.sh &&
-          a.rmk.sn == a.rmv.sn) {
-        hipLaunchKernelGGL(isa_flash_pps_kernel, dim3((unsigned)(a.sk_K > 0 ? grid : a.sk_G)), dim3(512), 0, s, a);
-        return hipGetLastError();
-      }
-      // else one workgroup per item: whole row tile Ri < sk_R0, or part p of
-      // row tile sk_R0 + Rs as item sk_R0 + Rs * sk_P + p
-      a.n_wg = (int)(a.sk_R0 + (R - a.sk_R0) * a.sk_P);
-      hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM>), dim3((unsigned)a.n_wg), dim3(512), 0, s, a);
+      // (without the stream-K split -- d = 64 with few key tiles per
+      // workgroup -- isa_flash_kernel on full_splits equal parts, below)
+      if (a.sk_R0 > 0) return flash_launch_sk<D, KM, RM>(a, ntiles, BH, s);
+    } else {
+      hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM, D>), dim3((unsigned)nwg), dim3(512), 0, s, a);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((isa_flash_pp_kernel<KM, RM>), dim3((unsigned)nwg), dim3(512), 0, s, a);
-    return hipGetLastError();
   }
   hipLaunchKernelGGL((isa_flash_kernel<D, KM, RM, kFlashWaves, WO, WP>), dim3((unsigned)nwg),
                      dim3(kFlashWaves * 64), 0, s, a);
@@ -1907,7 +1938,7 @@ static hipError_t flash_t(const Layout& L, const Bufs& B, FlashWhat what, hipStr
                                                                 L.BH, s);
     case FlashWhat::kFullMerge: {
       // the stream-K split of the d = 128 ping-pong kernels, else full_splits equal parts
-      const bool sk = D == 128 && kFlashWaves == 8 && L.sk_grid > 0;
+      const bool sk = (D == 128 || D == 64) && kFlashWaves == 8 && L.sk_grid > 0;
       if ((sk ? L.sk_P : L.full_splits) <= 1 || L.full_rows == 0) return hipSuccess;
       a.q_list = (const int*)(B.ws + L.off_fullq);
       a.q_k = L.kq;

@@ -165,7 +165,7 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
     L->full_splits = L->es == 2 ? choose_splits(bh * row_tiles, ntiles) : 1;
     L->n_keytab = ntiles * kTileKeys;
     L->sk_grid = L->sk_rounds = L->sk_G = L->sk_P = 0;
-    if (L->es == 2 && D.d == 128 && row_tiles > 0) {
+    if (L->es == 2 && (D.d == 128 || D.d == 64) && row_tiles > 0) {
       // whole row tiles in at most 5 rounds of a multiple of the compute
       // unit count, the rest in ranges of equal length: at least
       // (T - 1) / (kMaxSplits - 1) units, so that a row tile of T units
@@ -187,7 +187,25 @@ isa_status make_layout(const isa_desc* desc, Layout* L) {
         L->sk_G = (int)Gs;
         L->sk_P = (int)((T - 1 + W - 1) / W + 1);
         if (L->sk_P > kMaxSplits) L->sk_P = kMaxSplits;   // (not reached: W >= wmin or Gs = 1)
+        // Or, when that costs less, every remaining row tile cut into P equal
+        // parts (rest * P ranges, aligned to the row tiles): a workgroup then
+        // runs ceil(T / P) key tiles as one item, against the longest range's
+        // key tiles and the items it meets.  Costs in key tiles, with
+        // kItemCost per item (its queries, first tiles and output).
+        const int64_t wmax = (U + Gs - 1) / Gs;
+        const int64_t cost_ranges = wmax + kItemCost * ((wmax - 1 + T - 1) / T + 1);
+        int64_t P = G / rest;
+        if (P > kMaxSplits) P = kMaxSplits;
+        if (P > T) P = T;
+        if ((T + P - 1) / P + kItemCost <= cost_ranges) {
+          L->sk_G = (int)(rest * P);
+          L->sk_P = (int)P;
+        }
       }
+      // d = 64 with few key tiles per workgroup: the first-design kernel,
+      // whose shorter start-up wins there, on full_splits equal parts
+      const int64_t per_wg = rounds * T + (rest > 0 ? (U + L->sk_G - 1) / L->sk_G : 0);
+      if (D.d == 64 && per_wg < kPpMinTiles64) L->sk_grid = L->sk_rounds = L->sk_G = L->sk_P = 0;
     }
   }
 

@@ -23,6 +23,8 @@ constexpr int kFlashPipe = ISA_FLASH_PIPE;      // issue S(j+1) before the softm
 constexpr int kFlashRows = 32 * kFlashWaves;    // query rows per full-attention workgroup
 constexpr int kCUs = 256;          // compute units of the target GPU (split-K balance)
 constexpr int kMaxSplits = 8;
+constexpr int kItemCost = 3;      // fixed cost of a full-route work item, in key tiles (split choice)
+constexpr int kPpMinTiles64 = 48;  // key tiles per workgroup from which d = 64 takes the ping-pong kernel
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxBH = 65535;            // B*H: grid-y of the per-head launches
 constexpr int64_t kMaxSpan = int64_t(1) << 31;   // bytes of one head of a tensor (32-bit offsets)
@@ -62,7 +64,8 @@ struct Layout {
   int64_t full_rows;   // kq*b virtual full-route query rows
   int64_t taylor_rows; // (nb_s-kq)*b virtual Taylor-route query rows
   int full_splits;     // key-range splits of the full-route attention: the FP8 variant, d = 64, the backward's dQ
-  // bf16 full route at d = 128, on sk_grid workgroups (0: off): row tiles
+  // bf16 full route (d = 128; d = 64 from kPpMinTiles64 key tiles per
+  // workgroup), on sk_grid workgroups (0: off, full_splits parts): row tiles
   // Ri = bh * row tiles + rt.  Workgroup g first takes whole row tiles
   // g, g + sk_grid, ... (sk_rounds of them, row tiles below sk_rounds *
   // sk_grid), then range g of the (row tile, key tile) units of the rest,

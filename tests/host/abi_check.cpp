@@ -42,7 +42,7 @@ static int count_rule(double f, int n) {
   return (int)std::min<double>(n, std::max<double>(0, c));
 }
 
-// The work split of the d = 128 bf16 full route: R row tiles of T key tiles;
+// The work split of the bf16 full route (d = 128 and 64): R row tiles of T key tiles;
 // workgroup g of sk_grid takes row tiles g, g + sk_grid, ... whole
 // (sk_rounds of them), then range g of the remaining row tiles' units
 // u = (Ri - sk_rounds sk_grid) T + t, range g covering [g U / G, (g + 1) U / G)
@@ -55,7 +55,8 @@ static int count_rule(double f, int n) {
 // sk_P rows.
 static void check_stream_k(const isa::Layout& L) {
   const int64_t R = (L.full_rows + isa::kFlashRows - 1) / isa::kFlashRows * L.BH;
-  const bool on = L.es == 2 && L.d == 128 && R > 0;
+  // (d = 64 may leave it off: full_splits equal parts on the first-design kernel)
+  const bool on = L.es == 2 && R > 0 && (L.d == 128 || (L.d == 64 && L.sk_grid > 0));
   CHECK(on ? L.sk_grid >= 1 && L.sk_rounds >= 0 && L.sk_P >= 1 && L.sk_P <= isa::kMaxSplits
            : L.sk_grid == 0 && L.sk_G == 0 && L.sk_P == 0);
   if (!on) return;

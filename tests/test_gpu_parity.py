@@ -184,12 +184,18 @@ SMALL = [
     (1, 2, 128, 500, 0, 32, 0.5, 0.3, "bf16"),        # no context at d = 128: the key-row table is the source rows
     (1, 2, 128, 700, 630, 50, 1.0, 0.5, "bf16"),      # short last context block kept; tiles straddle Ns and the gap
     # more row tiles than compute units: the persistent full-route kernel,
-    # one whole row tile per workgroup, then ranges of 10 or 11 key tiles
-    # over the last 64 row tiles (41 key tiles each: up to 5 parts)
+    # one whole row tile per workgroup, then the last 64 row tiles (41 key
+    # tiles each) in 4 equal parts
     (1, 40, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),
     (2, 32, 128, 2000, 1100, 64, 0.5, 1.0, "bf16"),   # 512 row tiles: two whole each, no range, lse written
-    (1, 8, 128, 1500, 1024, 32, 1.0, 1.0, "bf16"),    # 48 row tiles of 40 key tiles in 240 ranges of 8: five parts each
-    (1, 3, 128, 1595, 500, 64, 1.0, 1.0, "bf16"),     # 21 row tiles of 33 key tiles in 86 ranges: parts of 1 to 9 tiles
+    (1, 8, 128, 1500, 1024, 32, 1.0, 1.0, "bf16"),    # 48 row tiles of 40 key tiles, five equal parts each
+    (1, 3, 128, 1595, 500, 64, 1.0, 1.0, "bf16"),     # 21 row tiles of 33 key tiles, eight parts of 4 or 5 each
+    (1, 22, 128, 1000, 1100, 64, 0.5, 1.0, "bf16"),   # 88 row tiles of 25 key tiles in 256 ranges: parts of 1 to 9
+    # d = 64: the ping-pong kernel from 48 key tiles per workgroup (its items
+    # one after another), else equal parts on the first-design kernel
+    (1, 40, 64, 2000, 1100, 64, 0.5, 1.0, "bf16"),    # whole row tiles, then 4 equal parts
+    (1, 24, 64, 5500, 0, 64, 0.5, 0.25, "bf16"),      # 144 row tiles of 86 key tiles in 256 ranges
+    (1, 22, 64, 1000, 1100, 64, 0.5, 1.0, "bf16"),    # 9 key tiles per workgroup: first-design kernel
     (1, 2, 64, 400, 300, 1, 0.003, 0.997, "bf16"),    # k = 1 of 300 context blocks, k = n - 1 of 400 query blocks
     (1, 2, 64, 400, 300, 1, 0.995, 0.0025, "bf16"),   # k = n - 1 of 300, k = 1 of 400
 ]
