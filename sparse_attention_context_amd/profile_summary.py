@@ -102,10 +102,10 @@ def _labels(names):
             s = short_name(name)
             if s.startswith("isa_flash_pps_kernel"):
                 s = "isa_flash_pps_kernel full route"
-            elif s.startswith("isa_flash_pp_kernel<1,1>"):
-                s = "isa_flash_pp_kernel<1,1> full route"
-            elif s.startswith("isa_flash_pp_kernel<0,0>"):
-                s = "isa_flash_pp_kernel<0,0> dense"
+            elif s.startswith("isa_flash_pp_kernel<1,1,"):
+                s = s[:s.index(">") + 1] + " full route"
+            elif s.startswith("isa_flash_pp_kernel<0,0,"):
+                s = s[:s.index(">") + 1] + " dense"
             labels.append(s)
         elif "rocclr" in name:
             labels.append("runtime copy (input upload)")

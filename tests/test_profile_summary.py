@@ -12,7 +12,7 @@ from sparse_attention_context_amd import profile_summary as ps
 KERNELS = ["void at::native::elementwise_kernel<cast>(int)",
            "void isa::isa_pool_kernel<unsigned short, 128>(isa::PoolArgs)",
            "isa::isa_flash_pps_kernel(isa::FlashArgs)",
-           "void isa::isa_flash_pp_kernel<0, 0>(isa::FlashArgs)",
+           "void isa::isa_flash_pp_kernel<0, 0, 128>(isa::FlashArgs)",
            "void at::native::vectorized_elementwise_kernel<4, FillFunctor>(int)",
            "void at::native::vectorized_elementwise_kernel<4, MulFunctor>(int)"]
 
@@ -45,7 +45,7 @@ def test_counter_summary_labels_and_calibration(tmp_path):
     # HBM_MB = (2000 KiB * 2 + 60 KiB) * 1024 / 1e6; MFMA busy = 512 / (8 / 8 * 1024) = 50 %
     assert float(pps[2]) == pytest.approx((2000 * 2 + 60) * 1024 / 1e6, abs=0.05)
     assert float(pps[3]) == pytest.approx(50.0)
-    assert "isa_pool_kernel<bf16,128>" in rows and "isa_flash_pp_kernel<0,0> dense" in rows
+    assert "isa_pool_kernel<bf16,128>" in rows and "isa_flash_pp_kernel<0,0,128> dense" in rows
 
 
 def test_counter_runs_must_dispatch_the_same_kernels(tmp_path):
