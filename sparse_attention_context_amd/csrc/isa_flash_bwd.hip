@@ -97,7 +97,59 @@ struct BwdArgs {
   float* rdel;           //   D (0 for padding)
   int n_rowtab;
   long long delta_wgs;   // workgroups of the delta launch that cover the source rows
+  // full-route dK / dV at d = 128: the last round's kv_rest items cut into
+  // kv_parts ranges of query tiles (0: not cut), their partials in part_kv
+  int kv_rounds, kv_rest, kv_parts;
+  float* part_kv;        // [kv_rest * kv_parts][kBwdKeys][D]
 };
+
+// Work item of the full-route dK and dV kernels at d = 128: head bh, key
+// tile kt, query tiles q0 .. q0 + nq - 1 of the route.  Uncut (kv_parts = 0):
+// item lid = bh * key_tiles + kt, all query tiles.  Cut: the n_wg / 8
+// workgroups of XCD x (logical ids x L .., L = n_wg / 8) take 32 kv_rounds
+// whole items of their own (consecutive items: one head's key tiles) and
+// then their share of the parts of the last round's items, part p of item
+// kCUs kv_rounds + s covering query tiles [p Q / P, (p + 1) Q / P) and
+// writing partial slot s P + p (slot < 0: a whole item, written directly).
+struct KvItem { int bh, kt, q0, nq, slot; bool live; };
+__device__ __forceinline__ KvItem kv_item(const BwdArgs& a, int qtiles) {
+  KvItem it = {0, 0, 0, qtiles, -1, true};
+  const int lid = xcd_remap(blockIdx.x, a.n_wg);
+  int id = lid;
+  if (a.kv_parts > 0) {
+    const int L = a.n_wg >> 3, x = lid / L, i = lid - x * L, nw = (kCUs / 8) * a.kv_rounds;
+    if (i < nw) {
+      id = x * nw + i;
+    } else {
+      const int p_idx = x * (L - nw) + (i - nw);
+      if (p_idx >= a.kv_rest * a.kv_parts) {
+        it.live = false;   // padding of the XCD's share
+        return it;
+      }
+      const int sp = p_idx / a.kv_parts, p = p_idx - sp * a.kv_parts;
+      id = kCUs * a.kv_rounds + sp;
+      it.q0 = p * qtiles / a.kv_parts;
+      it.nq = (p + 1) * qtiles / a.kv_parts - it.q0;
+      it.slot = p_idx;
+    }
+  }
+  it.bh = id / a.key_tiles;
+  it.kt = id - it.bh * a.key_tiles;
+  return it;
+}
+
+// A part's raw sum over its query tiles (lane: key w*32 + l32 of the tile,
+// d = 32 t + 8 g + 4 h + e), for isa_bwd_kv_merge_kernel.
+template <int NT>
+__device__ __forceinline__ void kv_store_part(const BwdArgs& a, int slot, int w, int l32, int h, const f32x16* acc) {
+  constexpr int D = NT * 32;
+  float* pp = a.part_kv + ((long long)slot * kBwdKeys + w * 32 + l32) * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(pp + 32 * t + 8 * g + 4 * h) = f32x4{acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]};
+}
 
 // ---------------------------------------------------------------------------
 // D_i = dO_i . O_i, 8 elements per lane, D/8 lanes per row.
@@ -646,9 +698,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int bh = lid / a.key_tiles;
-  const int kt = lid - bh * a.key_tiles;
+  const KvItem item = kv_item(a, a.n_rowtab / BN);
+  if (!item.live) return;
+  const int bh = item.bh, kt = item.kt;
 
   // ---- this lane's key: row of K/V and validity (as isa_bwd_dkdv_kernel)
   const int kv = kt * kBwdKeys + w * 32 + l32;
@@ -666,12 +718,12 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
     for (int s = 0; s < D / 16; ++s) kB[s] = *(const Op*)(Kg + (16 * s + 8 * h) * ES);
   }
 
-  const int nt = a.n_rowtab / BN;   // row tiles of the route
+  const int nt = item.nq;   // row tiles of the route in the item, from item.q0
   const char* Qg = (const char*)a.Q + rm_head(a.rmq, bh) * 2;
   const char* Gg = (const char*)a.dO + rm_head(a.rmo, bh) * 2;
   const unsigned qrs = (unsigned)a.rmq.sn * 2u, grs = (unsigned)a.rmo.sn * 2u;   // row steps in bytes
-  const int* tab = a.rrow + (long long)bh * a.n_rowtab;
-  const float* lseg = a.rlse + (long long)bh * a.n_rowtab;
+  const int* tab = a.rrow + (long long)bh * a.n_rowtab + item.q0 * BN;
+  const float* lseg = a.rlse + (long long)bh * a.n_rowtab + item.q0 * BN;
 
   // This wave loads rows 32*grp + 8*wg + 4*i + lane/16 (i = 0, 1) of each
   // tile; the row-table entries of its 8 rows of tile t come to slot t % 4 of
@@ -838,7 +890,12 @@ __global__ __launch_bounds__(512) void isa_bwd_dv_pp_kernel(BwdArgs a) {
   }
 
   // ---- epilogue: dV of the key plus the pooled share of its block (as
-  // isa_bwd_dkdv_kernel); lane holds key kv, d = 32 t + 8 g + 4 h + e
+  // isa_bwd_dkdv_kernel); lane holds key kv, d = 32 t + 8 g + 4 h + e.  A
+  // part of a cut item leaves its raw sum to the merge.
+  if (item.slot >= 0) {
+    kv_store_part<NT>(a, item.slot, w, l32, h, acc);
+    return;
+  }
   if (!kvalid) return;
   int j, n;
   if (kv < a.Ns) {
@@ -890,9 +947,9 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int bh = lid / a.key_tiles;
-  const int kt = lid - bh * a.key_tiles;
+  const KvItem item = kv_item(a, a.n_rowtab / BN);
+  if (!item.live) return;
+  const int bh = item.bh, kt = item.kt;
 
   // ---- this lane's key (as isa_bwd_dkdv_kernel)
   const int kv = kt * kBwdKeys + w * 32 + l32;
@@ -914,13 +971,13 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
     }
   }
 
-  const int nt = a.n_rowtab / BN;
+  const int nt = item.nq;   // row tiles of the route in the item, from item.q0
   const char* Qg = (const char*)a.Q + rm_head(a.rmq, bh) * 2;
   const char* Gg = (const char*)a.dO + rm_head(a.rmo, bh) * 2;
   const unsigned qrs = (unsigned)a.rmq.sn * 2u, grs = (unsigned)a.rmo.sn * 2u;   // row steps in bytes
-  const int* tab = a.rrow + (long long)bh * a.n_rowtab;
-  const float* lseg = a.rlse + (long long)bh * a.n_rowtab;
-  const float* delg = a.rdel + (long long)bh * a.n_rowtab;
+  const int* tab = a.rrow + (long long)bh * a.n_rowtab + item.q0 * BN;
+  const float* lseg = a.rlse + (long long)bh * a.n_rowtab + item.q0 * BN;
+  const float* delg = a.rdel + (long long)bh * a.n_rowtab + item.q0 * BN;
 
   const int lrow0 = 32 * grp + 8 * wg + (lane >> 4);
   struct Rows { int r[2]; };
@@ -1096,7 +1153,12 @@ __global__ __launch_bounds__(512) void isa_bwd_dk_pp_kernel(BwdArgs a) {
   }
 
   // ---- epilogue: dK of the key (scaled by 1/sqrt d) plus the pooled share
-  // of its block (as isa_bwd_dkdv_kernel); lane holds key kv, d = 32 t + 8 g + 4 h + e
+  // of its block (as isa_bwd_dkdv_kernel); lane holds key kv, d = 32 t + 8 g + 4 h + e.
+  // A part of a cut item leaves its raw sum to the merge.
+  if (item.slot >= 0) {
+    kv_store_part<NT>(a, item.slot, w, l32, h, acc);
+    return;
+  }
   if (!kvalid) return;
   int j, n;
   if (kv < a.Ns) {
@@ -1377,6 +1439,49 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
   }
 }
 
+// dK (DK) or dV of the keys of the cut items of the full-route dK / dV
+// kernels: the sum of their parts in part order, then those kernels'
+// epilogue (dK scaled by 1/sqrt d, plus the pooled share of the key's block,
+// in bf16).  Four d per thread, D / 4 threads per key.
+template <bool DK>
+__global__ __launch_bounds__(256) void isa_bwd_kv_merge_kernel(BwdArgs a) {
+  constexpr int D = 128, TPR = D / 4, RPB = 256 / TPR;
+  const long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;   // key of the cut items
+  const int e = (threadIdx.x % TPR) * 4;
+  if (gid >= (long long)a.kv_rest * kBwdKeys) return;
+  const int sp = (int)(gid / kBwdKeys), r = (int)(gid - (long long)sp * kBwdKeys);
+  const int id = kCUs * a.kv_rounds + sp;
+  const int bh = id / a.key_tiles, kt = id - bh * a.key_tiles;
+  const int kv = kt * kBwdKeys + r;
+  const int n_keys = a.Ns + (int)a.ctx_tok;
+  int krow;
+  if (kv < a.Ns) krow = kv;
+  else if (kv < n_keys) krow = a.ctx_rows[(long long)bh * a.ctx_tok + (kv - a.Ns)];
+  else krow = -1;
+  if (krow < 0) return;
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.kv_parts; ++p)
+    sum += *(const f32x4*)(a.part_kv + ((long long)(sp * a.kv_parts + p) * kBwdKeys + r) * D + e);
+  int j, n;
+  if (kv < a.Ns) {
+    j = kv / a.b;
+    n = j == a.nb_s - 1 ? a.tail_s : a.b;
+  } else {
+    const int u = (kv - a.Ns) / a.b;
+    j = a.nb_s + u;
+    n = a.kept[(long long)bh * a.kc + u] == a.nb_c - 1 ? a.tail_c : a.b;
+  }
+  const float inv_n = 1.0f / (float)n;
+  const f32x4 bb = *(const f32x4*)(a.dkvbar + ((long long)bh * a.mk_pad + j) * 2 * D + (DK ? 0 : D) + e);
+  const float sd = DK ? a.inv_sqrt_d : 1.0f;
+  f32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = fmaf(sum[i], sd, bb[i] * inv_n);
+  bf16_t* out = DK ? (bf16_t*)a.dK + rm_head(a.rmk, bh) + (long long)krow * a.rmk.sn
+                   : (bf16_t*)a.dV + rm_head(a.rmv, bh) + (long long)krow * a.rmv.sn;
+  *(u32x2*)(out + e) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
 // dkbar, dvbar = sum of the pooled partials over splits, in split order
 // (zero when there are no Taylor rows: nsplit = 0).
 template <int D>
@@ -1431,6 +1536,7 @@ static BwdArgs bwd_args(const Layout& L, const BwdLayout& W, const BwdBufs& B) {
   a.mk = L.mk; a.mk_pad = L.mk_pad;
   a.nb_s = L.nb_s;
   a.part_dq = (float*)(B.bws + W.off_part_dq);
+  a.part_kv = (float*)(B.bws + W.off_part_kv);
   a.part_dkv = (float*)(B.bws + W.off_part_dkv);
   a.dkvbar = (float*)(B.bws + W.off_dkvbar);
   a.nsplit = 1;
@@ -1486,16 +1592,33 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
     case BwdWhat::kDvFull: {
       a.q_list = fullq; a.q_k = L.kq; a.n_rows = L.full_rows;
       a.key_tiles = (int)((L.Ns + L.ctx_tok + kBwdKeys - 1) / kBwdKeys);
-      const long long nwg = L.BH * a.key_tiles;
+      long long nwg = L.BH * a.key_tiles;
+      const bool dk = what == BwdWhat::kDkFull;
+      // the ping-pong kernels cut the last, part-filled round (W.kv_parts)
+      const bool pp = D == 128 && (dk ? kUseDkPP : kUseDvPP);
+      const bool cut = pp && W.kv_parts > 0;
+      if (cut) {
+        if ((long long)kCUs * W.kv_rounds + W.kv_rest != nwg) return hipErrorInvalidValue;
+        a.kv_rounds = W.kv_rounds;
+        a.kv_rest = W.kv_rest;
+        a.kv_parts = W.kv_parts;
+        nwg = 8 * ((long long)(kCUs / 8) * W.kv_rounds + ((long long)W.kv_rest * W.kv_parts + 7) / 8);
+      }
       a.n_wg = (int)nwg;
-      if (what == BwdWhat::kDkFull && D == 128 && kUseDkPP)
+      if (dk && pp)
         hipLaunchKernelGGL(isa_bwd_dk_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
-      else if (what == BwdWhat::kDkFull)
+      else if (dk)
         hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, true>), dim3((unsigned)nwg), dim3(512), 0, s, a);
-      else if (D == 128 && kUseDvPP)
+      else if (pp)
         hipLaunchKernelGGL(isa_bwd_dv_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
       else
         hipLaunchKernelGGL((isa_bwd_dkdv_kernel<D, false, false>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+      if (cut) {
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        const unsigned mg = (unsigned)((long long)W.kv_rest * kBwdKeys / (256 / (128 / 4)));
+        if (dk) hipLaunchKernelGGL(isa_bwd_kv_merge_kernel<true>, dim3(mg), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(isa_bwd_kv_merge_kernel<false>, dim3(mg), dim3(256), 0, s, a);
+      }
       break;
     }
     case BwdWhat::kZeroPruned: {

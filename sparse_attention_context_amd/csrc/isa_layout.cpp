@@ -276,6 +276,19 @@ isa_status make_bwd_layout(const Layout& L, BwdLayout* B) {
     take(&B->off_part_dq, prow * d * 4);
   }
   B->n_rowtab = (int)((L.full_rows + 63) / 64 * 64);
+  {
+    // the last round of the d = 128 full-route dK/dV items, when at most
+    // half full, cut along the query tiles so that it fills the compute units
+    const int64_t items = (int64_t)bh * ((L.Ns + L.ctx_tok + kBwdKeys - 1) / kBwdKeys);
+    const int64_t qtiles = B->n_rowtab / 64;
+    B->kv_rounds = (int)(items / kCUs);
+    B->kv_rest = (int)(items % kCUs);
+    int64_t P = B->kv_rest > 0 ? kCUs / B->kv_rest : 0;
+    if (P > kBwdMaxParts) P = kBwdMaxParts;
+    if (P > qtiles) P = qtiles;
+    B->kv_parts = (L.d == 128 && P >= 2) ? (int)P : 0;
+    take(&B->off_part_kv, (size_t)(B->kv_parts ? B->kv_rest * B->kv_parts : 0) * kBwdKeys * d * 4);
+  }
   take(&B->off_rrow, bh * (size_t)B->n_rowtab * 4);
   take(&B->off_rlse, bh * (size_t)B->n_rowtab * 4);
   take(&B->off_rdel, bh * (size_t)B->n_rowtab * 4);

@@ -106,6 +106,7 @@ isa_status check_workspace(const void* ws, size_t bytes, size_t need);
 // rows staged per step.
 constexpr int kBwdKeys = 256;
 constexpr int kBwdRows = 64;
+constexpr int kBwdMaxParts = 16;   // parts of a split key tile of the last dK/dV round
 
 struct BwdLayout {
   int dkv_splits;      // query-row splits of the pooled (Taylor) dK/dV pass
@@ -115,6 +116,12 @@ struct BwdLayout {
   size_t off_part_dkv; // [dkv_splits][BH][mk_pad][2][d] fp32 pooled-key gradient partials
   size_t off_dkvbar;   // [BH][mk_pad][2][d] fp32: pooled-key gradients (dkbar, dvbar)
   size_t off_part_dq;  // [BH][full row tiles * kFlashRows][full_splits][d] fp32 split-K partials of dQ
+  // Full-route dK and dV at d = 128 (item = head x 256-key tile, all the
+  // route's query tiles): the items past kv_rounds * kCUs are the last,
+  // part-filled round; with kv_parts > 1 each of them is cut into kv_parts
+  // ranges of query tiles, one workgroup each, their fp32 partials merged.
+  int kv_rounds, kv_rest, kv_parts;
+  size_t off_part_kv;  // [kv_rest * kv_parts][kBwdKeys][d] fp32 partials (dK, then dV)
   int n_rowtab;        // full-route virtual rows per head, rounded up to 64
   size_t off_rrow;     // [BH][n_rowtab] int32: source row of each full-route row (0 for padding)
   size_t off_rlse;     // [BH][n_rowtab] fp32: its forward log-sum-exp (+inf for padding)

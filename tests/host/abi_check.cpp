@@ -142,6 +142,13 @@ static void check_layout(const isa::Layout& L, const isa_desc& D) {
   if (isa::make_bwd_layout(L, &W) == ISA_OK) {
     CHECK(W.total % isa::kWsAlign == 0 && W.off_rdel < W.total);
     CHECK(W.dkv_splits >= 1 && W.dkv_splits <= 64);
+    // the last round of the full-route dK/dV items: cut only when at most
+    // half full, into at most kBwdMaxParts ranges of at least one query tile
+    const int64_t items = (int64_t)L.BH * ((L.Ns + L.ctx_tok + isa::kBwdKeys - 1) / isa::kBwdKeys);
+    CHECK((int64_t)W.kv_rounds * isa::kCUs + W.kv_rest == items);
+    CHECK(W.kv_parts == 0 || (W.kv_parts >= 2 && W.kv_parts <= isa::kBwdMaxParts && L.d == 128 &&
+                              (int64_t)W.kv_rest * W.kv_parts <= isa::kCUs && W.kv_parts <= W.n_rowtab / 64));
+    CHECK(W.off_rrow - W.off_part_kv >= (size_t)W.kv_rest * W.kv_parts * isa::kBwdKeys * L.d * 4);
   }
   isa::Fp8Layout F;
   if (isa::make_fp8_layout(L, &F) == ISA_OK) CHECK(F.nkp % 64 == 0 && F.off_vs < F.total);
