@@ -226,7 +226,8 @@ typedef enum isa_bwd_stage {
   ISA_BWD_DV_POOLED = 2,    /* Taylor rows: per-split partial gradients of the kept pooled values */
   ISA_BWD_DKV_REDUCE = 3,   /* sums those partials in split order (zero without Taylor rows) */
   ISA_BWD_DK_FULL = 4,      /* full rows: dK of every source and kept context row, plus the pooled
-                               share of its block */
+                               share of its block (d = 128: a part-filled last round of key tiles is
+                               cut into query-tile parts, merged within the stage) */
   ISA_BWD_DV_FULL = 5,      /* the same for dV */
   ISA_BWD_ZERO_PRUNED = 6,  /* zeroes dK, dV rows of pruned context blocks */
   ISA_BWD_DQ_FULL = 7,      /* full rows: dQ, or split partials when the key range is split */
