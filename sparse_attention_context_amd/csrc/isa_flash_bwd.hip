@@ -101,6 +101,9 @@ struct BwdArgs {
   // kv_parts ranges of query tiles (0: not cut), their partials in part_kv
   int kv_rounds, kv_rest, kv_parts;
   float* part_kv;        // [kv_rest * kv_parts][kBwdKeys][D]
+  // full-route dQ at d = 128: the same cut of its last round of row tiles
+  // into dq_parts key ranges (partials [dq_rest * dq_parts][256][D] in part_dq)
+  int dq_rounds, dq_rest, dq_parts;
 };
 
 // Work item of the full-route dK and dV kernels at d = 128: head bh, key
@@ -111,31 +114,37 @@ struct BwdArgs {
 // then their share of the parts of the last round's items, part p of item
 // kCUs kv_rounds + s covering query tiles [p Q / P, (p + 1) Q / P) and
 // writing partial slot s P + p (slot < 0: a whole item, written directly).
-struct KvItem { int bh, kt, q0, nq, slot; bool live; };
-__device__ __forceinline__ KvItem kv_item(const BwdArgs& a, int qtiles) {
-  KvItem it = {0, 0, 0, qtiles, -1, true};
-  const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  int id = lid;
-  if (a.kv_parts > 0) {
-    const int L = a.n_wg >> 3, x = lid / L, i = lid - x * L, nw = (kCUs / 8) * a.kv_rounds;
+// (The cut in general: item id of `rounds` whole rounds of kCUs, then part p
+// of item kCUs rounds + s, covering [p span / parts, (p + 1) span / parts).)
+struct CutItem { int id, r0, n, slot; bool live; };
+__device__ __forceinline__ CutItem cut_item(int n_wg, int rounds, int rest, int parts, int span) {
+  CutItem it = {0, 0, span, -1, true};
+  const int lid = xcd_remap(blockIdx.x, n_wg);
+  it.id = lid;
+  if (parts > 0) {
+    const int L = n_wg >> 3, x = lid / L, i = lid - x * L, nw = (kCUs / 8) * rounds;
     if (i < nw) {
-      id = x * nw + i;
+      it.id = x * nw + i;
     } else {
       const int p_idx = x * (L - nw) + (i - nw);
-      if (p_idx >= a.kv_rest * a.kv_parts) {
+      if (p_idx >= rest * parts) {
         it.live = false;   // padding of the XCD's share
         return it;
       }
-      const int sp = p_idx / a.kv_parts, p = p_idx - sp * a.kv_parts;
-      id = kCUs * a.kv_rounds + sp;
-      it.q0 = p * qtiles / a.kv_parts;
-      it.nq = (p + 1) * qtiles / a.kv_parts - it.q0;
+      const int sp = p_idx / parts, p = p_idx - sp * parts;
+      it.id = kCUs * rounds + sp;
+      it.r0 = p * span / parts;
+      it.n = (p + 1) * span / parts - it.r0;
       it.slot = p_idx;
     }
   }
-  it.bh = id / a.key_tiles;
-  it.kt = id - it.bh * a.key_tiles;
   return it;
+}
+struct KvItem { int bh, kt, q0, nq, slot; bool live; };
+__device__ __forceinline__ KvItem kv_item(const BwdArgs& a, int qtiles) {
+  const CutItem c = cut_item(a.n_wg, a.kv_rounds, a.kv_rest, a.kv_parts, qtiles);
+  const int bh = c.id / a.key_tiles;
+  return KvItem{bh, c.id - bh * a.key_tiles, c.r0, c.n, c.slot, c.live};
 }
 
 // A part's raw sum over its query tiles (lane: key w*32 + l32 of the tile,
@@ -414,12 +423,28 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// dQ of full-route rows from the split partials, summed in split order.
+// dQ of full-route rows from the split partials, summed in split order:
+// every row tile's full_splits parts (d = 64), or the dq_parts parts of the
+// cut row tiles of the last round (dq_parts > 0: the launch covers their rows).
 template <int D>
 __global__ __launch_bounds__(256) void isa_bwd_dq_merge_kernel(BwdArgs a) {
   constexpr int TPR = D / 4, RPB = 256 / TPR;
-  const long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  long long gid = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int e = (threadIdx.x % TPR) * 4;
+  long long prow, pstep;   // partial rows prow + k pstep
+  int np;
+  if (a.dq_parts > 0) {
+    const long long sp = gid / kFlashRows, r = gid - sp * kFlashRows;
+    if (sp >= a.dq_rest) return;
+    prow = sp * a.dq_parts * kFlashRows + r;
+    pstep = kFlashRows;
+    np = a.dq_parts;
+    gid = ((long long)kCUs * a.dq_rounds + sp) * kFlashRows + r;   // the row tile's rows
+  } else {
+    prow = gid * a.nsplit;
+    pstep = 1;
+    np = a.nsplit;
+  }
   const long long rows_head = (long long)a.row_tiles * kFlashRows;
   const long long bh = gid / rows_head;
   const long long vrow = gid - bh * rows_head;
@@ -427,7 +452,7 @@ __global__ __launch_bounds__(256) void isa_bwd_dq_merge_kernel(BwdArgs a) {
   const int qrow = route_row(a.q_list + bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
   if (qrow < 0) return;
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < a.nsplit; ++k) s += *(const f32x4*)(a.part_dq + (gid * a.nsplit + k) * D + e);
+  for (int k = 0; k < np; ++k) s += *(const f32x4*)(a.part_dq + (prow + k * pstep) * D + e);
   s *= a.inv_sqrt_d;
   *(u32x2*)((bf16_t*)a.dQ + rm_head(a.rmq, bh) + (long long)qrow * a.rmq.sn + e) =
       u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
@@ -1211,14 +1236,16 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  // work item lid: row tile fastest, then key split, then head (as the
-  // forward flash kernels), so that the workgroups running at once on an XCD
-  // share one K/V range in its L2
-  const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int rt = lid % a.row_tiles;
-  const int rest = lid / a.row_tiles;
-  const int split = rest % a.nsplit;
-  const int bh = rest / a.nsplit;
+  // Work item (head bh, row tile rt) over all key tiles, or, in the cut last
+  // round, over the key range of its part (cut_item: an XCD's workgroups take
+  // whole row tiles of their own, consecutive row tiles of a head sharing its
+  // K/V in L2, then their share of the parts)
+  const int n_keys = a.Ns + (int)a.ctx_tok;
+  const int ntiles = (n_keys + BN - 1) / BN;
+  const CutItem item = cut_item(a.n_wg, a.dq_rounds, a.dq_rest, a.dq_parts, ntiles);
+  if (!item.live) return;
+  const int bh = item.id / a.row_tiles;
+  const int rt = item.id - bh * a.row_tiles;
 
   const long long vrow = (long long)rt * BM + w * 32 + l32;
   const int qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
@@ -1240,12 +1267,10 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
     }
   }
 
-  const int n_keys = a.Ns + (int)a.ctx_tok;
   const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
   const int n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
-  const int ntiles = (n_keys + BN - 1) / BN;
-  const int t_begin = split * a.tiles_per_split;
-  const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
+  const int t_begin = item.r0;
+  const int nt = item.n;
 
   const char* Kg = (const char*)a.K + rm_head(a.rmk, bh) * 2;
   const char* Vg = (const char*)a.V + rm_head(a.rmv, bh) * 2;
@@ -1414,9 +1439,11 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
     if (grp == 0) phase_barrier();   // balances group 1's extra barrier
   }
 
-  // ---- epilogue (as isa_bwd_dq_kernel)
-  if (qrow < 0 && a.nsplit == 1) return;
-  if (a.nsplit == 1) {
+  // ---- epilogue (as isa_bwd_dq_kernel): dQ of a whole row tile, or the raw
+  // sum of a part of a cut one ([slot][256 rows][D], merged by
+  // isa_bwd_dq_merge_kernel)
+  if (qrow < 0 && item.slot < 0) return;
+  if (item.slot < 0) {
     bf16_t* op = (bf16_t*)a.dQ + rm_head(a.rmq, bh) + (long long)qrow * a.rmq.sn;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -1428,7 +1455,7 @@ __global__ __launch_bounds__(512) void isa_bwd_dq_pp_kernel(BwdArgs a) {
                                                        pack_bf16x2(c[4 * g + 2] * sd, c[4 * g + 3] * sd)};
       }
   } else {
-    float* pp = a.part_dq + (((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split) * D;
+    float* pp = a.part_dq + ((long long)item.slot * BM + w * 32 + l32) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1639,9 +1666,20 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       const long long keys = full ? (long long)L.Ns + L.ctx_tok : (long long)L.mk_pad;
       const int ntiles = (int)((keys + 63) / 64);
       a.tiles_per_split = (ntiles + a.nsplit - 1) / a.nsplit;
-      const long long nwg = (long long)a.row_tiles * L.BH * a.nsplit;
+      long long nwg = (long long)a.row_tiles * L.BH * a.nsplit;
+      const bool pp = full && D == 128 && kUseDqPP;
+      if (pp) {
+        // whole row tiles, the part-filled last round cut into W.dq_parts key ranges
+        const long long items = (long long)a.row_tiles * L.BH;
+        if ((long long)kCUs * W.dq_rounds + W.dq_rest != items) return hipErrorInvalidValue;
+        a.dq_rounds = W.dq_rounds;
+        a.dq_rest = W.dq_rest;
+        a.dq_parts = W.dq_parts;
+        nwg = W.dq_parts > 0 ? 8 * ((long long)(kCUs / 8) * W.dq_rounds + ((long long)W.dq_rest * W.dq_parts + 7) / 8)
+                             : items;
+      }
       a.n_wg = (int)nwg;
-      if (full && D == 128 && kUseDqPP)
+      if (pp)
         hipLaunchKernelGGL(isa_bwd_dq_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
       else if (full)
         hipLaunchKernelGGL((isa_bwd_dq_kernel<D, false>), dim3((unsigned)nwg), dim3(512), 0, s, a);
@@ -1650,12 +1688,19 @@ static hipError_t bwd_t(const Layout& L, const BwdLayout& W, const BwdBufs& B, B
       break;
     }
     case BwdWhat::kDqMerge: {
-      if (L.full_rows == 0 || L.full_splits <= 1) return hipSuccess;
+      const bool pp = D == 128 && kUseDqPP;   // (as kDqFull)
+      if (L.full_rows == 0 || (pp ? W.dq_parts == 0 : L.full_splits <= 1)) return hipSuccess;
       a.q_list = fullq; a.q_k = L.kq; a.n_rows = L.full_rows;
       a.nsplit = L.full_splits;
       a.row_tiles = (int)((L.full_rows + kFlashRows - 1) / kFlashRows);
       constexpr int RPB = 256 / (D / 4);
-      const long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
+      long long rows = (long long)a.row_tiles * kFlashRows * L.BH;
+      if (pp) {
+        a.dq_rounds = W.dq_rounds;
+        a.dq_rest = W.dq_rest;
+        a.dq_parts = W.dq_parts;
+        rows = (long long)W.dq_rest * kFlashRows;
+      }
       hipLaunchKernelGGL((isa_bwd_dq_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
       break;
     }

@@ -272,7 +272,22 @@ isa_status make_bwd_layout(const Layout& L, BwdLayout* B) {
   take(&B->off_part_dkv, (size_t)B->dkv_splits * bh * L.mk_pad * 2 * d * 4);
   take(&B->off_dkvbar, bh * L.mk_pad * 2 * d * 4);
   {
-    const int64_t prow = L.full_splits > 1 ? (int64_t)bh * ((L.full_rows + kFlashRows - 1) / kFlashRows) * kFlashRows * L.full_splits : 0;
+    // dQ partials: d = 64 splits every row tile into full_splits key ranges;
+    // d = 128 cuts only the row tiles of a part-filled last round, into
+    // dq_parts key ranges
+    const int64_t row_tiles = (L.full_rows + kFlashRows - 1) / kFlashRows;
+    const int64_t items = (int64_t)bh * row_tiles, ktiles = (L.Ns + L.ctx_tok + 63) / 64;
+    B->dq_rounds = (int)(items / kCUs);
+    B->dq_rest = (int)(items % kCUs);
+    int64_t P = B->dq_rest > 0 ? kCUs / B->dq_rest : 0;
+    if (P > kMaxSplits) P = kMaxSplits;
+    if (P > ktiles) P = ktiles;
+    B->dq_parts = (L.d == 128 && P >= 2) ? (int)P : 0;
+    // (room for both: a build without the d = 128 ping-pong dQ kernel splits
+    // every row tile)
+    int64_t prow = L.full_splits > 1 ? (int64_t)bh * row_tiles * kFlashRows * L.full_splits : 0;
+    const int64_t prow_cut = B->dq_parts ? (int64_t)B->dq_rest * B->dq_parts * kFlashRows : 0;
+    if (prow_cut > prow) prow = prow_cut;
     take(&B->off_part_dq, prow * d * 4);
   }
   B->n_rowtab = (int)((L.full_rows + 63) / 64 * 64);

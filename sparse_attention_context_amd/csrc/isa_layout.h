@@ -122,6 +122,10 @@ struct BwdLayout {
   // ranges of query tiles, one workgroup each, their fp32 partials merged.
   int kv_rounds, kv_rest, kv_parts;
   size_t off_part_kv;  // [kv_rest * kv_parts][kBwdKeys][d] fp32 partials (dK, then dV)
+  // Full-route dQ at d = 128 (item = head x 256-row tile, all key tiles):
+  // the same cut of its last round into dq_parts key ranges (0: not cut; the
+  // partials then take off_part_dq as [dq_rest * dq_parts][kFlashRows][d]).
+  int dq_rounds, dq_rest, dq_parts;
   int n_rowtab;        // full-route virtual rows per head, rounded up to 64
   size_t off_rrow;     // [BH][n_rowtab] int32: source row of each full-route row (0 for padding)
   size_t off_rlse;     // [BH][n_rowtab] fp32: its forward log-sum-exp (+inf for padding)

@@ -149,6 +149,12 @@ static void check_layout(const isa::Layout& L, const isa_desc& D) {
     CHECK(W.kv_parts == 0 || (W.kv_parts >= 2 && W.kv_parts <= isa::kBwdMaxParts && L.d == 128 &&
                               (int64_t)W.kv_rest * W.kv_parts <= isa::kCUs && W.kv_parts <= W.n_rowtab / 64));
     CHECK(W.off_rrow - W.off_part_kv >= (size_t)W.kv_rest * W.kv_parts * isa::kBwdKeys * L.d * 4);
+    // the dQ cut of the last round of row tiles, and room for its partials
+    const int64_t rtiles = (int64_t)L.BH * ((L.full_rows + isa::kFlashRows - 1) / isa::kFlashRows);
+    CHECK((int64_t)W.dq_rounds * isa::kCUs + W.dq_rest == rtiles);
+    CHECK(W.dq_parts == 0 || (W.dq_parts >= 2 && W.dq_parts <= isa::kMaxSplits && L.d == 128 &&
+                              (int64_t)W.dq_rest * W.dq_parts <= isa::kCUs));
+    CHECK(W.off_part_kv - W.off_part_dq >= (size_t)W.dq_rest * W.dq_parts * isa::kFlashRows * L.d * 4);
   }
   isa::Fp8Layout F;
   if (isa::make_fp8_layout(L, &F) == ISA_OK) CHECK(F.nkp % 64 == 0 && F.off_vs < F.total);
