@@ -43,10 +43,12 @@
 // bf16 probabilities.  The true running max is tracked separately for the
 // peak probability.
 //
-// Full-route key ranges over few row tiles are split across workgroups
-// (split-K); each split writes its own normalised output in bf16 with its
-// reference max and sum in fp32, and the merge kernel takes the sum-weighted
-// mean of the splits in split order (deterministic).
+// The full route's key ranges are split across workgroups: on the ping-pong
+// kernels by the stream-K split below (whole row tiles, then equal ranges),
+// on isa_flash_kernel (short d = 64 work) into nsplit equal parts.  Each
+// part writes its own normalised output in bf16 with its reference max and
+// sum in fp32, and the merge kernel takes the sum-weighted mean of a row's
+// parts in part order (deterministic).
 #include "isa_device.h"
 #include "isa_kernels.h"
 
@@ -95,8 +97,11 @@ struct FlashArgs {
   long long n_rows;     // virtual query rows per head
   float* peak;          // pooled: [BH][Ns]
   float* lse;           // [BH][Ns] log2-domain log-sum-exp of each written row (null: not kept)
-  bf16_t* part_o;       // split-K: [BH][row_tiles*BM][nsplit][D] normalised split outputs
-  float* part_ml;       // split-K: [BH][row_tiles*BM][nsplit][2]
+  // split partials: [BH][row_tiles*BM][nsplit][D] normalised outputs and
+  // [..][2] (max, sum) for the equal splits; [Rs][sk_P][BM][..] for the
+  // stream-K split's cut row tiles
+  bf16_t* part_o;
+  float* part_ml;
   int nsplit, tiles_per_split;
   int Ns, Nk;
   int row_tiles;
@@ -1759,7 +1764,7 @@ __global__ __launch_bounds__(512) void isa_flash_pp_pooled_kernel(FlashArgs a) {
   }
 }
 
-// Merges the split-K partials of each full-route query row, in split order.
+// Merges the split partials of each full-route query row, in part order.
 template <int D>
 __global__ __launch_bounds__(256) void isa_flash_merge_kernel(FlashArgs a) {
   constexpr int TPR = D / 8;           // threads per row, 8 elements each
