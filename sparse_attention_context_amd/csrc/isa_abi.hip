@@ -131,9 +131,10 @@ isa_status fp8_prepare(const isa_desc* desc, const void* Q, const void* K, const
                        isa::Fp8Layout* F) {
   isa_status st = isa::make_layout(desc, L);
   if (st != ISA_OK) return st;
-  // the FP8 full route splits every row tile's keys into full_splits equal
-  // parts (the workspace holds room for either split)
-  L->sk_grid = L->sk_rounds = L->sk_G = L->sk_P = 0;
+  // the FP8 full route at d = 128 takes the bf16 route's stream-K split; at
+  // d = 64 it splits every row tile's keys into full_splits equal parts (the
+  // workspace holds room for either split)
+  if (L->d != 128) L->sk_grid = L->sk_rounds = L->sk_G = L->sk_P = 0;
   if ((st = isa::make_fp8_layout(*L, F)) != ISA_OK) return st;
   if ((st = check_io(Q, K, V, O, true)) != ISA_OK) return st;
   if ((st = check_ws(*L, ws, ws_bytes)) != ISA_OK) return st;

@@ -28,6 +28,7 @@
 //   split-K partials merged by the bf16 merge kernel).
 #include "isa_device.h"
 #include "isa_kernels.h"
+#include "isa_split.h"
 
 namespace isa {
 
@@ -91,6 +92,9 @@ struct Fp8Args {
   int row_tiles;
   int n_wg;
   float scale_log2;      // log2(e)/sqrt(d)
+  // d = 128: the stream-K split of the bf16 full route (isa_split.h)
+  long long sk_U;
+  int sk_G, sk_P, sk_T, sk_R0, sk_K, sk_grid, sk_q, sk_x;
 };
 
 // ---------------------------------------------------------------------------
@@ -450,271 +454,275 @@ __global__ __launch_bounds__(512) void isa_flash_fp8_pp_kernel(Fp8Args a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  // work item lid: row tile fastest, then key split, then head (as the
-  // forward flash kernels), so that the workgroups running at once on an XCD
-  // share one K/V range in its L2
-  const int lid = xcd_remap(blockIdx.x, a.n_wg);
-  const int rt = lid % a.row_tiles;
-  const int rest = lid / a.row_tiles;
-  const int split = rest % a.nsplit;
-  const int bh = rest / a.nsplit;
+  // Work items: the items of stream-K workgroup g (the logical id; whole row
+  // tiles, then the row tiles that its range meets), one after the other,
+  // the pipeline drained between them.  Consecutive workgroups run on one XCD
+  // and share its L2.
+  const SkItems sk = sk_items(a, xcd_remap((int)blockIdx.x, (int)gridDim.x));
+#pragma unroll 1
+  for (int item = 0; item < sk.kdp + sk.nsk; ++item) {
+    const SkItem it = sk_item(a, sk, item);
+    const int bh = it.bh, rt = it.rt;
+    const int part = it.part < 0 ? -1 : (it.part & 7), Rs = it.part >> 3;   // part < 0: the whole row tile
+    if (item > 0) __syncthreads();   // the previous item's LDS reads are done
 
-  // ---- query row, quantised as in isa_flash_fp8_kernel
-  const long long vrow = (long long)rt * BM + w * 32 + l32;
-  const int qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
-  v8i qB[NU];
-  int qS[NU];
-  {
-    const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      float x[32];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bf16_t* p = qp + 64 * u + 32 * b + 16 * h;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u32x4 wv = *(const u32x4*)(p + 8 * c);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[16 * b + 8 * c + 2 * j] = __uint_as_float(wv[j] << 16);
-            x[16 * b + 8 * c + 2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
-          }
-        }
-      }
-      int eb[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float m = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(x[16 * b + j]));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        eb[b] = m > 0.f ? block_exp(m) : 0;
-      }
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const float sq = pow2_neg(eb[g >> 2]);
-        qB[u][g] = (int)pack4_fp8(x[4 * g] * sq, x[4 * g + 1] * sq, x[4 * g + 2] * sq, x[4 * g + 3] * sq);
-      }
-      qS[u] = eb[h] + 127;
-    }
-  }
-
-  // ---- key range
-  const int n_keys = a.Ns + (int)a.ctx_tok;
-  const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
-  const int n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
-  const int ntiles = (n_keys + BN - 1) / BN;
-  const int t_begin = split * a.tiles_per_split;
-  const int nt = max(0, min(a.tiles_per_split, ntiles - t_begin));
-
-  const uint8_t* Kg = a.k8 + (long long)bh * a.nkp * D;
-  const uint8_t* KSg = a.ks + (long long)bh * a.nkp * NB;
-  const uint8_t* Vg = a.v8t + (long long)bh * a.ntile * D * 64;
-  const uint8_t* VSg = a.vs + (long long)bh * a.ntile * D * 2;
-  const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem, lds_v = lds_k + NST * KTB;
-  const unsigned lds_ks = (unsigned)(size_t)(lds_char*)&sks[0][0];
-  const unsigned lds_vs = (unsigned)(size_t)(lds_char*)&svs[0][0];
-  // this wave's share of a tile: K8 rows 32*grp + 8*wg + lane/8 (chunk lane%8),
-  // V8T rows 64*grp + 16*wg + lane/4 (chunk lane%4); wave 0 of group 0 the
-  // key scales, wave 0 of group 1 the value scales
-  const int krow_l = 32 * grp + 8 * wg + (lane >> 3), vrow_l = 64 * grp + 16 * wg + (lane >> 2);
-  const unsigned kvo = (unsigned)krow_l * D + (unsigned)(((lane & 7) ^ k8_swz(krow_l)) * 16);
-  const unsigned vvo = (unsigned)vrow_l * 64 + (unsigned)(((lane & 3) ^ v8_swz(vrow_l)) * 16);
-  auto issue_k = [&](int stage, int tile) {
-    dma16(__builtin_amdgcn_readfirstlane(lds_k + stage * KTB + (32 * grp + 8 * wg) * D), Kg,
-          (unsigned)tile * KTB + kvo);
-    if (wg == 0 && grp == 0) dma4(lds_ks + stage * BN * 4, KSg, (unsigned)tile * BN * NB + (unsigned)lane * 4u);
-  };
-  auto issue_v = [&](int stage, int tile) {
-    dma16(__builtin_amdgcn_readfirstlane(lds_v + stage * VTB + (64 * grp + 16 * wg) * 64), Vg,
-          (unsigned)tile * VTB + vvo);
-    if (wg == 0 && grp == 1) dma4(lds_vs + stage * D * 2, VSg, (unsigned)tile * D * 2 + (unsigned)lane * 4u);
-  };
-
-  f32x16 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.f;   // m_ref: exp2 domain, a whole number once set
-  const float sc = a.scale_log2;
-
-  struct STile { f32x16 t[2]; };
-  // X: 4 P.V MFMAs, then 4 K.Q^T MFMAs; P.V operands read first, each K.Q^T
-  // operand pair read one MFMA ahead
-  auto pv_qk = [&](int vstage, const v8i& pB, int kstage) -> STile {
-    const char* V0 = smem + NST * KTB + vstage * VTB;
-    const char* K0 = smem + kstage * KTB;
-    v8i va[NT], ka[4];
-    int vsc[NT], ksc[4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int d = 32 * t + l32;
-      const char* vp = V0 + d * 64;
-      va[t] = lds_operand(vp + (((2 * h) ^ v8_swz(d)) * 16), vp + (((2 * h + 1) ^ v8_swz(d)) * 16));
-      vsc[t] = (int)((svs[vstage][d >> 1] >> (16 * (d & 1) + 8 * h)) & 0xffu);
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int krow = half * 32 + l32;
-      const char* kp = K0 + krow * D;
-      const uint32_t ksw = sks[kstage][krow];
+    // ---- query row, quantised as in isa_flash_fp8_kernel
+    const long long vrow = (long long)rt * BM + w * 32 + l32;
+    const int qrow = route_row(a.q_list + (long long)bh * a.q_k, a.q_k, a.b, a.nb_s, a.Ns, vrow);
+    v8i qB[NU];
+    int qS[NU];
+    {
+      const bf16_t* qp = (const bf16_t*)a.Q + rm_head(a.rmq, bh) + (long long)(qrow < 0 ? 0 : qrow) * a.rmq.sn;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        ka[2 * half + u] = lds_operand(kp + (((4 * u + h) ^ k8_swz(krow)) * 16), kp + (((4 * u + 2 + h) ^ k8_swz(krow)) * 16));
-        ksc[2 * half + u] = (int)((ksw >> (8 * (2 * u + h))) & 0xffu);
-      }
-    }
+        float x[32];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[t], pB, acc[t], 0, 0, 0, vsc[t], 0, 127);
-    STile S;
-    S.t[0] = f32x16{};
-    S.t[1] = f32x16{};
+        for (int b = 0; b < 2; ++b) {
+          const bf16_t* p = qp + 64 * u + 32 * b + 16 * h;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      S.t[m >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[m], qB[m & 1], S.t[m >> 1], 0, 0, 0, ksc[m], 0,
-                                                                   qS[m & 1]);
-    constexpr int kMFMA = 0x8, kDSR = 0x100;
-    __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NT + 2, 0);
+          for (int c = 0; c < 2; ++c) {
+            const u32x4 wv = *(const u32x4*)(p + 8 * c);
 #pragma unroll
-    for (int m = 0; m < 7; ++m) {
-      __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
-      if (m < 3) __builtin_amdgcn_sched_group_barrier(kDSR, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
-    return S;
-  };
-
-  // softmax of tile j (exp2 domain, integer reference max): probabilities
-  // first against the current reference, the row max and the move rule only
-  // when a lane's tile sum leaves [0, 2^7] (a probability above 2^8, where
-  // isa_flash_fp8_kernel moves the reference, implies that)
-  auto softmax = [&](int j, STile St, v8i& pB) {
-    const int t0 = (t_begin + j) * BN;
-    float x[32];
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[16 * half + r] = St.t[half][r];
-    if (t0 + BN > n_valid) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int key = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * h + (i & 3);
-        if (t0 + key >= n_valid) x[i] = -INFINITY;
-      }
-    }
-    auto probs = [&]() -> float {
-      float psum = 0.f;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + e], sc, -m_ref));
-          psum += p[e];
+            for (int j = 0; j < 4; ++j) {
+              x[16 * b + 8 * c + 2 * j] = __uint_as_float(wv[j] << 16);
+              x[16 * b + 8 * c + 2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+            }
+          }
         }
-        pB[g] = (int)pack4_fp8(p[0], p[1], p[2], p[3]);
-      }
-      return psum;
-    };
-    float psum = probs();
-    if (__ballot(!(psum <= 128.f))) {
-      float mx = -INFINITY;
+        int eb[2];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, x[i]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
-      const bool move = mx > m_ref + 8.0f;
-      if (__ballot(move)) {
-        const float m_new = move ? ceilf(mx) : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-        l_run *= alpha;
+        for (int b = 0; b < 2; ++b) {
+          float m = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-        m_ref = m_new;
-        psum = probs();
+          for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(x[16 * b + j]));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          eb[b] = m > 0.f ? block_exp(m) : 0;
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const float sq = pow2_neg(eb[g >> 2]);
+          qB[u][g] = (int)pack4_fp8(x[4 * g] * sq, x[4 * g + 1] * sq, x[4 * g + 2] * sq, x[4 * g + 3] * sq);
+        }
+        qS[u] = eb[h] + 127;
       }
     }
-    l_run += psum;
-  };
-  auto phase_barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
 
-  const int t_last = t_begin + nt - 1;
-  auto tl = [&](int j) { return min(t_begin + j, t_last); };
-  if (nt > 0) {
-    issue_k(0, tl(0));
-    issue_k(1, tl(1));
-    issue_k(2, tl(2));
-    issue_v(0, tl(0));
-    issue_v(1, tl(1));
-    // V stage 3 is first loaded in step 1; step 0 multiplies it (as zeros) by P = 0
-    u32x4* vz = (u32x4*)(smem + NST * KTB + 3 * VTB);
-    for (int q = tid; q < VTB / 16; q += 512) vz[q] = u32x4{0u, 0u, 0u, 0u};
-    if (tid < D / 2) svs[3][tid] = 0u;
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    phase_barrier();
-    if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
-    STile S = {};
-    v8i pB = {};
-    auto step = [&](int j) {
-      const int Z = j & 3;
-      // X_j (step nt computes an S that is never used)
-      __builtin_amdgcn_s_setprio(3);
-      S = pv_qk((Z + 3) & 3, pB, Z);
-      __builtin_amdgcn_sched_barrier(0);
-      // loads past the last tile re-read it into the stage the schedule
-      // frees for tile j+3 / j+2 and are never read
-      issue_k((Z + 3) & 3, tl(j + 3));
-      issue_v((Z + 2) & 3, tl(j + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-      phase_barrier();
-      // Y_j
-      if (j < nt) softmax(j, S, pB);
-      // the loads of X_{j-1} have landed before the barrier that closes Y_j
-      // (wave 0 of each group also loads one scale slice per step)
-      if (wg == 0) __builtin_amdgcn_s_waitcnt(0x0f73);   // vmcnt(3)
-      else __builtin_amdgcn_s_waitcnt(0x0f72);           // vmcnt(2)
-      phase_barrier();
+    // ---- key range
+    const int n_keys = a.Ns + (int)a.ctx_tok;
+    const bool tail_kept = a.kc > 0 && a.kept[(long long)bh * a.kc + a.kc - 1] == a.nb_c - 1;
+    const int n_valid = n_keys - (tail_kept ? a.b - a.tail_c : 0);
+    const int t_begin = it.t_begin;   // (rotated key order of a cut row tile: no wrap)
+    const int nt = it.nt;
+
+    const uint8_t* Kg = a.k8 + (long long)bh * a.nkp * D;
+    const uint8_t* KSg = a.ks + (long long)bh * a.nkp * NB;
+    const uint8_t* Vg = a.v8t + (long long)bh * a.ntile * D * 64;
+    const uint8_t* VSg = a.vs + (long long)bh * a.ntile * D * 2;
+    const unsigned lds_k = (unsigned)(size_t)(lds_char*)smem, lds_v = lds_k + NST * KTB;
+    const unsigned lds_ks = (unsigned)(size_t)(lds_char*)&sks[0][0];
+    const unsigned lds_vs = (unsigned)(size_t)(lds_char*)&svs[0][0];
+    // this wave's share of a tile: K8 rows 32*grp + 8*wg + lane/8 (chunk lane%8),
+    // V8T rows 64*grp + 16*wg + lane/4 (chunk lane%4); wave 0 of group 0 the
+    // key scales, wave 0 of group 1 the value scales
+    const int krow_l = 32 * grp + 8 * wg + (lane >> 3), vrow_l = 64 * grp + 16 * wg + (lane >> 2);
+    const unsigned kvo = (unsigned)krow_l * D + (unsigned)(((lane & 7) ^ k8_swz(krow_l)) * 16);
+    const unsigned vvo = (unsigned)vrow_l * 64 + (unsigned)(((lane & 3) ^ v8_swz(vrow_l)) * 16);
+    auto issue_k = [&](int stage, int tile) {
+      dma16(__builtin_amdgcn_readfirstlane(lds_k + stage * KTB + (32 * grp + 8 * wg) * D), Kg,
+            (unsigned)tile * KTB + kvo);
+      if (wg == 0 && grp == 0) dma4(lds_ks + stage * BN * 4, KSg, (unsigned)tile * BN * NB + (unsigned)lane * 4u);
     };
-    for (int j = 0; j <= nt; ++j) step(j);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
-    if (grp == 0) phase_barrier();   // balances group 1's extra barrier
-  }
+    auto issue_v = [&](int stage, int tile) {
+      dma16(__builtin_amdgcn_readfirstlane(lds_v + stage * VTB + (64 * grp + 16 * wg) * 64), Vg,
+            (unsigned)tile * VTB + vvo);
+      if (wg == 0 && grp == 1) dma4(lds_vs + stage * D * 2, VSg, (unsigned)tile * D * 2 + (unsigned)lane * 4u);
+    };
 
-  // ---- epilogue (as isa_flash_fp8_kernel's)
-  const float l_tot = l_run + wave_shfl_xor(l_run, 32);
-  if (a.nsplit == 1) {
-    if (qrow < 0) return;
-    const float inv = 1.0f / l_tot;
-    bf16_t* op = (bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn;
+    f32x16 acc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.f;   // m_ref: exp2 domain, a whole number once set
+    const float sc = a.scale_log2;
+
+    struct STile { f32x16 t[2]; };
+    // X: 4 P.V MFMAs, then 4 K.Q^T MFMAs; P.V operands read first, each K.Q^T
+    // operand pair read one MFMA ahead
+    auto pv_qk = [&](int vstage, const v8i& pB, int kstage) -> STile {
+      const char* V0 = smem + NST * KTB + vstage * VTB;
+      const char* K0 = smem + kstage * KTB;
+      v8i va[NT], ka[4];
+      int vsc[NT], ksc[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2*)(op + 32 * t + 8 * g + 4 * h) =
-            u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
-                  pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
-    if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref + __builtin_log2f(l_tot);
-  } else {
-    const long long prow = ((long long)bh * a.row_tiles * BM + vrow) * a.nsplit + split;
-    bf16_t* po = a.part_o + prow * D;
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      for (int t = 0; t < NT; ++t) {
+        const int d = 32 * t + l32;
+        const char* vp = V0 + d * 64;
+        va[t] = lds_operand(vp + (((2 * h) ^ v8_swz(d)) * 16), vp + (((2 * h + 1) ^ v8_swz(d)) * 16));
+        vsc[t] = (int)((svs[vstage][d >> 1] >> (16 * (d & 1) + 8 * h)) & 0xffu);
+      }
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int half = 0; half < 2; ++half) {
+        const int krow = half * 32 + l32;
+        const char* kp = K0 + krow * D;
+        const uint32_t ksw = sks[kstage][krow];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2*)(po + 32 * t + 8 * g + 4 * h) =
-            u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
-                  pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
-    if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref / sc, l_tot};
-  }
+        for (int u = 0; u < NU; ++u) {
+          ka[2 * half + u] = lds_operand(kp + (((4 * u + h) ^ k8_swz(krow)) * 16), kp + (((4 * u + 2 + h) ^ k8_swz(krow)) * 16));
+          ksc[2 * half + u] = (int)((ksw >> (8 * (2 * u + h))) & 0xffu);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[t], pB, acc[t], 0, 0, 0, vsc[t], 0, 127);
+      STile S;
+      S.t[0] = f32x16{};
+      S.t[1] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        S.t[m >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[m], qB[m & 1], S.t[m >> 1], 0, 0, 0, ksc[m], 0,
+                                                                     qS[m & 1]);
+      constexpr int kMFMA = 0x8, kDSR = 0x100;
+      __builtin_amdgcn_sched_group_barrier(kDSR, 2 * NT + 2, 0);
+#pragma unroll
+      for (int m = 0; m < 7; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+        if (m < 3) __builtin_amdgcn_sched_group_barrier(kDSR, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+      return S;
+    };
+
+    // softmax of tile j (exp2 domain, integer reference max): probabilities
+    // first against the current reference, the row max and the move rule only
+    // when a lane's tile sum leaves [0, 2^7] (a probability above 2^8, where
+    // isa_flash_fp8_kernel moves the reference, implies that)
+    auto softmax = [&](int j, STile St, v8i& pB) {
+      const int t0 = (t_begin + j) * BN;
+      float x[32];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[16 * half + r] = St.t[half][r];
+      if (t0 + BN > n_valid) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int key = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * h + (i & 3);
+          if (t0 + key >= n_valid) x[i] = -INFINITY;
+        }
+      }
+      auto probs = [&]() -> float {
+        float psum = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + e], sc, -m_ref));
+            psum += p[e];
+          }
+          pB[g] = (int)pack4_fp8(p[0], p[1], p[2], p[3]);
+        }
+        return psum;
+      };
+      float psum = probs();
+      if (__ballot(!(psum <= 128.f))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) mx = fmaxf(mx, x[i]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
+        const bool move = mx > m_ref + 8.0f;
+        if (__ballot(move)) {
+          const float m_new = move ? ceilf(mx) : m_ref;
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+          m_ref = m_new;
+          psum = probs();
+        }
+      }
+      l_run += psum;
+    };
+    auto phase_barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int t_last = t_begin + nt - 1;
+    auto tl = [&](int j) { return min(t_begin + j, t_last); };
+    if (nt > 0) {
+      issue_k(0, tl(0));
+      issue_k(1, tl(1));
+      issue_k(2, tl(2));
+      issue_v(0, tl(0));
+      issue_v(1, tl(1));
+      // V stage 3 is first loaded in step 1; step 0 multiplies it (as zeros) by P = 0
+      u32x4* vz = (u32x4*)(smem + NST * KTB + 3 * VTB);
+      for (int q = tid; q < VTB / 16; q += 512) vz[q] = u32x4{0u, 0u, 0u, 0u};
+      if (tid < D / 2) svs[3][tid] = 0u;
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+      phase_barrier();
+      if (grp == 1) phase_barrier();   // group 1 runs one phase behind group 0
+      STile S = {};
+      v8i pB = {};
+      auto step = [&](int j) {
+        const int Z = j & 3;
+        // X_j (step nt computes an S that is never used)
+        __builtin_amdgcn_s_setprio(3);
+        S = pv_qk((Z + 3) & 3, pB, Z);
+        __builtin_amdgcn_sched_barrier(0);
+        // loads past the last tile re-read it into the stage the schedule
+        // frees for tile j+3 / j+2 and are never read
+        issue_k((Z + 3) & 3, tl(j + 3));
+        issue_v((Z + 2) & 3, tl(j + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        phase_barrier();
+        // Y_j
+        if (j < nt) softmax(j, S, pB);
+        // the loads of X_{j-1} have landed before the barrier that closes Y_j
+        // (wave 0 of each group also loads one scale slice per step)
+        if (wg == 0) __builtin_amdgcn_s_waitcnt(0x0f73);   // vmcnt(3)
+        else __builtin_amdgcn_s_waitcnt(0x0f72);           // vmcnt(2)
+        phase_barrier();
+      };
+      for (int j = 0; j <= nt; ++j) step(j);
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // no load into this workgroup's LDS outlives it
+      if (grp == 0) phase_barrier();   // balances group 1's extra barrier
+    }
+
+    // ---- epilogue (as isa_flash_fp8_kernel's)
+    const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+    if (part < 0) {
+      if (qrow < 0) continue;
+      const float inv = 1.0f / l_tot;
+      bf16_t* op = (bf16_t*)a.O + rm_head(a.rmo, bh) + (long long)qrow * a.rmo.sn;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(op + 32 * t + 8 * g + 4 * h) =
+              u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                    pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+      if (a.lse && h == 0) a.lse[(long long)bh * a.Ns + qrow] = m_ref + __builtin_log2f(l_tot);
+    } else {
+      // part `part` of range-phase row tile Rs: [Rs][sk_P][BM][D]
+      const long long prow = ((long long)Rs * a.sk_P + part) * BM + w * 32 + l32;
+      bf16_t* po = a.part_o + prow * D;
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(po + 32 * t + 8 * g + 4 * h) =
+              u32x2{pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
+                    pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
+      if (h == 0) *(float2*)(a.part_ml + prow * 2) = float2{m_ref / sc, l_tot};
+    }
+  }  // items
 }
 
 // ---------------------------------------------------------------------------
@@ -757,7 +765,22 @@ static hipError_t fp8_t(const Layout& L, const Fp8Layout& F, const Bufs& B, char
   if (nwg == 0) return hipSuccess;
   a.n_wg = (int)nwg;
   if constexpr (D == 128 && kFlashWaves == 8) {
-    hipLaunchKernelGGL(isa_flash_fp8_pp_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a);
+    // the stream-K split of the bf16 route (the layout's): whole row tiles in
+    // a.sk_K rounds of grid workgroups, then a.sk_G ranges
+    const long long R = (long long)a.row_tiles * L.BH, grid = L.sk_grid;
+    a.sk_K = L.sk_rounds;
+    a.sk_G = L.sk_G;
+    a.sk_P = L.sk_P;
+    a.sk_R0 = (int)(grid * a.sk_K);
+    a.sk_grid = (int)grid;
+    a.sk_q = (int)(R / 8);
+    a.sk_x = (int)(R % 8);
+    a.sk_T = ntiles;
+    a.sk_U = (R - a.sk_R0) * ntiles;
+    if (grid <= 0 || grid % 8 != 0 || a.sk_K < 0 || a.sk_R0 > R || (a.sk_U > 0) != (a.sk_G > 0) || a.sk_U < a.sk_G ||
+        a.sk_P < 1 || a.sk_P > kMaxSplits)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(isa_flash_fp8_pp_kernel, dim3((unsigned)(a.sk_K > 0 ? grid : a.sk_G)), dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL((isa_flash_fp8_kernel<D>), dim3((unsigned)nwg), dim3(512), 0, s, a);
   }
